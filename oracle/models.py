@@ -1,0 +1,341 @@
+"""Bit-level models of the barrier-free protocols (LL, Sentinel, LL128 atomic,
+double buffering with implicit credits).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  These are written from
+the prose of "Every Microsecond Matters: Achieving Near Speed-of-Light Latency
+in GPU Collectives" (agihunt.info summary), the four protocol paragraphs:
+
+* LL: an 8-byte flag and 8 bytes of data leave in one 16-byte write, so seeing
+  the flag means the data is there.  Half the bandwidth, twice the staging.
+* Sentinel: the receive buffer is prefilled with a value data should not take
+  (the page's example is -NaN); a change of value means arrival; the buffer
+  must be reset after use and data must never equal the sentinel.
+* Bidirectional + double buffering: a chunk received from the peer is the
+  permission to send the next one, and two alternating buffers remove the
+  barrier between iterations.
+* Two-shot LL128 atomic: reduce-scatter + all-gather; groups of 8 threads per
+  128-byte line; the group's first thread sets its own element to 1 as the
+  flag; all 8 atomically add into staging; the line is complete when the flag
+  sums to N; about D/N staging; waste about 1.5 % (FP16) and 3 % (FP32).
+
+Readings where the page is silent (each is listed with its reason in the
+design notes): LL words are laid out [data0, epoch, data1, epoch] with a
+monotone non-zero epoch; the sentinel is the all-ones pattern (a negative NaN
+in all three formats) and producers replace a datum equal to it by the
+all-ones-minus-one pattern (still a negative NaN); the LL128 flag is 1.0 in
+the staging type in slot 0 of the line; element e lives in line e // K, slot
+1 + e % K with K = 128 / sizeof(A) - 1; owners hold contiguous balanced line
+ranges; the consumer zeroes a line after reading it.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import F32, F16, BF16, ELEM_BYTES, BITS_DTYPE, decode, round_to
+
+# ----------------------------------------------------------------------------
+# LL: 16-byte line = 8 bytes payload + 8 bytes flag
+# ----------------------------------------------------------------------------
+LL_LINE_BYTES = 16
+LL_PAYLOAD_BYTES = 8
+
+
+def next_epoch(e: int) -> int:
+    """Epochs run 1, 2, ..., 2^32-1, 1, ...; 0 means 'never written'."""
+    e = (e + 1) & 0xFFFFFFFF
+    return 1 if e == 0 else e
+
+
+def ll_pack(payload_words: np.ndarray, epoch: int) -> np.ndarray:
+    """(L, 2) uint32 payload words -> (L, 4) uint32 lines [d0, e, d1, e]."""
+    p = np.asarray(payload_words, dtype=np.uint32).reshape(-1, 2)
+    lines = np.empty((p.shape[0], 4), dtype=np.uint32)
+    lines[:, 0] = p[:, 0]
+    lines[:, 1] = epoch
+    lines[:, 2] = p[:, 1]
+    lines[:, 3] = epoch
+    return lines
+
+
+def ll_unpack(lines: np.ndarray, epoch: int):
+    """(L, 4) lines -> (valid[L], payload (L, 2)).  A line is valid only when
+    both flag words carry the expected epoch (either 8-byte half may land
+    first)."""
+    ln = np.asarray(lines, dtype=np.uint32).reshape(-1, 4)
+    valid = (ln[:, 1] == epoch) & (ln[:, 3] == epoch)
+    return valid, ln[:, [0, 2]].copy()
+
+
+def ll_payload_words(partial_bits: np.ndarray) -> np.ndarray:
+    """A partial's bytes, zero-padded to whole 8-byte payloads, as (L, 2) u32."""
+    raw = np.ascontiguousarray(partial_bits).view(np.uint8)
+    n_lines = -(-raw.size // LL_PAYLOAD_BYTES)
+    buf = np.zeros(n_lines * LL_PAYLOAD_BYTES, dtype=np.uint8)
+    buf[: raw.size] = raw
+    return buf.view(np.uint32).reshape(n_lines, 2)
+
+
+def ll_staging_bytes(message_bytes: int) -> int:
+    """Staging for one message: one 16-byte line per 8 payload bytes."""
+    return -(-message_bytes // LL_PAYLOAD_BYTES) * LL_LINE_BYTES
+
+
+# ----------------------------------------------------------------------------
+# Sentinel
+# ----------------------------------------------------------------------------
+SENTINEL_BITS = {F32: 0xFFFFFFFF, F16: 0xFFFF, BF16: 0xFFFF}
+
+
+def sentinel_canon(bits: np.ndarray, dtype: int) -> np.ndarray:
+    """Replace the sentinel pattern by the pattern one below it (both NaN)."""
+    s = SENTINEL_BITS[dtype]
+    b = np.asarray(bits, dtype=BITS_DTYPE[dtype])
+    return np.where(b == s, BITS_DTYPE[dtype](s - 1), b).astype(BITS_DTYPE[dtype])
+
+
+def sentinel_ready(bits: np.ndarray, dtype: int) -> np.ndarray:
+    return np.asarray(bits) != SENTINEL_BITS[dtype]
+
+
+def sentinel_reset(n_elems: int, dtype: int) -> np.ndarray:
+    return np.full(n_elems, SENTINEL_BITS[dtype], dtype=BITS_DTYPE[dtype])
+
+
+# ----------------------------------------------------------------------------
+# LL128 atomic two-shot
+# ----------------------------------------------------------------------------
+LL128_LINE_BYTES = 128
+LL128_LANES = 8            # threads per line
+LL128_LANE_BYTES = 16
+
+
+@dataclass(frozen=True)
+class LL128Geometry:
+    n: int                 # elements per rank
+    n_ranks: int
+    acc_bytes: int         # bytes per staging slot (4 for fp32, 2 for 16-bit)
+
+    @property
+    def slots(self) -> int:
+        return LL128_LINE_BYTES // self.acc_bytes
+
+    @property
+    def k(self) -> int:     # data slots per line
+        return self.slots - 1
+
+    @property
+    def lines(self) -> int:
+        return -(-self.n // self.k)
+
+    def owner_range(self, s: int):
+        ln = self.lines
+        return (s * ln) // self.n_ranks, ((s + 1) * ln) // self.n_ranks
+
+    def owner_of_line(self, line: int) -> int:
+        for s in range(self.n_ranks):
+            a, b = self.owner_range(s)
+            if a <= line < b:
+                return s
+        raise IndexError(line)
+
+    def line_slot(self, e: int):
+        return e // self.k, 1 + e % self.k
+
+    @property
+    def waste(self) -> float:
+        """Fraction of every line spent on the flag."""
+        return 1.0 / self.slots
+
+    @property
+    def staging_bytes(self) -> int:
+        return self.lines * LL128_LINE_BYTES
+
+    def max_owner_staging_bytes(self) -> int:
+        return max(b - a for a, b in (self.owner_range(s) for s in range(self.n_ranks))) * LL128_LINE_BYTES
+
+
+def _acc_add(a: np.ndarray, b: np.ndarray, acc: int) -> np.ndarray:
+    """One atomic add in the staging type, correctly rounded."""
+    if acc == F32:
+        return (a.astype(np.float32) + b.astype(np.float32)).astype(np.float32)
+    # 16-bit staging: the binary64 sum of two 16-bit values is exact up to a
+    # single rounding of the binary64 sum (both fit comfortably), then round
+    # to the 16-bit format.
+    s = a.astype(np.float64) + b.astype(np.float64)
+    return decode(round_to(s, acc), acc)
+
+
+def ll128_staging_image(partials_bits: np.ndarray, dtype: int, acc: int, order=None) -> np.ndarray:
+    """Staging contents (L, slots) as binary64 values after every rank's atomic
+    contribution, applied rank by rank in ``order`` with rounding to the
+    staging type after each add."""
+    parts = np.asarray(partials_bits)
+    n_ranks, n = parts.shape
+    g = LL128Geometry(n, n_ranks, ELEM_BYTES[acc])
+    order = list(range(n_ranks)) if order is None else list(order)
+    stage = np.zeros((g.lines, g.slots), dtype=np.float64)
+    for r in order:
+        contrib = np.zeros((g.lines, g.slots), dtype=np.float64)
+        contrib[:, 0] = 1.0
+        vals = decode(parts[r], dtype)
+        if acc != dtype:
+            # conversion to the staging type (exact when widening)
+            vals = decode(round_to(vals, acc), acc)
+        flat = np.zeros(g.lines * g.k, dtype=np.float64)
+        flat[:n] = vals
+        contrib[:, 1:] = flat.reshape(g.lines, g.k)
+        stage = _acc_add(stage, contrib, acc).astype(np.float64)
+    return stage
+
+
+def ll128_result(stage: np.ndarray, n: int, dtype: int) -> np.ndarray:
+    """All-gather half: read each data slot back and round it to the output type."""
+    data = stage[:, 1:].reshape(-1)[:n]
+    return round_to(data, dtype)
+
+
+def ll128_error_bound(partials_bits: np.ndarray, dtype: int, acc: int) -> np.ndarray:
+    """|staged sum - exact sum| <= (N-1) * u_A * sum_r |p_r| for any add order
+    (the first add lands on zero and is exact), plus half an ulp of the output
+    type when the staging type differs from it."""
+    parts = np.asarray(partials_bits)
+    n_ranks = parts.shape[0]
+    absum = np.zeros(parts.shape[1], dtype=np.float64)
+    for r in range(n_ranks):
+        absum += np.abs(decode(parts[r], dtype))
+    u = {F32: 2.0 ** -24, F16: 2.0 ** -11, BF16: 2.0 ** -8}[acc]
+    bound = (n_ranks - 1) * u * absum * (1 + 1e-12)
+    if acc != dtype:
+        p = {F32: 24, F16: 11, BF16: 8}[dtype]
+        exact = np.abs(sum(decode(parts[r], dtype) for r in range(n_ranks)))
+        bound = bound + (exact + bound) * 2.0 ** (-p) + (2.0 ** -149 if dtype == F32 else 2.0 ** -133 if dtype == BF16 else 2.0 ** -24)
+    return bound
+
+
+# ----------------------------------------------------------------------------
+# Double buffering with implicit credits: a small model checker
+# ----------------------------------------------------------------------------
+@dataclass
+class PipelineResult:
+    states: int
+    terminal_ok: int
+    violations: list = field(default_factory=list)
+    deadlocks: int = 0
+
+
+def check_pipeline(n_ranks: int, slices: int, chunks: int, parities: int = 2,
+                   run_ahead: bool = False, max_states: int = 2_000_000) -> PipelineResult:
+    """Explore every interleaving of the chunked two-shot schedule.
+
+    Agents are workgroups (rank r, slice w).  Agent program, for c = 0..C-1:
+      produce(c): one atomic contribution into line (parity c % P, owner s,
+                  slice w) for every owner s (N separate steps);
+      consume(c): wait until line (parity c % P, owner r, slice w) has N
+                  contributions of chunk c, read it, zero it.
+    With ``run_ahead`` the agent produces chunk c+1 before consuming chunk c
+    (a schedule without the credit), which must be caught.
+
+    A line's state is (chunk it holds, contribution count).  Checked:
+      no overwrite -- a contribution for chunk c only lands on a line that is
+                      empty or already holds chunk c;
+      no early read -- consume(c) only after N contributions of chunk c;
+      progress     -- every state with unfinished agents has a move.
+    """
+    agents = [(r, w) for r in range(n_ranks) for w in range(slices)]
+
+    def program(c_count):
+        steps = []
+        if not run_ahead:
+            for c in range(c_count):
+                steps += [("p", c, s) for s in range(n_ranks)]
+                steps.append(("c", c, None))
+        else:
+            steps += [("p", 0, s) for s in range(n_ranks)]
+            for c in range(c_count):
+                if c + 1 < c_count:
+                    steps += [("p", c + 1, s) for s in range(n_ranks)]
+                steps.append(("c", c, None))
+        return steps
+
+    prog = program(chunks)
+    n_lines = parities * n_ranks * slices
+
+    def line_id(par, owner, w):
+        return (par * n_ranks + owner) * slices + w
+
+    # line state: (held_chunk or -1 for empty, count)
+    init = (tuple([0] * len(agents)), tuple([(-1, 0)] * n_lines))
+    res = PipelineResult(states=0, terminal_ok=0)
+    seen = set()
+    stack = [init]
+    while stack:
+        st = stack.pop()
+        if st in seen:
+            continue
+        seen.add(st)
+        res.states += 1
+        if res.states > max_states:
+            raise RuntimeError("state space too large")
+        pcs, lines = st
+        if all(pc == len(prog) for pc in pcs):
+            res.terminal_ok += 1
+            continue
+        moved = False
+        for ai, (r, w) in enumerate(agents):
+            pc = pcs[ai]
+            if pc == len(prog):
+                continue
+            kind, c, s = prog[pc]
+            par = c % parities
+            if kind == "p":
+                lid = line_id(par, s, w)
+                held, cnt = lines[lid]
+                if held not in (-1, c):
+                    res.violations.append(("overwrite", (r, w), c, s, held))
+                    continue
+                if cnt >= n_ranks:
+                    res.violations.append(("overflow", (r, w), c, s))
+                    continue
+                nl = list(lines)
+                nl[lid] = (c, cnt + 1)
+                npcs = list(pcs)
+                npcs[ai] += 1
+                stack.append((tuple(npcs), tuple(nl)))
+                moved = True
+            else:
+                lid = line_id(par, r, w)
+                held, cnt = lines[lid]
+                if held == c and cnt == n_ranks:
+                    nl = list(lines)
+                    nl[lid] = (-1, 0)
+                    npcs = list(pcs)
+                    npcs[ai] += 1
+                    stack.append((tuple(npcs), tuple(nl)))
+                    moved = True
+                # otherwise the consumer spins (no move)
+        if not moved:
+            res.deadlocks += 1
+        if res.violations:
+            break
+    return res
+
+
+# ----------------------------------------------------------------------------
+# Speed-of-light arithmetic and the alpha + beta * size model
+# ----------------------------------------------------------------------------
+def sol_floor(t_l2_round_trip: float, t_remote_write: float) -> float:
+    """Lower bound of one AllReduce: two L2 round trips plus one remote write."""
+    return 2.0 * t_l2_round_trip + t_remote_write
+
+
+def fit_alpha_beta(sizes, times):
+    """Least-squares fit of T(size) = alpha + beta * size."""
+    x = np.asarray(sizes, dtype=np.float64)
+    y = np.asarray(times, dtype=np.float64)
+    a = np.vstack([np.ones_like(x), x]).T
+    (alpha, beta), *_ = np.linalg.lstsq(a, y, rcond=None)
+    return float(alpha), float(beta)

@@ -1,0 +1,273 @@
+"""Pins for the protocol models (LL line, Sentinel buffer, LL128 atomic line,
+double buffering with implicit credits) against the figures the page prints,
+closed forms, exhaustive enumeration and model checking."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import F32, F16, BF16, models
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def pages():
+    with open(os.path.join(GOLDEN, "pages_figures.json")) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------- SoL
+def test_sol_floor_reproduces_page_figure(pages):
+    s = pages["sol"]
+    assert models.sol_floor(s["l2_round_trip_us"], s["remote_write_us"]) == pytest.approx(s["bound_us"], abs=1e-12)
+
+
+def test_alpha_beta_fit_recovers_synthetic_line():
+    sizes = [2**k for k in range(7, 27)]
+    alpha, beta = 3.2, 1.7e-4
+    t = [alpha + beta * s for s in sizes]
+    a, b = models.fit_alpha_beta(sizes, t)
+    assert a == pytest.approx(alpha, rel=1e-9) and b == pytest.approx(beta, rel=1e-9)
+
+
+# --------------------------------------------------------------------------- LL
+def test_ll_line_is_one_16_byte_store_of_8_flag_and_8_data_bytes(pages):
+    ll = pages["ll"]
+    assert models.LL_LINE_BYTES == ll["store_bytes"] == ll["flag_bytes"] + ll["data_bytes"]
+    assert models.LL_PAYLOAD_BYTES == ll["data_bytes"]
+
+
+@pytest.mark.parametrize("nbytes", [8, 128, 16384, 1 << 20])
+def test_ll_staging_is_exactly_double(pages, nbytes):
+    assert models.ll_staging_bytes(nbytes) == pages["ll"]["staging_factor"] * nbytes
+
+
+def test_ll_pack_unpack_roundtrip_and_stale_detection():
+    g = np.random.default_rng(0)
+    payload = g.integers(0, 2**32, size=(1000, 2), dtype=np.uint64).astype(np.uint32)
+    for e in [1, 2, 7, 0xFFFFFFFF]:
+        lines = models.ll_pack(payload, e)
+        valid, back = models.ll_unpack(lines, e)
+        assert valid.all() and np.array_equal(back, payload)
+        # last call's epoch is stale
+        prev = e - 1 if e > 1 else 0xFFFFFFFF
+        valid_prev, _ = models.ll_unpack(models.ll_pack(payload, prev), e)
+        assert not valid_prev.any()
+        # a half-updated line (one 8-byte half from the old epoch) is rejected
+        torn = lines.copy()
+        torn[:, 3] = prev
+        assert not models.ll_unpack(torn, e)[0].any()
+        torn = lines.copy()
+        torn[:, 1] = prev
+        assert not models.ll_unpack(torn, e)[0].any()
+    # a zeroed buffer is never valid
+    assert not models.ll_unpack(np.zeros((4, 4), np.uint32), 1)[0].any()
+
+
+def test_epoch_sequence_skips_zero():
+    assert models.next_epoch(1) == 2
+    assert models.next_epoch(0xFFFFFFFF) == 1
+    e, seen = 0xFFFFFFF0, set()
+    for _ in range(40):
+        e = models.next_epoch(e)
+        assert e != 0
+        seen.add(e)
+    assert len(seen) == 40
+
+
+def test_ll_payload_padding_is_zero_and_bytes_are_preserved():
+    parts = np.arange(13, dtype=np.uint16)  # 26 bytes -> 4 payloads
+    w = models.ll_payload_words(parts)
+    assert w.shape == (4, 2)
+    raw = w.reshape(-1).view(np.uint8)
+    assert np.array_equal(raw[:26], parts.view(np.uint8)) and not raw[26:].any()
+
+
+# --------------------------------------------------------------------------- Sentinel
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_sentinel_canonicalization_exhaustive_16bit(dt):
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    c = models.sentinel_canon(allb, dt)
+    s = models.SENTINEL_BITS[dt]
+    assert not (c == s).any()                          # never equals the sentinel
+    changed = c != allb
+    assert changed.sum() == 1 and allb[changed][0] == s  # only the sentinel moves
+    assert oracle.is_nan_bits(c[changed], dt).all()      # and stays a NaN
+    assert (c[changed] & 0x8000).all()                   # a negative one
+    # the sentinel itself is a negative NaN ("e.g. -NaN")
+    assert oracle.is_nan_bits(np.array([s], np.uint16), dt)[0] and (s & 0x8000)
+
+
+def test_sentinel_fp32_specials_and_random():
+    s = models.SENTINEL_BITS[F32]
+    assert oracle.is_nan_bits(np.array([s], np.uint32), F32)[0] and (s >> 31)
+    # the x86 default NaN, the canonical quiet NaN, Inf and zeros are not it
+    for b in [0x7FC00000, 0xFFC00000, 0x7F800000, 0x80000000, 0]:
+        assert b != s
+    g = np.random.default_rng(1)
+    b = g.integers(0, 2**32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    b[::100_000] = s
+    c = models.sentinel_canon(b, F32)
+    assert not (c == s).any()
+    assert np.array_equal(c[b != s], b[b != s])
+    assert oracle.is_nan_bits(c[b == s], F32).all()
+
+
+@pytest.mark.parametrize("dt", [F32, F16, BF16])
+def test_sentinel_canonicalization_does_not_change_the_sum(dt):
+    g = np.random.default_rng(2 + dt)
+    bits = oracle.round_to(g.standard_normal((4, 5000)), dt)
+    bits[1, ::97] = models.SENTINEL_BITS[dt]
+    want = oracle.allreduce(bits, dt)
+    canon = np.stack([models.sentinel_canon(bits[r], dt) for r in range(4)])
+    got = oracle.allreduce(canon, dt)
+    assert oracle.same_result(got, want, dt).all()
+
+
+def test_sentinel_reset_and_readiness():
+    for dt in (F32, F16, BF16):
+        buf = models.sentinel_reset(64, dt)
+        assert not models.sentinel_ready(buf, dt).any()
+        buf[3] = 0
+        assert models.sentinel_ready(buf, dt)[3] and models.sentinel_ready(buf, dt).sum() == 1
+
+
+def test_workload_3_is_sentinel_free():
+    from workloads import WORKLOADS, workload_partials
+    w = WORKLOADS[3]
+    for rep in range(3):
+        p = workload_partials(w, rep)
+        assert not (p == models.SENTINEL_BITS[F16]).any()
+
+
+# --------------------------------------------------------------------------- LL128
+def test_ll128_lane_grouping_matches_page(pages):
+    p = pages["ll128"]
+    assert models.LL128_LINE_BYTES == p["line_bytes"]
+    assert models.LL128_LINE_BYTES // models.LL128_LANE_BYTES == p["threads_per_line"] == models.LL128_LANES
+
+
+def test_ll128_waste_recomputed_from_layout(pages):
+    p = pages["ll128"]
+    w16 = models.LL128Geometry(8192, 4, 2).waste
+    w32 = models.LL128Geometry(8192, 4, 4).waste
+    assert w16 == 1 / 64 and w32 == 1 / 32
+    assert abs(w16 - p["waste_fp16_approx"]) <= p["waste_tolerance_of_approx"]
+    assert abs(w32 - p["waste_fp32_approx"]) <= p["waste_tolerance_of_approx"]
+
+
+def test_ll128_geometry_closed_forms_for_the_workloads():
+    g2 = models.LL128Geometry(8192, 4, 2)          # 16 KiB bf16, 16-bit staging
+    assert g2.k == 63 and g2.lines == 131 and g2.staging_bytes == 16768
+    g2f = models.LL128Geometry(8192, 4, 4)         # same, fp32 staging
+    assert g2f.k == 31 and g2f.lines == 265 and g2f.staging_bytes == 33920
+    g4 = models.LL128Geometry(16384, 8, 4)         # one 64 KiB fp32 chunk
+    assert g4.lines == 529 and g4.staging_bytes == 67712
+    # owner ranges tile the lines exactly, balanced within one line
+    for g in (g2, g2f, g4):
+        spans = [g.owner_range(s) for s in range(g.n_ranks)]
+        assert spans[0][0] == 0 and spans[-1][1] == g.lines
+        assert all(a[1] == b[0] for a, b in zip(spans, spans[1:]))
+        sizes = [b - a for a, b in spans]
+        assert max(sizes) - min(sizes) <= 1
+
+
+@pytest.mark.parametrize("n_ranks", [2, 4, 8])
+def test_ll128_staging_per_owner_is_about_d_over_n(n_ranks):
+    n = 8192
+    g = models.LL128Geometry(n, n_ranks, 2)
+    d = n * 2
+    per_owner = g.max_owner_staging_bytes()
+    assert per_owner <= (d / n_ranks) * (g.slots / g.k) + models.LL128_LINE_BYTES
+
+
+def test_ll128_element_mapping_is_a_bijection_onto_data_slots():
+    g = models.LL128Geometry(1000, 4, 4)
+    seen = set()
+    for e in range(1000):
+        line, slot = g.line_slot(e)
+        assert 1 <= slot < g.slots and 0 <= line < g.lines
+        seen.add((line, slot))
+    assert len(seen) == 1000
+
+
+def ints_bits(seed, n_ranks, n, dt):
+    g = np.random.default_rng(seed)
+    return oracle.round_to(g.integers(-50, 51, size=(n_ranks, n)).astype(np.float64), dt)
+
+
+@pytest.mark.parametrize("dt,acc", [(BF16, BF16), (F16, F16), (BF16, F32), (F32, F32)])
+def test_ll128_flag_counts_contributions_exactly(dt, acc):
+    parts = ints_bits(3, 4, 300, dt)
+    for k in range(1, 5):
+        img = models.ll128_staging_image(parts[:k], dt, acc)
+        assert (img[:, 0] == k).all()
+    # a missing contribution leaves N-1, a duplicate gives N+1
+    full = models.ll128_staging_image(parts, dt, acc)
+    assert (full[:, 0] == 4).all()
+    dup = models.ll128_staging_image(parts, dt, acc, order=[0, 1, 2, 3, 2])
+    assert (dup[:, 0] == 5).all()
+
+
+@pytest.mark.parametrize("dt,acc", [(BF16, BF16), (F16, F16), (BF16, F32), (F16, F32), (F32, F32)])
+def test_ll128_integer_data_is_exact_in_every_order(dt, acc):
+    parts = ints_bits(4, 4, 200, dt)
+    want = oracle.allreduce(parts, dt)
+    for order in itertools.permutations(range(4)):
+        img = models.ll128_staging_image(parts, dt, acc, order)
+        got = models.ll128_result(img, 200, dt)
+        assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("dt,acc", [(BF16, BF16), (F16, F16), (BF16, F32), (F16, F32), (F32, F32)])
+def test_ll128_any_order_within_error_bound(dt, acc):
+    g = np.random.default_rng(5 + dt + 3 * acc)
+    parts = oracle.round_to(g.standard_normal((4, 2000)) * 0.02, dt)
+    exact = oracle.sum_f64(parts, dt)  # binary64 sum of <=4 such values is exact here
+    bound = models.ll128_error_bound(parts, dt, acc)
+    for order in itertools.permutations(range(4)):
+        img = models.ll128_staging_image(parts, dt, acc, order)
+        got = oracle.decode(models.ll128_result(img, 2000, dt), dt)
+        assert (np.abs(got - exact) <= bound).all()
+
+
+def test_ll128_error_bound_is_not_vacuous():
+    # the bound must be tight enough that a dropped rank breaks it
+    g = np.random.default_rng(9)
+    parts = oracle.round_to(g.standard_normal((4, 2000)) * 0.02, BF16)
+    exact = oracle.sum_f64(parts, BF16)
+    bound = models.ll128_error_bound(parts, BF16, F32)
+    img = models.ll128_staging_image(parts[:3], BF16, F32)
+    got = oracle.decode(models.ll128_result(img, 2000, BF16), BF16)
+    assert (np.abs(got - exact) > bound).mean() > 0.5
+
+
+# --------------------------------------------------------------------------- credits
+def test_pipeline_double_buffer_is_safe_exhaustively_n2():
+    r = models.check_pipeline(n_ranks=2, slices=1, chunks=3)
+    assert not r.violations and r.deadlocks == 0 and r.terminal_ok == 1 and r.states > 20
+
+
+def test_pipeline_double_buffer_is_safe_exhaustively_n3():
+    r = models.check_pipeline(n_ranks=3, slices=1, chunks=3)
+    assert not r.violations and r.deadlocks == 0 and r.terminal_ok == 1
+
+
+def test_pipeline_two_slices_is_safe():
+    r = models.check_pipeline(n_ranks=2, slices=2, chunks=3)
+    assert not r.violations and r.deadlocks == 0
+
+
+def test_pipeline_single_buffer_overwrites():
+    r = models.check_pipeline(n_ranks=2, slices=1, chunks=3, parities=1)
+    assert any(v[0] == "overwrite" for v in r.violations)
+
+
+def test_pipeline_without_credit_overwrites():
+    r = models.check_pipeline(n_ranks=2, slices=1, chunks=4, run_ahead=True)
+    assert any(v[0] == "overwrite" for v in r.violations)

@@ -1,0 +1,103 @@
+"""Seeded synthetic inputs for the N-way AllReduce: the workload table and the
+generators shared by the tests, the smoke check and the benchmark.
+
+This module holds no arithmetic of the reduction or its protocols: it only
+draws random partial outputs of the stated shapes and distributions and hands
+out their bit patterns.  Both the CPU oracle and the GPU library consume what
+it returns; neither is imported here.
+
+Shapes follow the tensor-parallel decode setting of "Every Microsecond
+Matters: Achieving Near Speed-of-Light Latency in GPU Collectives"
+(agihunt.info summary): every decode step of every layer reduces the N shard
+outputs of width hidden x batch, a few KB to a few hundred KB.  hidden = 8192
+is the output width used for the TP cases.  No dataset or trained weights are
+involved; the values stand in for partial outputs of a layer (N(0,1) * 0.02)
+or for generic data (U[-1, 1], N(0,1)).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+DTYPES = ("fp32", "fp16", "bf16")
+ELEM_BYTES = {"fp32": 4, "fp16": 2, "bf16": 2}
+BITS_NP = {"fp32": np.uint32, "fp16": np.uint16, "bf16": np.uint16}
+CODE = {"fp32": 0, "fp16": 1, "bf16": 2}
+
+
+@dataclass(frozen=True)
+class Workload:
+    cfg_id: int
+    name: str
+    n_ranks: int
+    dtype: str
+    n_elems: int               # elements per rank (for the sweep: the default size)
+    dist: str                  # "uniform" (U[-1,1]*scale) or "normal" (N(0,1)*scale)
+    scale: float
+    protocol: str              # "ll", "sentinel", "ll128", "ll128_pipelined", "auto"
+    reps: int
+    chunk_bytes: int = 0       # pipelined protocol: bytes per rank per chunk
+    sweep_bytes: Optional[List[int]] = field(default=None, hash=False)
+
+    @property
+    def bytes_per_rank(self) -> int:
+        return self.n_elems * ELEM_BYTES[self.dtype]
+
+
+WORKLOADS = {
+    1: Workload(1, "ll_n2_fp32_128B", 2, "fp32", 32, "uniform", 1.0, "ll", 1000),
+    2: Workload(2, "ll128_n4_bf16_16KiB", 4, "bf16", 8192, "normal", 0.02, "ll128", 1000),
+    3: Workload(3, "sentinel_n8_fp16_128KiB", 8, "fp16", 65536, "normal", 0.02, "sentinel", 1000),
+    4: Workload(4, "ll128pipe_n8_fp32_4MiB", 8, "fp32", 1 << 20, "uniform", 1.0, "ll128_pipelined", 200,
+                chunk_bytes=65536),
+    5: Workload(5, "sweep_n8_bf16", 8, "bf16", 8192, "normal", 1.0, "auto", 1000,
+                sweep_bytes=[1 << k for k in range(7, 27)]),
+}
+
+
+def draw_values(cfg_id: int, rep: int, n_ranks: int, n_elems: int, dist: str, scale: float) -> np.ndarray:
+    """(n_ranks, n_elems) float32 draws from numpy's PCG64 seeded by [cfg_id, rep]."""
+    rng = np.random.default_rng([int(cfg_id), int(rep)])
+    shape = (n_ranks, n_elems)
+    if dist == "uniform":
+        v = rng.random(shape, dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
+    elif dist == "normal":
+        v = rng.standard_normal(shape, dtype=np.float32)
+    elif dist == "integer":
+        # small integers: every partial sum is exact in all three formats
+        v = rng.integers(-64, 65, size=shape).astype(np.float32)
+    else:
+        raise ValueError(dist)
+    if scale != 1.0:
+        v = v * np.float32(scale)
+    return v
+
+
+def to_bits(values_f32: np.ndarray, dtype: str) -> np.ndarray:
+    """Element bit patterns of the drawn values in the I/O type.
+
+    fp32: the float32 draw itself.  fp16: numpy's float16 conversion.  bf16:
+    the upper 16 bits of the float32 pattern (a plain truncation; it only
+    shapes the input distribution).
+    """
+    v = np.ascontiguousarray(values_f32, dtype=np.float32)
+    if dtype == "fp32":
+        return v.view(np.uint32).copy()
+    if dtype == "fp16":
+        return v.astype(np.float16).view(np.uint16).copy()
+    if dtype == "bf16":
+        return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    raise ValueError(dtype)
+
+
+def make_partials(cfg_id: int, rep: int, n_ranks: int, dtype: str, n_elems: int,
+                  dist: str = "normal", scale: float = 1.0) -> np.ndarray:
+    """(n_ranks, n_elems) array of element bits, seeded by [cfg_id, rep]."""
+    return to_bits(draw_values(cfg_id, rep, n_ranks, n_elems, dist, scale), dtype)
+
+
+def workload_partials(w: Workload, rep: int, n_elems: Optional[int] = None) -> np.ndarray:
+    n = w.n_elems if n_elems is None else n_elems
+    return make_partials(w.cfg_id, rep, w.n_ranks, w.dtype, n, w.dist, w.scale)
