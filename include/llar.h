@@ -1,0 +1,177 @@
+/*
+ * llar.h -- barrier-free small-message AllReduce protocols on one MI355X.
+ *
+ * The library reduces N tensor-parallel partial outputs into one output,
+ * out[i] = sum_r partials[r][i], with the protocols described in "Every
+ * Microsecond Matters: Achieving Near Speed-of-Light Latency in GPU
+ * Collectives" (agihunt.info summary of arXiv 2607.16100):
+ *
+ *   LL        -- paragraph "LL (Low-Latency)": an 8-byte flag and 8 bytes of
+ *                data leave in one 16-byte store; seeing the flag means the
+ *                data is there (no separate signal, 2x staging).
+ *   SENTINEL  -- paragraph "Sentinel": the receive buffer is prefilled with a
+ *                value data never takes (a negative NaN); the receiver polls
+ *                for the value to change and resets the buffer after use.
+ *   LL128     -- paragraph "Two-shot LL128 atomic AllReduce": reduce-scatter
+ *                by atomic adds into 128-byte lines whose first slot counts
+ *                contributions up to N, then all-gather; about D/N staging.
+ *   *_PIPELINED -- paragraph "bidirectional communication + double
+ *                buffering": the message moves in chunks through two
+ *                alternating staging buffers; receiving a chunk from a peer
+ *                is the permission to send the next one, so no barrier sits
+ *                between iterations.
+ *
+ * The N ranks are emulated inside one GPU: each rank is a set of workgroups
+ * that reads its own partial buffer; ranks exchange data only through the
+ * library's staging memory with device-coherent stores, loads and atomics,
+ * and every wait is a bounded poll on a flag or a value -- no grid-wide
+ * barrier.  The produced value is the AllReduce result seen by one rank.
+ *
+ * Conventions for every call:
+ *   - All functions are plain C, never throw, and return an llar status
+ *     (LLAR_OK == 0, negative on error) unless stated otherwise.
+ *   - Device pointers are HIP device allocations on the device that was
+ *     current when the communicator was created.
+ *   - Streams are hipStream_t passed as void* (0 = the null stream).
+ */
+#ifndef LLAR_H
+#define LLAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct llar_comm llar_comm; /* opaque; owned by the library */
+
+typedef enum {
+  LLAR_FP32 = 0, /* IEEE binary32 */
+  LLAR_FP16 = 1, /* IEEE binary16 */
+  LLAR_BF16 = 2  /* bfloat16 */
+} llar_dtype;   /* the pages' "two-shot LL128" paragraph limits the method to these three */
+
+typedef enum {
+  LLAR_AUTO = 0,                /* pick per (N, dtype, size) from the tuned table */
+  LLAR_LL = 1,                  /* one-shot LL */
+  LLAR_SENTINEL = 2,            /* one-shot Sentinel */
+  LLAR_LL128 = 3,               /* two-shot LL128 atomic, one round */
+  LLAR_LL128_PIPELINED = 4,     /* two-shot LL128 atomic, chunked, double-buffered, implicit credits */
+  LLAR_SENTINEL_PIPELINED = 5   /* two-shot Sentinel, chunked, double-buffered, implicit credits */
+} llar_protocol;
+
+enum {
+  LLAR_OK = 0,
+  LLAR_ERR_ARG = -1,          /* bad argument; nothing was launched */
+  LLAR_ERR_UNSUPPORTED = -2,  /* valid but not supported (dtype, N, size) */
+  LLAR_ERR_NOMEM = -3,        /* device allocation failed */
+  LLAR_ERR_HIP = -4,          /* a HIP runtime call failed */
+  LLAR_ERR_TIMEOUT = -5,      /* a device-side poll exceeded its time limit */
+  LLAR_ERR_DEVICE = -6        /* another device-side protocol error (see the status bits) */
+};
+
+/* Create a communicator for n_ranks emulated ranks (1..8) reducing values of
+ * `dtype`, with messages up to max_bytes per rank.  Allocates and initialises
+ * all staging (two parities per protocol), the device-resident epoch and the
+ * status word on the current device, then synchronises.  Returns NULL on
+ * failure; llar_last_error() then tells why. */
+llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes);
+
+/* out[i] = partials[0][i] + ... + partials[n_ranks-1][i] for i < n_elems.
+ *
+ * partials: host array of n_ranks device pointers (read during the call only).
+ * out:      device pointer to n_elems elements; it may alias one partial.
+ * All device pointers must be 16-byte aligned.  dtype must equal the
+ * create-time dtype and n_elems * sizeof(dtype) <= max_bytes.  n_elems == 0
+ * is a no-op.  The call only enqueues work on `stream` and returns; the
+ * caller keeps the buffers alive until the stream reaches that point.
+ *
+ * Rounding: LL and SENTINEL (one-shot and pipelined) add in binary64 in rank
+ * order and round once to dtype (round-to-nearest-even) -- deterministic.
+ * LL128 adds with float atomics in an unspecified order (binary32 staging by
+ * default) -- non-deterministic, within the staging type's rounding error.
+ *
+ * Errors: argument errors return at once with nothing enqueued.  Device-side
+ * errors (a poll timeout) are latched in the communicator's status word;
+ * `out` is then undefined.  One stream at a time per communicator. */
+int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t n_elems,
+                   llar_dtype dtype, llar_protocol protocol, void* stream);
+
+/* Free all resources (synchronises the device first).  NULL is a no-op. */
+int llar_destroy(llar_comm* h);
+
+/* Status of the last failing host call on this thread (for NULL returns). */
+int llar_last_error(void);
+
+/* Human-readable name of a status code (static string). */
+const char* llar_status_string(int status);
+
+/* Sticky device-side status: synchronises the device, returns LLAR_OK,
+ * LLAR_ERR_TIMEOUT or LLAR_ERR_DEVICE, and writes the raw status bits to
+ * *bits when bits is not NULL.  The status stays set until
+ * llar_clear_device_status(). */
+int llar_get_device_status(llar_comm* h, uint32_t* bits);
+int llar_clear_device_status(llar_comm* h);
+
+/* Options (key, value).  Keys:
+ *   "spin_timeout_us"  device poll limit in microseconds (default 200000)
+ *   "ll128_acc"        LL128 staging type: 0 = binary32 (default), 1 = the I/O type (16-bit packed)
+ *   "chunk_bytes"      per-rank chunk of the pipelined protocols (0 = tuned default)
+ *   "slices"           workgroups per rank (0 = tuned default)
+ *   "threads"          threads per workgroup: 64, 128, 256 or 512 (0 = tuned default)
+ *   "placement"        0 = auto, 1 = spread (rank r on XCD r mod 8), 2 = local (one slice's ranks share an XCD)
+ *   "timing"           1 = record device-side start/end wall-clock per call (see llar_get_timing)
+ *   "keep_staging"     1 = LL128/Sentinel consumers do not reset staging (tests only; the next call is invalid)
+ *   "debug_drop_rank"  tests: the producers of this rank write nothing, so consumers time out (-1 = none)
+ *   "auto_threshold_sentinel", "auto_threshold_ll128", "auto_threshold_pipelined"
+ *                      AUTO size boundaries in bytes per rank
+ * Returns LLAR_ERR_ARG for an unknown key or a bad value. */
+int llar_set_option(llar_comm* h, const char* key, long long value);
+int llar_get_option(llar_comm* h, const char* key, long long* value);
+
+/* Protocol AUTO would run for a message of `bytes` per rank. */
+int llar_select_protocol(llar_comm* h, size_t bytes);
+
+/* Copy `bytes` of the staging region of `protocol` (both parities, layout as
+ * documented in the design notes) to host memory; synchronises first.  For
+ * tests of flags and packing. */
+int llar_debug_copy_staging(llar_comm* h, llar_protocol protocol, void* host_dst, size_t bytes);
+/* Size in bytes of that staging region (0 if none). */
+size_t llar_staging_bytes(llar_comm* h, llar_protocol protocol);
+
+/* Current device epoch (synchronises first). */
+int llar_get_epoch(llar_comm* h, uint32_t* epoch);
+
+/* Device-side timing of the last `count` timed calls (option "timing"):
+ * for each call, the wall-clock ticks (see llar_wallclock_hz) of the first
+ * workgroup start and of the last workgroup end (after its final stores were
+ * acknowledged).  Writes 2*count uint64 to host_dst, oldest first; returns the
+ * number of records written (>= 0) or an error. */
+int llar_get_timing(llar_comm* h, uint64_t* host_dst, int count);
+double llar_wallclock_hz(void);
+
+/* Workgroup geometry the library would launch for this call (for tests and
+ * tuning): writes grid size, threads per workgroup, slices and chunks. */
+int llar_launch_geometry(llar_comm* h, size_t n_elems, llar_protocol protocol,
+                         int* grid, int* threads, int* slices, int* chunks);
+
+/* ---- speed-of-light floor microbenchmarks (same device) ---------------- *
+ * "Every Microsecond Matters" (agihunt.info summary), paragraph on the
+ * speed-of-light bound: one AllReduce cannot beat two L2 round trips plus one
+ * remote write.  On one GPU the analogues are measured here:
+ *   kind 0: L2 round trip -- dependent chain of device-coherent 4-byte loads
+ *           over a 64-line ring, ns per hop (param: XCD-distance unused)
+ *   kind 1: store-to-visibility -- half the round trip of a 16-byte coherent
+ *           store / poll ping-pong between workgroups on XCDs a and b,
+ *           ns (param = b, a = 0; b = 8 means a second workgroup on XCD 0)
+ *   kind 2: empty-kernel launch interval, ns per launch (host timed)
+ *   kind 3: device-coherent returning-atomic latency, ns
+ *   kind 4: streaming copy bandwidth, GB/s of read+write (param = MiB)
+ * Results go to *value.  Synchronous. */
+int llar_floor_measure(int kind, int param, double* value);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LLAR_H */

@@ -1,0 +1,222 @@
+// llar_device.h -- device-side building blocks of the emulated-rank AllReduce
+// protocols on gfx950 (MI355X): coherent 16-byte accesses, the ordering
+// primitive, element conversions and rounding, bounded polling.
+//
+// Memory-ordering scheme (gfx950, one agent, 8 XCDs, one L2 per XCD):
+//   * Every access that crosses workgroups goes through device-coherent
+//     instructions: buffer loads/stores carrying the sc1 cache-policy bit
+//     (what the compiler emits for agent-scope relaxed atomic loads and
+//     stores) or agent-scope float/int atomics (which the compiler emits
+//     without cache bits).  No staging word is ever read by a plain load.
+//   * "Release" is s_waitcnt vmcnt(0): every earlier store/atomic of the wave
+//     has been acknowledged at its coherence point before the next one
+//     issues.  The agent-scope fences (buffer_wbl2 / buffer_inv) are never
+//     used: they walk the whole L2 and cost microseconds.
+//   * "Acquire" is the sc1 load itself: loads issued after a flag was seen
+//     are coherent and issued later, so they observe what was performed
+//     before the flag.
+//   * In the XCD-local placement all workgroups that touch a staging range
+//     run on one XCD and share its L2, so payload stores there may be plain
+//     (write-back) stores; sc1 loads are then served by that L2.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace llar {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// gfx950 cache-policy bits of vector memory instructions
+constexpr int kCpolNone = 0;
+constexpr int kCpolSc0 = 1;
+constexpr int kCpolNt = 2;
+constexpr int kCpolSc1 = 16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // word3 0x00020000: raw (untyped) 32-bit data format for gfx9-family buffers
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// ---- coherent accesses to staging -------------------------------------------
+__device__ __forceinline__ u32x4 ld16_coh(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1);
+}
+__device__ __forceinline__ uint32_t ld4_coh(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCpolSc1);
+}
+__device__ __forceinline__ void st16_coh(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolSc1);
+}
+__device__ __forceinline__ void st16_l2(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolNone);
+}
+template <bool kLocal>
+__device__ __forceinline__ void st16_stage(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  if constexpr (kLocal) st16_l2(r, off, v);
+  else st16_coh(r, off, v);
+}
+
+// ---- ordering -----------------------------------------------------------------
+// Wait until every vector memory operation of this wave has completed; the
+// signal fences keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void drain_vm() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// ---- clocks and ids -------------------------------------------------------------
+__device__ __forceinline__ uint64_t wall_ticks() { return (uint64_t)wall_clock64(); }
+__device__ __forceinline__ uint32_t xcc_id() {
+  // HW register XCC_ID (20), bits 3:0
+  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xFu;
+}
+
+// ---- element decode (exact) ----------------------------------------------------------
+__device__ __forceinline__ double dec_f32(uint32_t b) { return (double)__uint_as_float(b); }
+__device__ __forceinline__ double dec_bf16(uint32_t h) { return (double)__uint_as_float(h << 16); }
+__device__ __forceinline__ double dec_f16(uint32_t h) {
+  _Float16 x = __builtin_bit_cast(_Float16, (uint16_t)h);
+  return (double)(float)x;
+}
+
+// ---- rounding binary64 -> output type ------------------------------------------------
+// binary32: the hardware conversion (round to nearest even in the default mode).
+__device__ __forceinline__ uint32_t rne_f32(double d) { return __float_as_uint((float)d); }
+
+// binary64 -> binary32 rounded to odd (Boldo & Melquiond): truncate toward zero,
+// then force the last bit to 1 when the conversion was inexact.  Rounding that
+// value to nearest-even in a format of at most 22 significand bits gives the
+// correctly rounded result, because binary32 keeps >= 2 extra bits.
+__device__ __forceinline__ float round_odd_f32(double d) {
+  float f = (float)d;
+  double back = (double)f;
+  if (back != d && d == d) {
+    uint32_t u = __float_as_uint(f);
+    if (__builtin_fabs(back) > __builtin_fabs(d)) u -= 1u;  // one step toward zero
+    u |= 1u;
+    f = __uint_as_float(u);
+  }
+  return f;
+}
+// binary32 -> bfloat16 round to nearest even on the bit pattern; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return ((u >> 16) | 0x0040u) & 0xFFFFu;
+  uint32_t lsb = (u >> 16) & 1u;
+  return ((u + 0x7FFFu + lsb) >> 16) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t rne_bf16(double d) { return f32_to_bf16_rne(round_odd_f32(d)); }
+__device__ __forceinline__ uint32_t rne_f16(double d) {
+  _Float16 h = (_Float16)round_odd_f32(d);  // v_cvt_f16_f32: nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+// ---- per-type traits ------------------------------------------------------------------
+// kind: 0 = binary32, 1 = binary16, 2 = bfloat16 (the ABI's llar_dtype values)
+template <int kKind> struct Elem;
+template <> struct Elem<0> {
+  static constexpr int kBytes = 4, kPerVec = 4;
+  static constexpr uint32_t kSentinelWord = 0xFFFFFFFFu;
+  __device__ static double dec(uint32_t b) { return dec_f32(b); }
+  __device__ static uint32_t enc(double d) { return rne_f32(d); }
+  __device__ static float to_f32(uint32_t b) { return __uint_as_float(b); }
+  __device__ static uint32_t from_f32(float f) { return __float_as_uint(f); }
+};
+template <> struct Elem<1> {
+  static constexpr int kBytes = 2, kPerVec = 8;
+  __device__ static double dec(uint32_t b) { return dec_f16(b); }
+  __device__ static uint32_t enc(double d) { return rne_f16(d); }
+  __device__ static float to_f32(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
+  __device__ static uint32_t from_f32(float f) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f); }
+};
+template <> struct Elem<2> {
+  static constexpr int kBytes = 2, kPerVec = 8;
+  __device__ static double dec(uint32_t b) { return dec_bf16(b); }
+  __device__ static uint32_t enc(double d) { return rne_bf16(d); }
+  __device__ static float to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+  __device__ static uint32_t from_f32(float f) { return f32_to_bf16_rne(f); }
+};
+
+// Element k (0-based) of a 16-byte vector, as raw bits.
+template <int kKind>
+__device__ __forceinline__ uint32_t vec_elem(const u32x4& v, int k) {
+  if constexpr (Elem<kKind>::kBytes == 4) return v[k];
+  else return (v[k >> 1] >> ((k & 1) * 16)) & 0xFFFFu;
+}
+template <int kKind>
+__device__ __forceinline__ void vec_set(u32x4& v, int k, uint32_t bits) {
+  if constexpr (Elem<kKind>::kBytes == 4) v[k] = bits;
+  else {
+    uint32_t sh = (k & 1) * 16;
+    v[k >> 1] = (v[k >> 1] & ~(0xFFFFu << sh)) | ((bits & 0xFFFFu) << sh);
+  }
+}
+
+// Sentinel: the all-ones pattern (a negative NaN in all three formats).  A
+// datum equal to it is replaced by the pattern one below (still a negative
+// NaN), so the staged data can never look like an empty slot.
+template <int kKind>
+__device__ __forceinline__ u32x4 sentinel_canon(u32x4 v) {
+  if constexpr (Elem<kKind>::kBytes == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (v[i] == 0xFFFFFFFFu) ? 0xFFFFFFFEu : v[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w = v[i];
+      if ((w & 0xFFFFu) == 0xFFFFu) w -= 1u;
+      if ((w >> 16) == 0xFFFFu) w -= 0x10000u;
+      v[i] = w;
+    }
+  }
+  return v;
+}
+// true when no element of the vector still holds the sentinel
+template <int kKind>
+__device__ __forceinline__ bool sentinel_ready(const u32x4& v) {
+  if constexpr (Elem<kKind>::kBytes == 4) {
+    return (v[0] != 0xFFFFFFFFu) & (v[1] != 0xFFFFFFFFu) & (v[2] != 0xFFFFFFFFu) & (v[3] != 0xFFFFFFFFu);
+  } else {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ok &= ((v[i] & 0xFFFFu) != 0xFFFFu) & ((v[i] >> 16) != 0xFFFFu);
+    return ok;
+  }
+}
+
+// ---- device control block --------------------------------------------------------------
+constexpr int kTimingRing = 64;
+constexpr uint32_t kStatusTimeout = 1u;
+constexpr uint32_t kStatusPlacement = 2u;
+
+struct Ctrl {
+  uint32_t epoch;      // current call's epoch, 1..2^32-1 (0 = never written)
+  uint32_t pad0[31];
+  uint32_t arrivals;   // workgroups of the running call that have read the epoch
+  uint32_t pad1[31];
+  uint32_t status;     // sticky error bits
+  uint32_t pad2[31];
+  uint64_t timing[kTimingRing][2];  // per epoch slot: first start, last end (wall ticks)
+};
+
+__device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return (e + 1u == 0u) ? 1u : e + 1u; }
+
+// Bounded poll helper: true while the wave may keep spinning.
+struct Spin {
+  uint64_t t0, limit;
+  uint32_t n;
+  __device__ __forceinline__ Spin(uint64_t lim) : t0(wall_ticks()), limit(lim), n(0) {}
+  __device__ __forceinline__ bool expired() {
+    if ((++n & 15u) != 0u) return false;
+    return wall_ticks() - t0 > limit;
+  }
+};
+
+__device__ __forceinline__ void raise_status(Ctrl* c, uint32_t bits) {
+  __hip_atomic_fetch_or(&c->status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace llar

@@ -1,0 +1,219 @@
+// llar_floor.hip -- single-GPU analogues of the speed-of-light terms.
+//
+// "Every Microsecond Matters" (agihunt.info summary), paragraph on the
+// speed-of-light bound: an AllReduce needs at least two L2 round trips plus
+// one remote write (0.306 us and 0.792 us on GB200, 1.404 us in total).  With
+// the ranks emulated on one MI355X the analogues are:
+//   L2 round trip   -- one device-coherent (sc1) load of an L2-resident line,
+//                      measured as ns per hop of a dependent pointer chase;
+//   remote write    -- the time from a 16-byte coherent store on one XCD to
+//                      its observation by a poller on another XCD, measured
+//                      as half of a store/poll ping-pong round trip.
+// Plus the launch interval of an empty kernel, the latency of a returning
+// device-scope atomic and the streaming copy bandwidth used as HBM reference.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "llar.h"
+#include "llar_device.h"
+
+using namespace llar;
+
+namespace {
+
+__global__ void k_floor_chase(const uint32_t* ring, uint32_t ring_bytes, int hops, uint64_t* out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(ring, ring_bytes);
+  uint32_t idx = 0;
+  for (int i = 0; i < 64; ++i) idx = ld4_coh(rs, idx * 4u);  // warm the lines
+  idx = 0;
+  uint64_t t0 = wall_ticks();
+  for (int i = 0; i < hops; ++i) idx = ld4_coh(rs, idx * 4u);
+  uint64_t t1 = wall_ticks();
+  out[0] = t1 - t0;
+  out[1] = idx;
+}
+
+// Workgroups wa and wb play ping-pong with 16-byte coherent stores on two
+// separate 256-byte-apart lines; the others return at once.  Each wait is
+// bounded by `spin_limit` polls; out[1] / out[3] report success.
+__global__ void k_floor_pingpong(uint32_t* flags, int iters, int wa, int wb, long long spin_limit, uint64_t* out) {
+  const int b = blockIdx.x;
+  if (threadIdx.x != 0 || (b != wa && b != wb)) return;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(flags, 1024);
+  const bool ping = (b == wa);
+  const uint32_t mine = ping ? 0u : 256u, theirs = ping ? 256u : 0u;
+  long long spins = 0;
+  int ok = 1;
+  uint64_t t0 = wall_ticks();
+  for (int i = 1; i <= iters && ok; ++i) {
+    const uint32_t u = (uint32_t)i;
+    if (ping) st16_coh(rs, mine, u32x4{u, u, u, u});
+    while (true) {
+      u32x4 v = ld16_coh(rs, theirs);
+      if (v[3] == u) break;
+      if (++spins > spin_limit) {
+        ok = 0;
+        break;
+      }
+    }
+    if (!ping && ok) st16_coh(rs, mine, u32x4{u, u, u, u});
+  }
+  uint64_t t1 = wall_ticks();
+  if (ping) {
+    out[0] = t1 - t0;
+    out[1] = (uint64_t)ok;
+  } else {
+    out[3] = (uint64_t)ok;
+  }
+}
+
+__global__ void k_floor_atomic(uint32_t* p, int iters, uint64_t* out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  uint32_t v = 0;
+  uint64_t t0 = wall_ticks();
+  for (int i = 0; i < iters; ++i)
+    v = __hip_atomic_fetch_add(p + (v & 1u) * 64u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t t1 = wall_ticks();
+  out[0] = t1 - t0;
+  out[1] = v;
+}
+
+__global__ void k_floor_empty() {}
+
+__global__ void k_floor_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n) {
+  size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) dst[i] = __builtin_nontemporal_load(src + i);
+}
+
+double wall_hz_now() {
+  int dev = 0, wc = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 100e6;
+  if (hipDeviceGetAttribute(&wc, hipDeviceAttributeWallClockRate, dev) != hipSuccess || wc <= 0) return 100e6;
+  return wc * 1000.0;
+}
+
+}  // namespace
+
+extern "C" int llar_floor_measure(int kind, int param, double* value) {
+  if (!value || kind < 0 || kind > 4) return LLAR_ERR_ARG;
+  const double hz = wall_hz_now();
+  uint64_t* d_out = nullptr;
+  uint64_t h_out[4] = {0, 0, 0, 0};
+  if (hipMalloc(&d_out, 64) != hipSuccess) return LLAR_ERR_NOMEM;
+  int status = LLAR_OK;
+  hipError_t e = hipSuccess;
+  switch (kind) {
+    case 0: {  // L2 round trip: 64 lines of 128 B, pseudo-random cyclic order
+      const int lines = 64, hops = 4000;
+      std::vector<uint32_t> h(lines * 32, 0u);
+      std::vector<int> order(lines);
+      for (int i = 0; i < lines; ++i) order[i] = (i * 37) % lines;  // 37 is coprime with 64
+      for (int i = 0; i < lines; ++i) h[order[i] * 32] = (uint32_t)(order[(i + 1) % lines] * 32);
+      uint32_t* d = nullptr;
+      e = hipMalloc(&d, h.size() * 4);
+      if (e == hipSuccess) e = hipMemcpy(d, h.data(), h.size() * 4, hipMemcpyHostToDevice);
+      for (int rep = 0; rep < 2 && e == hipSuccess; ++rep) {
+        hipLaunchKernelGGL(k_floor_chase, dim3(1), dim3(64), 0, 0, d, (uint32_t)(h.size() * 4), hops, d_out);
+        e = hipDeviceSynchronize();
+      }
+      if (e == hipSuccess) e = hipMemcpy(h_out, d_out, 16, hipMemcpyDeviceToHost);
+      if (d) (void)hipFree(d);
+      *value = (double)h_out[0] / hz * 1e9 / hops;
+      break;
+    }
+    case 1: {  // store -> visibility, half a ping-pong round trip
+      if (param < 1 || param > 63) {
+        status = LLAR_ERR_ARG;
+        break;
+      }
+      uint32_t* d = nullptr;
+      const int iters = 2000;
+      e = hipMalloc(&d, 1024);
+      for (int rep = 0; rep < 2 && e == hipSuccess; ++rep) {
+        e = hipMemset(d, 0, 1024);
+        if (e == hipSuccess) {
+          hipLaunchKernelGGL(k_floor_pingpong, dim3(64), dim3(64), 0, 0, d, iters, 0, param, 4000000LL, d_out);
+          e = hipDeviceSynchronize();
+        }
+      }
+      if (e == hipSuccess) e = hipMemcpy(h_out, d_out, 32, hipMemcpyDeviceToHost);
+      if (d) (void)hipFree(d);
+      if (e == hipSuccess && (h_out[1] != 1 || h_out[3] != 1)) status = LLAR_ERR_TIMEOUT;
+      *value = (double)h_out[0] / hz * 1e9 / iters / 2.0;
+      break;
+    }
+    case 2: {  // empty launch interval
+      hipEvent_t a, b;
+      e = hipEventCreate(&a);
+      if (e == hipSuccess) e = hipEventCreate(&b);
+      const int n = 2000;
+      for (int i = 0; i < 100 && e == hipSuccess; ++i) hipLaunchKernelGGL(k_floor_empty, dim3(1), dim3(64), 0, 0);
+      if (e == hipSuccess) e = hipDeviceSynchronize();
+      if (e == hipSuccess) e = hipEventRecord(a, 0);
+      for (int i = 0; i < n && e == hipSuccess; ++i) hipLaunchKernelGGL(k_floor_empty, dim3(1), dim3(64), 0, 0);
+      if (e == hipSuccess) e = hipEventRecord(b, 0);
+      if (e == hipSuccess) e = hipEventSynchronize(b);
+      float ms = 0.f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+      *value = ms * 1e6 / n;
+      (void)hipEventDestroy(a);
+      (void)hipEventDestroy(b);
+      break;
+    }
+    case 3: {  // returning atomic latency
+      uint32_t* d = nullptr;
+      const int iters = 2000;
+      e = hipMalloc(&d, 1024);
+      if (e == hipSuccess) e = hipMemset(d, 0, 1024);
+      for (int rep = 0; rep < 2 && e == hipSuccess; ++rep) {
+        hipLaunchKernelGGL(k_floor_atomic, dim3(1), dim3(64), 0, 0, d, iters, d_out);
+        e = hipDeviceSynchronize();
+      }
+      if (e == hipSuccess) e = hipMemcpy(h_out, d_out, 16, hipMemcpyDeviceToHost);
+      if (d) (void)hipFree(d);
+      *value = (double)h_out[0] / hz * 1e9 / iters;
+      break;
+    }
+    case 4: {  // streaming copy, GB/s of read + write
+      if (param < 1 || param > 8192) {
+        status = LLAR_ERR_ARG;
+        break;
+      }
+      const size_t bytes = (size_t)param << 20;
+      const size_t n = bytes / 16;
+      u32x4 *s = nullptr, *t = nullptr;
+      e = hipMalloc(&s, bytes);
+      if (e == hipSuccess) e = hipMalloc(&t, bytes);
+      if (e == hipSuccess) e = hipMemset(s, 1, bytes);
+      hipEvent_t a, b;
+      if (e == hipSuccess) e = hipEventCreate(&a);
+      if (e == hipSuccess) e = hipEventCreate(&b);
+      const int reps = 10;
+      if (e == hipSuccess) {
+        hipLaunchKernelGGL(k_floor_copy, dim3(1024), dim3(256), 0, 0, s, t, n);
+        e = hipDeviceSynchronize();
+      }
+      if (e == hipSuccess) e = hipEventRecord(a, 0);
+      for (int i = 0; i < reps && e == hipSuccess; ++i) hipLaunchKernelGGL(k_floor_copy, dim3(1024), dim3(256), 0, 0, s, t, n);
+      if (e == hipSuccess) e = hipEventRecord(b, 0);
+      if (e == hipSuccess) e = hipEventSynchronize(b);
+      float ms = 0.f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+      *value = ms > 0.f ? 2.0 * (double)bytes * reps / (ms * 1e-3) / 1e9 : 0.0;
+      if (s) (void)hipFree(s);
+      if (t) (void)hipFree(t);
+      (void)hipEventDestroy(a);
+      (void)hipEventDestroy(b);
+      break;
+    }
+    default:
+      status = LLAR_ERR_ARG;
+  }
+  (void)hipFree(d_out);
+  if (status == LLAR_OK && e != hipSuccess) status = LLAR_ERR_HIP;
+  return status;
+}

@@ -1,0 +1,582 @@
+// llar_host.hip -- host side of the C ABI declared in include/llar.h:
+// communicator lifetime, staging layout, protocol choice, launch geometry,
+// options, status and debug exports.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "llar.h"
+#include "llar_device.h"
+#include "llar_internal.h"
+
+using namespace llar;
+
+namespace {
+
+thread_local int g_last_error = LLAR_OK;
+
+int fail(int status) {
+  g_last_error = status;
+  return status;
+}
+
+// Per-protocol size caps (bytes per rank) of the single-round protocols; the
+// pipelined protocols have no cap (their staging is chunk-sized).
+constexpr size_t kCapLL = 8ull << 20;
+constexpr size_t kCapSentinel = 16ull << 20;
+constexpr size_t kCapLL128 = 16ull << 20;
+constexpr size_t kCapChunk = 4ull << 20;  // largest chunk of the pipelined protocols
+
+size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
+
+struct Region {
+  uint8_t* ptr = nullptr;
+  size_t bytes = 0;
+  size_t parity_stride = 0;
+  size_t rank_stride = 0;
+};
+
+}  // namespace
+
+struct llar_comm {
+  int device = 0;
+  int n_ranks = 0;
+  int kind = 0;
+  size_t elem = 0;
+  size_t max_bytes = 0;
+  int cu_count = 0;
+  double wall_hz = 100e6;
+  Ctrl* ctrl = nullptr;
+  Region ll, sent, ll128, ll128_pipe, sent_pipe;
+  bool local_ok = false;  // workgroup b runs on XCD b % 8
+  // options
+  long long spin_timeout_us = 200000;
+  long long ll128_acc = 0;
+  long long chunk_bytes = 0;
+  long long slices = 0;
+  long long threads = 0;
+  long long placement = 0;
+  long long timing = 0;
+  long long keep_staging = 0;
+  long long debug_drop_rank = -1;
+  long long thr_sentinel = 2048;          // AUTO: LL below (<=) this many bytes
+  long long thr_ll128 = 1ll << 62;        // AUTO: one-shot Sentinel up to here (LL128 one round above)
+  long long thr_pipelined = 512ll << 10;  // AUTO: pipelined Sentinel above this
+};
+
+namespace {
+
+int elem_bytes_of(int dtype) { return dtype == LLAR_FP32 ? 4 : 2; }
+
+hipError_t alloc_region(Region& r, size_t bytes, int fill) {
+  r.bytes = bytes;
+  if (bytes == 0) return hipSuccess;
+  hipError_t e = hipMalloc(&r.ptr, bytes);
+  if (e != hipSuccess) {
+    r.ptr = nullptr;
+    return e;
+  }
+  return hipMemset(r.ptr, fill, bytes);
+}
+
+void free_region(Region& r) {
+  if (r.ptr) (void)hipFree(r.ptr);
+  r.ptr = nullptr;
+}
+
+hipError_t init_ctrl(llar_comm* h) {
+  Ctrl c;
+  memset(&c, 0, sizeof(c));
+  c.epoch = 1u;
+  for (int i = 0; i < kTimingRing; ++i) {
+    c.timing[i][0] = ~0ull;
+    c.timing[i][1] = 0ull;
+  }
+  return hipMemcpy(h->ctrl, &c, sizeof(c), hipMemcpyHostToDevice);
+}
+
+hipError_t reset_staging(llar_comm* h) {
+  hipError_t e = hipSuccess;
+  if (h->ll.ptr && (e = hipMemset(h->ll.ptr, 0, h->ll.bytes)) != hipSuccess) return e;
+  if (h->sent.ptr && (e = hipMemset(h->sent.ptr, 0xFF, h->sent.bytes)) != hipSuccess) return e;
+  if (h->ll128.ptr && (e = hipMemset(h->ll128.ptr, 0, h->ll128.bytes)) != hipSuccess) return e;
+  if (h->ll128_pipe.ptr && (e = hipMemset(h->ll128_pipe.ptr, 0, h->ll128_pipe.bytes)) != hipSuccess) return e;
+  if (h->sent_pipe.ptr && (e = hipMemset(h->sent_pipe.ptr, 0xFF, h->sent_pipe.bytes)) != hipSuccess) return e;
+  return hipDeviceSynchronize();
+}
+
+void destroy_all(llar_comm* h) {
+  if (!h) return;
+  (void)hipSetDevice(h->device);
+  (void)hipDeviceSynchronize();
+  free_region(h->ll);
+  free_region(h->sent);
+  free_region(h->ll128);
+  free_region(h->ll128_pipe);
+  free_region(h->sent_pipe);
+  if (h->ctrl) (void)hipFree(h->ctrl);
+  h->ctrl = nullptr;
+  delete h;
+}
+
+// Sentinel two-shot slot size: 16-byte vectors per (owner, sender) slot.
+uint32_t sentinel_shard_cap(size_t chunk_bytes, int n_ranks) {
+  return (uint32_t)(ceil_div(ceil_div(chunk_bytes, 16), (size_t)n_ranks) + 1);
+}
+
+size_t effective_chunk(const llar_comm* h, int proto) {
+  size_t c = (size_t)h->chunk_bytes;
+  if (c == 0) c = (proto == LLAR_LL128_PIPELINED) ? (64u << 10) : (1u << 20);
+  c = std::min(c, kCapChunk);
+  c = std::max(c, (size_t)1024);
+  c = (c / 16) * 16;  // whole 16-byte vectors
+  return c;
+}
+
+struct Geometry {
+  int kernel = 0;
+  int threads = 64;
+  int slices = 1;
+  int chunks = 1;
+  uint32_t chunk_elems = 0;
+  uint32_t placement = kPlaceSpread;
+};
+
+int clampi(long long v, int lo, int hi) { return (int)std::max<long long>(lo, std::min<long long>(hi, v)); }
+
+// Choose kernel and geometry.  Returns LLAR_OK or an error.
+int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
+  const size_t nbytes = n_elems * h->elem;
+  const int N = h->n_ranks;
+  switch (proto) {
+    case LLAR_LL:
+    case LLAR_SENTINEL: {
+      if (nbytes > (proto == LLAR_LL ? kCapLL : kCapSentinel)) return LLAR_ERR_UNSUPPORTED;
+      g.kernel = proto == LLAR_LL ? kKernOneShotLL : kKernOneShotSentinel;
+      size_t n_vec = ceil_div(nbytes, 16);
+      g.threads = h->threads ? (int)h->threads : (n_vec <= 4096 ? 64 : 256);
+      g.slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(n_vec, (size_t)g.threads), 1, 64);
+      break;
+    }
+    case LLAR_LL128:
+    case LLAR_LL128_PIPELINED: {
+      const bool acc16 = (h->ll128_acc == 1) && h->kind != kKindF32;
+      const size_t K = acc16 ? 63 : 31;
+      size_t chunk_elems;
+      if (proto == LLAR_LL128) {
+        if (nbytes > kCapLL128) return LLAR_ERR_UNSUPPORTED;
+        chunk_elems = std::max<size_t>(n_elems, 1);
+      } else {
+        chunk_elems = effective_chunk(h, proto) / h->elem;
+      }
+      g.kernel = acc16 ? kKernLL128Acc16 : kKernLL128Acc32;
+      g.chunk_elems = (uint32_t)chunk_elems;
+      g.chunks = (int)ceil_div(n_elems, chunk_elems);
+      size_t lines = ceil_div(std::min(chunk_elems, n_elems), K);
+      size_t per_owner = ceil_div(lines, (size_t)N);
+      g.threads = h->threads ? (int)h->threads : 64;
+      size_t per_wg = (size_t)(g.threads / 64) * 8;  // lines one workgroup covers per step
+      g.slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(per_owner, per_wg), 1, 64);
+      break;
+    }
+    case LLAR_SENTINEL_PIPELINED: {
+      size_t cb = effective_chunk(h, proto);
+      g.kernel = kKernSentinelPipe;
+      g.chunk_elems = (uint32_t)(cb / h->elem);
+      g.chunks = (int)ceil_div(n_elems, (size_t)g.chunk_elems);
+      size_t vecs = ceil_div(std::min(cb, nbytes), 16);
+      size_t per_owner = ceil_div(vecs, (size_t)N);
+      g.threads = h->threads ? (int)h->threads : 256;
+      g.slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(per_owner, (size_t)g.threads), 1, 32);
+      break;
+    }
+    default:
+      return LLAR_ERR_ARG;
+  }
+  // placement
+  uint32_t place = kPlaceSpread;
+  if (h->placement == 2) place = kPlaceLocal;
+  else if (h->placement == 0 && proto == LLAR_SENTINEL_PIPELINED) place = kPlaceLocal;
+  if (place == kPlaceLocal) {
+    if (!h->local_ok) place = kPlaceSpread;
+    else g.slices = (int)ceil_div((size_t)g.slices, 8) * 8;
+  }
+  if (place == kPlaceLocal && proto == LLAR_SENTINEL_PIPELINED) g.kernel = kKernSentinelPipeLocal;
+  g.placement = place;
+  if (g.threads != 64 && g.threads != 128 && g.threads != 256 && g.threads != 512) return LLAR_ERR_ARG;
+  return LLAR_OK;
+}
+
+int auto_protocol(const llar_comm* h, size_t nbytes) {
+  if ((long long)nbytes <= h->thr_sentinel && nbytes <= kCapLL) return LLAR_LL;
+  if ((long long)nbytes > h->thr_pipelined) return LLAR_SENTINEL_PIPELINED;
+  if ((long long)nbytes > h->thr_ll128 && nbytes <= kCapLL128) return LLAR_LL128;
+  if (nbytes <= kCapSentinel) return LLAR_SENTINEL;
+  return LLAR_SENTINEL_PIPELINED;
+}
+
+const Region* region_of(const llar_comm* h, int proto) {
+  switch (proto) {
+    case LLAR_LL: return &h->ll;
+    case LLAR_SENTINEL: return &h->sent;
+    case LLAR_LL128: return &h->ll128;
+    case LLAR_LL128_PIPELINED: return &h->ll128_pipe;
+    case LLAR_SENTINEL_PIPELINED: return &h->sent_pipe;
+    default: return nullptr;
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int llar_last_error(void) { return g_last_error; }
+
+const char* llar_status_string(int status) {
+  switch (status) {
+    case LLAR_OK: return "LLAR_OK";
+    case LLAR_ERR_ARG: return "LLAR_ERR_ARG: invalid argument";
+    case LLAR_ERR_UNSUPPORTED: return "LLAR_ERR_UNSUPPORTED: unsupported dtype, rank count or size";
+    case LLAR_ERR_NOMEM: return "LLAR_ERR_NOMEM: device allocation failed";
+    case LLAR_ERR_HIP: return "LLAR_ERR_HIP: HIP runtime error";
+    case LLAR_ERR_TIMEOUT: return "LLAR_ERR_TIMEOUT: a device poll exceeded its time limit";
+    case LLAR_ERR_DEVICE: return "LLAR_ERR_DEVICE: device-side protocol error";
+    default: return "unknown llar status";
+  }
+}
+
+llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes) {
+  if (n_ranks < 1 || (int)dtype < 0 || (int)dtype > 2 || max_bytes == 0) {
+    fail(LLAR_ERR_ARG);
+    return nullptr;
+  }
+  if (n_ranks > 8) {
+    fail(LLAR_ERR_UNSUPPORTED);
+    return nullptr;
+  }
+  llar_comm* h = new (std::nothrow) llar_comm();
+  if (!h) {
+    fail(LLAR_ERR_NOMEM);
+    return nullptr;
+  }
+  h->n_ranks = n_ranks;
+  h->kind = (int)dtype;
+  h->elem = (size_t)elem_bytes_of(dtype);
+  h->max_bytes = (max_bytes / h->elem) * h->elem;
+  if (h->max_bytes == 0) {
+    delete h;
+    fail(LLAR_ERR_ARG);
+    return nullptr;
+  }
+  hipError_t e = hipGetDevice(&h->device);
+  hipDeviceProp_t prop;
+  if (e == hipSuccess) e = hipGetDeviceProperties(&prop, h->device);
+  int wc = 0;
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&wc, hipDeviceAttributeWallClockRate, h->device);
+  if (e != hipSuccess) {
+    delete h;
+    fail(LLAR_ERR_HIP);
+    return nullptr;
+  }
+  h->cu_count = prop.multiProcessorCount;
+  h->wall_hz = wc > 0 ? wc * 1000.0 : 100e6;
+
+  const int N = n_ranks;
+  const size_t mb = h->max_bytes;
+  // LL: [parity][rank 1..N-1][vector][2 x 16 B]
+  size_t ll_vec = ceil_div(std::min(mb, kCapLL), 16);
+  h->ll.rank_stride = ll_vec * 32;
+  h->ll.parity_stride = h->ll.rank_stride * (size_t)std::max(N - 1, 1);
+  // Sentinel one-shot: [parity][rank 1..N-1][vector] 16 B
+  size_t s_vec = ceil_div(std::min(mb, kCapSentinel), 16);
+  h->sent.rank_stride = s_vec * 16;
+  h->sent.parity_stride = h->sent.rank_stride * (size_t)std::max(N - 1, 1);
+  // LL128 one round: [parity][line] 128 B, binary32 staging needs the most lines
+  size_t l_one = ceil_div(std::min(mb, kCapLL128) / h->elem, 31) + 1;
+  h->ll128.parity_stride = l_one * 128;
+  // LL128 pipelined: [parity][line] for the largest chunk
+  size_t l_pipe = ceil_div(std::min(mb, kCapChunk) / h->elem, 31) + 1;
+  h->ll128_pipe.parity_stride = l_pipe * 128;
+  // Sentinel pipelined: [parity][owner][sender][shard vector] 16 B
+  size_t cap = sentinel_shard_cap(std::min(mb, kCapChunk), N);
+  h->sent_pipe.parity_stride = (size_t)N * (size_t)N * cap * 16;
+
+  e = hipMalloc(&h->ctrl, sizeof(Ctrl));
+  if (e == hipSuccess) e = init_ctrl(h);
+  if (e == hipSuccess) e = alloc_region(h->ll, 2 * h->ll.parity_stride, 0);
+  if (e == hipSuccess) e = alloc_region(h->sent, 2 * h->sent.parity_stride, 0xFF);
+  if (e == hipSuccess) e = alloc_region(h->ll128, 2 * h->ll128.parity_stride, 0);
+  if (e == hipSuccess) e = alloc_region(h->ll128_pipe, 2 * h->ll128_pipe.parity_stride, 0);
+  if (e == hipSuccess) e = alloc_region(h->sent_pipe, 2 * h->sent_pipe.parity_stride, 0xFF);
+  // every region is addressed with 32-bit offsets
+  const Region* regs[] = {&h->ll, &h->sent, &h->ll128, &h->ll128_pipe, &h->sent_pipe};
+  for (const Region* r : regs)
+    if (r->bytes >= (1ull << 32)) {
+      destroy_all(h);
+      fail(LLAR_ERR_UNSUPPORTED);
+      return nullptr;
+    }
+  // placement check: the local placement needs workgroup b on XCD b % 8
+  if (e == hipSuccess) {
+    uint32_t* d = nullptr;
+    const int G = 64;
+    e = hipMalloc(&d, G * sizeof(uint32_t));
+    if (e == hipSuccess) e = launch_xcc_probe(d, G, 0);
+    std::vector<uint32_t> hx(G, 99u);
+    if (e == hipSuccess) e = hipMemcpy(hx.data(), d, G * sizeof(uint32_t), hipMemcpyDeviceToHost);
+    if (d) (void)hipFree(d);
+    if (e == hipSuccess) {
+      bool ok = true;
+      for (int i = 0; i < G; ++i) ok &= (hx[i] == (uint32_t)(i % 8));
+      h->local_ok = ok;
+    }
+  }
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    int st = (e == hipErrorOutOfMemory) ? LLAR_ERR_NOMEM : LLAR_ERR_HIP;
+    destroy_all(h);
+    fail(st);
+    return nullptr;
+  }
+  const char* env = getenv("LLAR_SPIN_TIMEOUT_US");
+  if (env) h->spin_timeout_us = std::max(1ll, atoll(env));
+  g_last_error = LLAR_OK;
+  return h;
+}
+
+int llar_destroy(llar_comm* h) {
+  if (!h) return LLAR_OK;
+  destroy_all(h);
+  return LLAR_OK;
+}
+
+int llar_select_protocol(llar_comm* h, size_t bytes) {
+  if (!h) return fail(LLAR_ERR_ARG);
+  return auto_protocol(h, bytes);
+}
+
+int llar_launch_geometry(llar_comm* h, size_t n_elems, llar_protocol protocol, int* grid, int* threads, int* slices,
+                         int* chunks) {
+  if (!h) return fail(LLAR_ERR_ARG);
+  int proto = protocol == LLAR_AUTO ? auto_protocol(h, n_elems * h->elem) : (int)protocol;
+  Geometry g;
+  int st = plan(h, n_elems, proto, g);
+  if (st != LLAR_OK) return fail(st);
+  if (grid) *grid = h->n_ranks * g.slices;
+  if (threads) *threads = g.threads;
+  if (slices) *slices = g.slices;
+  if (chunks) *chunks = g.chunks;
+  return LLAR_OK;
+}
+
+int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t n_elems, llar_dtype dtype,
+                   llar_protocol protocol, void* stream) {
+  if (!h || !partials) return fail(LLAR_ERR_ARG);
+  if ((int)dtype != h->kind) return fail(LLAR_ERR_ARG);
+  if (n_elems == 0) return LLAR_OK;
+  if (!out || !aligned16(out)) return fail(LLAR_ERR_ARG);
+  if (n_elems > h->max_bytes / h->elem) return fail(LLAR_ERR_ARG);
+  for (int r = 0; r < h->n_ranks; ++r)
+    if (!partials[r] || !aligned16(partials[r])) return fail(LLAR_ERR_ARG);
+  if ((int)protocol < 0 || (int)protocol > LLAR_SENTINEL_PIPELINED) return fail(LLAR_ERR_ARG);
+
+  const size_t nbytes = n_elems * h->elem;
+  const int proto = protocol == LLAR_AUTO ? auto_protocol(h, nbytes) : (int)protocol;
+  Geometry g;
+  int st = plan(h, n_elems, proto, g);
+  if (st != LLAR_OK) return fail(st);
+  const Region* reg = region_of(h, proto);
+
+  LaunchSpec ls;
+  memset(&ls, 0, sizeof(ls));
+  ls.kind = h->kind;
+  ls.n_ranks = h->n_ranks;
+  ls.kernel = g.kernel;
+  ls.threads = g.threads;
+  ls.grid = h->n_ranks * g.slices;
+
+  // every workgroup must be resident at once: consumers spin on producers
+  int occ = occupancy(h->kind, h->n_ranks, g.kernel, g.threads);
+  if (occ <= 0) return fail(LLAR_ERR_HIP);
+  if (ls.grid > occ * h->cu_count) return fail(LLAR_ERR_UNSUPPORTED);
+
+  const uint64_t spin = (uint64_t)((double)h->spin_timeout_us * 1e-6 * h->wall_hz);
+  if (g.kernel == kKernOneShotLL || g.kernel == kKernOneShotSentinel) {
+    OneShotArgs& a = ls.oneshot;
+    for (int r = 0; r < h->n_ranks; ++r) a.part[r] = static_cast<const uint8_t*>(partials[r]);
+    a.out = static_cast<uint8_t*>(out);
+    a.stage = reg->ptr;
+    a.ctrl = h->ctrl;
+    a.nbytes = nbytes;
+    a.spin_limit = spin;
+    a.n_vec = (uint32_t)ceil_div(nbytes, 16);
+    a.stage_bytes = (uint32_t)reg->bytes;
+    a.parity_stride = (uint32_t)reg->parity_stride;
+    a.rank_stride = (uint32_t)reg->rank_stride;
+    a.grid = (uint32_t)ls.grid;
+    a.slices = (uint32_t)g.slices;
+    a.placement = g.placement;
+    a.timing = h->timing ? 1u : 0u;
+    a.keep = h->keep_staging ? 1u : 0u;
+    a.drop_rank = h->debug_drop_rank < 0 ? 0xFFFFFFFFu : (uint32_t)h->debug_drop_rank;
+  } else {
+    TwoShotArgs& a = ls.twoshot;
+    for (int r = 0; r < h->n_ranks; ++r) a.part[r] = static_cast<const uint8_t*>(partials[r]);
+    a.out = static_cast<uint8_t*>(out);
+    a.stage = reg->ptr;
+    a.ctrl = h->ctrl;
+    a.n = n_elems;
+    a.spin_limit = spin;
+    a.chunk_elems = g.chunk_elems;
+    a.n_chunks = (uint32_t)g.chunks;
+    a.stage_bytes = (uint32_t)reg->bytes;
+    a.parity_stride = (uint32_t)reg->parity_stride;
+    a.shard_cap = (proto == LLAR_SENTINEL_PIPELINED) ? sentinel_shard_cap(std::min(h->max_bytes, kCapChunk), h->n_ranks) : 0u;
+    a.grid = (uint32_t)ls.grid;
+    a.slices = (uint32_t)g.slices;
+    a.placement = g.placement;
+    a.timing = h->timing ? 1u : 0u;
+    a.keep = h->keep_staging ? 1u : 0u;
+    a.drop_rank = h->debug_drop_rank < 0 ? 0xFFFFFFFFu : (uint32_t)h->debug_drop_rank;
+    // the chunk must fit the staging that was allocated
+    if (proto == LLAR_SENTINEL_PIPELINED) {
+      uint32_t need = sentinel_shard_cap((size_t)g.chunk_elems * h->elem, h->n_ranks);
+      if (need > a.shard_cap) return fail(LLAR_ERR_UNSUPPORTED);
+    } else {
+      size_t K = (g.kernel == kKernLL128Acc16) ? 63 : 31;
+      size_t lines = ceil_div(std::min<size_t>(g.chunk_elems, n_elems), K);
+      if (lines * 128 > reg->parity_stride) return fail(LLAR_ERR_UNSUPPORTED);
+    }
+  }
+  if (!reg->ptr) return fail(LLAR_ERR_UNSUPPORTED);
+  hipError_t e = launch(ls, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LLAR_ERR_HIP);
+  return LLAR_OK;
+}
+
+int llar_get_device_status(llar_comm* h, uint32_t* bits) {
+  if (!h) return fail(LLAR_ERR_ARG);
+  if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
+  uint32_t s = 0;
+  if (hipMemcpy(&s, &h->ctrl->status, sizeof(s), hipMemcpyDeviceToHost) != hipSuccess) return fail(LLAR_ERR_HIP);
+  if (bits) *bits = s;
+  if (s & kStatusTimeout) return LLAR_ERR_TIMEOUT;
+  if (s) return LLAR_ERR_DEVICE;
+  return LLAR_OK;
+}
+
+int llar_clear_device_status(llar_comm* h) {
+  if (!h) return fail(LLAR_ERR_ARG);
+  if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
+  if (init_ctrl(h) != hipSuccess) return fail(LLAR_ERR_HIP);
+  if (reset_staging(h) != hipSuccess) return fail(LLAR_ERR_HIP);
+  return LLAR_OK;
+}
+
+static long long* option_slot(llar_comm* h, const char* key) {
+  struct {
+    const char* name;
+    long long llar_comm::*field;
+  } static const table[] = {
+      {"spin_timeout_us", &llar_comm::spin_timeout_us},
+      {"ll128_acc", &llar_comm::ll128_acc},
+      {"chunk_bytes", &llar_comm::chunk_bytes},
+      {"slices", &llar_comm::slices},
+      {"threads", &llar_comm::threads},
+      {"placement", &llar_comm::placement},
+      {"timing", &llar_comm::timing},
+      {"keep_staging", &llar_comm::keep_staging},
+      {"debug_drop_rank", &llar_comm::debug_drop_rank},
+      {"auto_threshold_sentinel", &llar_comm::thr_sentinel},
+      {"auto_threshold_ll128", &llar_comm::thr_ll128},
+      {"auto_threshold_pipelined", &llar_comm::thr_pipelined},
+  };
+  for (const auto& t : table)
+    if (strcmp(t.name, key) == 0) return &(h->*(t.field));
+  return nullptr;
+}
+
+int llar_set_option(llar_comm* h, const char* key, long long value) {
+  if (!h || !key) return fail(LLAR_ERR_ARG);
+  long long* slot = option_slot(h, key);
+  if (!slot) return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "spin_timeout_us") == 0 && value < 1) return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "ll128_acc") == 0 && (value < 0 || value > 1)) return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "chunk_bytes") == 0 && (value < 0 || (size_t)value > kCapChunk)) return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "slices") == 0 && (value < 0 || value > 1024)) return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "threads") == 0 && !(value == 0 || value == 64 || value == 128 || value == 256 || value == 512))
+    return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "placement") == 0 && (value < 0 || value > 2)) return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "placement") == 0 && value == 2 && !h->local_ok) return fail(LLAR_ERR_UNSUPPORTED);
+  if ((strcmp(key, "timing") == 0 || strcmp(key, "keep_staging") == 0) && (value < 0 || value > 1))
+    return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "debug_drop_rank") == 0 && (value < -1 || value >= h->n_ranks)) return fail(LLAR_ERR_ARG);
+  *slot = value;
+  return LLAR_OK;
+}
+
+int llar_get_option(llar_comm* h, const char* key, long long* value) {
+  if (!h || !key || !value) return fail(LLAR_ERR_ARG);
+  long long* slot = option_slot(h, key);
+  if (!slot) return fail(LLAR_ERR_ARG);
+  *value = *slot;
+  return LLAR_OK;
+}
+
+size_t llar_staging_bytes(llar_comm* h, llar_protocol protocol) {
+  if (!h) return 0;
+  const Region* r = region_of(h, (int)protocol);
+  return r ? r->bytes : 0;
+}
+
+int llar_debug_copy_staging(llar_comm* h, llar_protocol protocol, void* host_dst, size_t bytes) {
+  if (!h || !host_dst) return fail(LLAR_ERR_ARG);
+  const Region* r = region_of(h, (int)protocol);
+  if (!r || !r->ptr || bytes > r->bytes) return fail(LLAR_ERR_ARG);
+  if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
+  if (hipMemcpy(host_dst, r->ptr, bytes, hipMemcpyDeviceToHost) != hipSuccess) return fail(LLAR_ERR_HIP);
+  return LLAR_OK;
+}
+
+int llar_get_epoch(llar_comm* h, uint32_t* epoch) {
+  if (!h || !epoch) return fail(LLAR_ERR_ARG);
+  if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
+  if (hipMemcpy(epoch, &h->ctrl->epoch, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess) return fail(LLAR_ERR_HIP);
+  return LLAR_OK;
+}
+
+int llar_get_timing(llar_comm* h, uint64_t* host_dst, int count) {
+  if (!h || !host_dst || count < 0) return fail(LLAR_ERR_ARG);
+  if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
+  Ctrl c;
+  if (hipMemcpy(&c, h->ctrl, sizeof(Ctrl), hipMemcpyDeviceToHost) != hipSuccess) return fail(LLAR_ERR_HIP);
+  int n = std::min(count, kTimingRing - 1);
+  // the current epoch's slot has not run yet; the last n epochs precede it
+  uint32_t e = c.epoch;
+  int written = 0;
+  for (int i = n; i >= 1; --i) {
+    uint32_t ep = e;
+    for (int k = 0; k < i; ++k) ep = (ep == 1u) ? 0xFFFFFFFFu : ep - 1u;
+    host_dst[2 * written] = c.timing[ep % kTimingRing][0];
+    host_dst[2 * written + 1] = c.timing[ep % kTimingRing][1];
+    ++written;
+  }
+  return written;
+}
+
+double llar_wallclock_hz(void) {
+  int dev = 0, wc = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0.0;
+  if (hipDeviceGetAttribute(&wc, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0.0;
+  return wc * 1000.0;
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// llar_internal.h -- kernel argument blocks and launch descriptors shared by
+// the HIP kernels and the host library (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace llar {
+
+struct Ctrl;
+
+// element kinds (same numbering as llar_dtype)
+constexpr int kKindF32 = 0;
+constexpr int kKindF16 = 1;
+constexpr int kKindBF16 = 2;
+
+// wire formats of the one-shot kernel
+constexpr int kWireLL = 0;
+constexpr int kWireSentinel = 1;
+
+// placements of (rank, slice) onto workgroup ids
+constexpr uint32_t kPlaceSpread = 1;
+constexpr uint32_t kPlaceLocal = 2;
+
+// kernel variants
+enum KernelId : int {
+  kKernOneShotLL = 0,
+  kKernOneShotSentinel = 1,
+  kKernLL128Acc32 = 2,
+  kKernLL128Acc16 = 3,
+  kKernSentinelPipe = 4,
+  kKernSentinelPipeLocal = 5,
+  kKernCount = 6
+};
+
+struct OneShotArgs {
+  const uint8_t* part[8];
+  uint8_t* out;
+  uint8_t* stage;        // base of this protocol's staging (both parities)
+  Ctrl* ctrl;
+  uint64_t nbytes;       // bytes per rank
+  uint64_t spin_limit;   // wall-clock ticks
+  uint32_t n_vec;        // 16-byte vectors per rank (last one may be partial)
+  uint32_t stage_bytes;  // size of the staging region (buffer descriptor bound)
+  uint32_t parity_stride;
+  uint32_t rank_stride;  // bytes per sending rank per parity
+  uint32_t grid;
+  uint32_t slices;
+  uint32_t placement;
+  uint32_t timing;
+  uint32_t keep;
+  uint32_t drop_rank;    // tests: this rank's producers write nothing (0xFFFFFFFF = none)
+};
+
+struct TwoShotArgs {
+  const uint8_t* part[8];
+  uint8_t* out;
+  uint8_t* stage;
+  Ctrl* ctrl;
+  uint64_t n;            // elements per rank
+  uint64_t spin_limit;
+  uint32_t chunk_elems;  // elements per rank per chunk
+  uint32_t n_chunks;
+  uint32_t stage_bytes;
+  uint32_t parity_stride;
+  uint32_t shard_cap;    // Sentinel: 16-byte vectors per (owner, sender) slot
+  uint32_t grid;
+  uint32_t slices;
+  uint32_t placement;
+  uint32_t timing;
+  uint32_t keep;
+  uint32_t drop_rank;
+};
+
+struct LaunchSpec {
+  int kind;
+  int n_ranks;
+  int kernel;
+  int grid;
+  int threads;
+  OneShotArgs oneshot;
+  TwoShotArgs twoshot;
+};
+
+hipError_t launch(const LaunchSpec& ls, hipStream_t stream);
+int occupancy(int kind, int n_ranks, int kernel, int threads);
+hipError_t launch_xcc_probe(uint32_t* out, int grid, hipStream_t stream);
+
+}  // namespace llar

@@ -1,0 +1,90 @@
+"""CPU checks of the C-ABI library: it builds for gfx950, loads, exports every
+function include/llar.h declares, and its host-side argument checks work
+without a GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llar.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import message_allreduce_amd as m
+    if not os.path.exists(m.library_path):
+        from message_allreduce_amd import _build
+        _build.build()
+    return m.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"\b(llar_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_header_declares_the_three_core_calls():
+    names = declared_functions()
+    for core in ("llar_create", "llar_allreduce", "llar_destroy"):
+        assert core in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    import message_allreduce_amd as m
+    out = subprocess.run(["nm", "-D", "--defined-only", m.library_path], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (llar_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+    # the binding lists exactly the header's functions
+    assert sorted(m.EXPORTED_SYMBOLS) == declared_functions()
+
+
+def test_library_is_built_for_gfx950(L):
+    import message_allreduce_amd as m
+    blob = open(m.library_path, "rb").read()
+    # the embedded device code object carries its offload target id
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_status_strings(L):
+    import message_allreduce_amd as m
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        s = m.llar_status_string(code)
+        assert s.startswith(m.STATUS[code])
+
+
+def test_null_handle_is_rejected_without_touching_the_gpu(L):
+    import message_allreduce_amd as m
+    assert L.llar_allreduce(None, None, None, 16, 0, 0, None) == -1
+    assert L.llar_destroy(None) == 0
+    assert L.llar_set_option(None, b"timing", 1) == -1
+    assert L.llar_get_device_status(None, None) == -1
+    assert L.llar_staging_bytes(None, 1) == 0
+    v = ctypes.c_double(0)
+    assert L.llar_floor_measure(99, 0, ctypes.byref(v)) == -1
+    assert L.llar_floor_measure(-1, 0, ctypes.byref(v)) == -1
+
+
+def test_create_rejects_bad_arguments(L):
+    import message_allreduce_amd as m
+    assert not L.llar_create(0, 0, 1024) and L.llar_last_error() == -1
+    assert not L.llar_create(2, 7, 1024) and L.llar_last_error() == -1
+    assert not L.llar_create(2, 0, 0) and L.llar_last_error() == -1
+    assert not L.llar_create(9, 0, 1024) and L.llar_last_error() == -2
+
+
+def test_package_has_no_cpu_fallback():
+    # the product package must not import the oracle or compute on the host
+    pkg = os.path.join(ROOT, "message_allreduce_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in src and "from oracle" not in src, f
+                assert "oracle/" not in src, f

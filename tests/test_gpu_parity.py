@@ -1,0 +1,345 @@
+"""GPU parity of the HIP protocols against the CPU oracle, through the C ABI.
+
+LL and Sentinel (one-shot and pipelined) must match the oracle bit for bit
+(binary64 rank-order sums, one rounding).  The atomic LL128 protocol is
+non-deterministic: it must stay within |got - oracle| <= 1e-3 + rtol*|oracle|
+(rtol 1e-5 fp32, 2e-3 fp16, 1.6e-2 bf16), and be bit-exact on integer data.
+Every repetition draws fresh inputs (seed [workload, rep]) so that a consumer
+reading the previous call's staging would fail.
+"""
+import numpy as np
+import pytest
+import torch
+
+import message_allreduce_amd as llar
+import oracle
+from oracle import F32, F16, BF16, models
+from workloads import WORKLOADS, make_partials, workload_partials
+
+from gpu_util import CODE, TORCH_DT, assert_exact, assert_tol, run, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+ALL_PROTOCOLS = ["ll", "sentinel", "ll128", "ll128_pipelined", "sentinel_pipelined"]
+EXACT = {"ll", "sentinel", "sentinel_pipelined"}
+
+
+def comm_for(n_ranks, dt, max_bytes, **opts):
+    c = llar.Communicator(n_ranks, TORCH_DT[dt], max_bytes)
+    c.set_option("spin_timeout_us", 100_000)
+    for k, v in opts.items():
+        c.set_option(k, v)
+    return c
+
+
+def check(got, want, dt, proto, what):
+    if proto in EXACT:
+        assert_exact(got, want, dt, what)
+    else:
+        assert_tol(got, want, dt, what)
+
+
+# --------------------------------------------------------------------------- the five workloads
+def test_workload1_ll_n2_fp32_1000_reps():
+    w = WORKLOADS[1]
+    dt = CODE[w.dtype]
+    with comm_for(w.n_ranks, dt, w.bytes_per_rank) as c:
+        out = torch.empty(w.n_elems, dtype=TORCH_DT[dt], device="cuda")
+        for rep in range(w.reps):
+            bits = workload_partials(w, rep)
+            got = run(c, bits, "ll", dt, out=out)
+            assert_exact(got, oracle.allreduce(bits, dt), dt, "rep %d" % rep)
+        # LL staging of the last call: both 8-byte halves carry the epoch
+        e_last = c.epoch() - 1
+        stage = c.staging(llar.LL).view(np.uint32)
+        n_lines = 2 * ((w.bytes_per_rank + 15) // 16)
+        par = (e_last & 1) * (stage.size // 2)
+        lines = stage[par: par + n_lines * 4].reshape(n_lines, 4)
+        want_lines = models.ll_pack(models.ll_payload_words(bits[1]), e_last)
+        assert np.array_equal(lines, want_lines[:n_lines])
+
+
+@pytest.mark.parametrize("acc", [0, 1], ids=["fp32_staging", "bf16_staging"])
+def test_workload2_ll128_n4_bf16(acc):
+    w = WORKLOADS[2]
+    dt = CODE[w.dtype]
+    with comm_for(w.n_ranks, dt, w.bytes_per_rank, ll128_acc=acc) as c:
+        out = torch.empty(w.n_elems, dtype=TORCH_DT[dt], device="cuda")
+        for rep in range(300):
+            bits = workload_partials(w, rep)
+            got = run(c, bits, "ll128", dt, out=out)
+            assert_tol(got, oracle.allreduce(bits, dt), dt, "rep %d" % rep)
+        stage = c.staging(llar.LL128)
+        assert not stage.any(), "LL128 staging must be zero after every call"
+
+
+def test_workload3_sentinel_n8_fp16():
+    w = WORKLOADS[3]
+    dt = CODE[w.dtype]
+    with comm_for(w.n_ranks, dt, w.bytes_per_rank) as c:
+        out = torch.empty(w.n_elems, dtype=TORCH_DT[dt], device="cuda")
+        for rep in range(200):
+            bits = workload_partials(w, rep)
+            got = run(c, bits, "sentinel", dt, out=out)
+            assert_exact(got, oracle.allreduce(bits, dt), dt, "rep %d" % rep)
+            if rep % 50 == 0:
+                stage = c.staging(llar.SENTINEL).view(np.uint16)
+                assert (stage == 0xFFFF).all(), "sentinel staging must be reset after use"
+
+
+def test_workload4_ll128_pipelined_n8_fp32():
+    w = WORKLOADS[4]
+    dt = CODE[w.dtype]
+    with comm_for(w.n_ranks, dt, w.bytes_per_rank, chunk_bytes=w.chunk_bytes) as c:
+        assert c.geometry(w.n_elems, llar.LL128_PIPELINED)["chunks"] == 64
+        out = torch.empty(w.n_elems, dtype=TORCH_DT[dt], device="cuda")
+        for rep in range(12):
+            bits = workload_partials(w, rep)
+            got = run(c, bits, "ll128_pipelined", dt, out=out)
+            assert_tol(got, oracle.allreduce(bits, dt), dt, "rep %d" % rep)
+        assert not c.staging(llar.LL128_PIPELINED).any()
+
+
+def test_workload5_sweep_auto_n8_bf16():
+    w = WORKLOADS[5]
+    dt = CODE[w.dtype]
+    top = max(w.sweep_bytes)
+    with comm_for(w.n_ranks, dt, top) as c:
+        for nbytes in w.sweep_bytes:
+            n = nbytes // 2
+            bits = make_partials(w.cfg_id, nbytes, w.n_ranks, w.dtype, n, w.dist, w.scale)
+            proto = c.select_protocol(nbytes)
+            got = run(c, bits, "auto", dt)
+            want = oracle.allreduce(bits, dt)
+            name = [k for k, v in llar.PROTOCOLS.items() if v == proto][0]
+            print("sweep %9d B -> %s" % (nbytes, name), flush=True)
+            check(got, want, dt, name, "%d bytes (%s)" % (nbytes, name))
+
+
+# --------------------------------------------------------------------------- every protocol, ragged sizes
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("proto", ALL_PROTOCOLS)
+def test_protocols_ragged_sizes(proto, dtype):
+    dt = CODE[dtype]
+    sizes = [1, 2, 3, 7, 8, 9, 31, 33, 63, 65, 127, 1000, 4097, 8191, 20001]
+    n_ranks = 8 if dtype != "fp32" else 5
+    with comm_for(n_ranks, dt, 65536 * 4, chunk_bytes=4096) as c:
+        for i, n in enumerate(sizes):
+            bits = make_partials(100 + dt, i, n_ranks, dtype, n, "normal", 1.0)
+            got = run(c, bits, proto, dt)
+            check(got, oracle.allreduce(bits, dt), dt, proto, "n=%d" % n)
+
+
+@pytest.mark.parametrize("n_ranks", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("proto", ALL_PROTOCOLS)
+def test_protocols_every_rank_count(proto, n_ranks):
+    dt = BF16
+    n = 5000
+    with comm_for(n_ranks, dt, n * 2, chunk_bytes=2048) as c:
+        for rep in range(3):
+            bits = make_partials(200 + n_ranks, rep, n_ranks, "bf16", n, "normal", 0.5)
+            got = run(c, bits, proto, dt)
+            check(got, oracle.allreduce(bits, dt), dt, proto, "N=%d rep %d" % (n_ranks, rep))
+
+
+@pytest.mark.parametrize("proto", ALL_PROTOCOLS)
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_integer_data_is_exact_for_every_protocol(proto, dtype):
+    dt = CODE[dtype]
+    n = 9000
+    with comm_for(8, dt, n * 4, chunk_bytes=4096) as c:
+        bits = make_partials(300 + dt, 0, 8, dtype, n, "integer", 1.0)
+        got = run(c, bits, proto, dt)
+        assert_exact(got, oracle.allreduce(bits, dt), dt, proto)
+
+
+@pytest.mark.parametrize("proto", ["ll", "sentinel", "sentinel_pipelined"])
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_special_values_bit_exact(proto, dtype):
+    dt = CODE[dtype]
+    n_ranks, n = 4, 4096
+    g = np.random.default_rng(7 + dt)
+    bits = make_partials(400 + dt, 0, n_ranks, dtype, n, "normal", 1.0)
+    specials = {
+        F32: [0x7F800000, 0xFF800000, 0x7FC00000, 0xFFFFFFFF, 0x80000000, 0x00000001, 0x80000001, 0x7F7FFFFF, 0x00800000],
+        F16: [0x7C00, 0xFC00, 0x7E00, 0xFFFF, 0x8000, 0x0001, 0x8001, 0x7BFF, 0x0400],
+        BF16: [0x7F80, 0xFF80, 0x7FC0, 0xFFFF, 0x8000, 0x0001, 0x8001, 0x7F7F, 0x0080],
+    }[dt]
+    for r in range(n_ranks):
+        idx = g.choice(n, size=400, replace=False)
+        bits[r, idx] = g.choice(specials, size=400)
+    # every element where all ranks hold -0, and overflow to +-Inf
+    bits[:, :8] = specials[4]
+    bits[:, 8:16] = specials[7]
+    with comm_for(n_ranks, dt, n * 4, chunk_bytes=2048) as c:
+        got = run(c, bits, proto, dt)
+        want = oracle.allreduce(bits, dt)
+        assert_exact(got, want, dt, proto)
+        if proto == "sentinel":
+            stage = c.staging(llar.SENTINEL)
+            assert (stage == 0xFF).all()
+
+
+@pytest.mark.parametrize("proto", ["ll", "sentinel", "sentinel_pipelined"])
+def test_subnormal_sums_bit_exact(proto):
+    for dtype in ("fp32", "fp16", "bf16"):
+        dt = CODE[dtype]
+        n = 2048
+        g = np.random.default_rng(11)
+        mant = g.integers(0, 1 << (23 if dt == F32 else 10 if dt == F16 else 7), size=(3, n))
+        sign = g.integers(0, 2, size=(3, n)) << (31 if dt == F32 else 15)
+        bits = (mant | sign).astype(oracle.BITS_DTYPE[dt])
+        with comm_for(3, dt, n * 4, chunk_bytes=1024) as c:
+            got = run(c, bits, proto, dt)
+            assert_exact(got, oracle.allreduce(bits, dt), dt, "%s %s" % (proto, dtype))
+
+
+# --------------------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("proto", ALL_PROTOCOLS)
+def test_in_place_output_aliases_a_partial(proto):
+    dt = BF16
+    n = 6000
+    bits = make_partials(500, 0, 4, "bf16", n, "normal", 1.0)
+    want = oracle.allreduce(bits, dt)
+    for alias in (0, 3):
+        with comm_for(4, dt, n * 2, chunk_bytes=2048) as c:
+            parts = [to_device(bits[r], dt) for r in range(4)]
+            c.allreduce(parts, parts[alias], proto)
+            torch.cuda.synchronize()
+            assert c.device_status()[0] == 0
+            check(to_host(parts[alias], dt), want, dt, proto, "alias %d" % alias)
+
+
+def test_zero_elements_is_a_noop():
+    with comm_for(2, F32, 1024) as c:
+        parts = [torch.zeros(4, device="cuda") for _ in range(2)]
+        out = torch.full((4,), 7.0, device="cuda")
+        e0 = c.epoch()
+        c.allreduce(parts, out[:0], "ll")
+        torch.cuda.synchronize()
+        assert c.epoch() == e0 and (out == 7.0).all()
+
+
+def test_argument_errors():
+    with comm_for(2, F32, 1024) as c:
+        parts = [torch.zeros(256, device="cuda") for _ in range(2)]
+        out = torch.zeros(256, device="cuda")
+        h = c.h
+        ptrs = [p.data_ptr() for p in parts]
+        assert llar.llar_allreduce(h, ptrs, out.data_ptr(), 257, F32, 0, 0) == -1          # over max_bytes
+        assert llar.llar_allreduce(h, ptrs, out.data_ptr(), 16, F16, 0, 0) == -1           # wrong dtype
+        assert llar.llar_allreduce(h, [ptrs[0] + 4, ptrs[1]], out.data_ptr(), 16, F32, 0, 0) == -1  # misaligned
+        assert llar.llar_allreduce(h, ptrs, out.data_ptr() + 8, 16, F32, 0, 0) == -1       # misaligned out
+        assert llar.llar_allreduce(h, ptrs, out.data_ptr(), 16, F32, 9, 0) == -1           # bad protocol
+        assert llar.llar_set_option(h, "no_such_option", 1) == -1
+        assert llar.llar_set_option(h, "threads", 96) == -1
+
+
+@pytest.mark.parametrize("proto", ALL_PROTOCOLS)
+def test_maximum_size(proto):
+    dt = F16
+    n = (1 << 20) // 2  # 1 MiB per rank, the communicator's maximum
+    bits = make_partials(600, 0, 8, "fp16", n, "normal", 0.02)
+    with comm_for(8, dt, n * 2) as c:
+        got = run(c, bits, proto, dt)
+        check(got, oracle.allreduce(bits, dt), dt, proto, "max size")
+
+
+def test_non_default_stream_and_back_to_back_calls():
+    dt = BF16
+    n = 8192
+    with comm_for(8, dt, n * 2) as c:
+        s = torch.cuda.Stream()
+        outs, wants = [], []
+        with torch.cuda.stream(s):
+            for rep in range(20):
+                bits = make_partials(700, rep, 8, "bf16", n, "normal", 1.0)
+                parts = [to_device(bits[r], dt) for r in range(8)]
+                out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+                c.allreduce(parts, out, ["ll", "sentinel", "sentinel_pipelined", "auto"][rep % 4], stream=s)
+                outs.append((out, parts))
+                wants.append(oracle.allreduce(bits, dt))
+        s.synchronize()
+        assert c.device_status()[0] == 0
+        for i, ((out, _), want) in enumerate(zip(outs, wants)):
+            assert_exact(to_host(out, dt), want, dt, "call %d" % i)
+
+
+def test_epoch_advances_once_per_call_and_timing_records():
+    with comm_for(4, BF16, 16384, timing=1) as c:
+        bits = make_partials(800, 0, 4, "bf16", 8192, "normal", 1.0)
+        parts = [to_device(bits[r], BF16) for r in range(4)]
+        out = torch.empty(8192, dtype=torch.bfloat16, device="cuda")
+        e0 = c.epoch()
+        for proto in ALL_PROTOCOLS:
+            c.allreduce(parts, out, proto)
+        torch.cuda.synchronize()
+        assert c.epoch() == e0 + len(ALL_PROTOCOLS)
+        recs = c.timing(len(ALL_PROTOCOLS))
+        assert len(recs) == len(ALL_PROTOCOLS)
+        hz = llar.llar_wallclock_hz()
+        for t0, t1 in recs:
+            assert t0 != 2**64 - 1 and t1 > t0
+            assert (t1 - t0) / hz < 0.05
+
+
+@pytest.mark.parametrize("proto", ALL_PROTOCOLS)
+def test_lost_contribution_times_out_and_recovers(proto):
+    """A rank whose producers write nothing (forced from the host) makes the
+    consumers' bounded polls expire: the kernel ends, the status word says
+    TIMEOUT, and after a reset the communicator works again."""
+    dt = BF16
+    n = 4096
+    bits = make_partials(900, 0, 4, "bf16", n, "normal", 1.0)
+    with comm_for(4, dt, n * 2, chunk_bytes=2048) as c:
+        c.set_option("spin_timeout_us", 2000)
+        c.set_option("debug_drop_rank", 2)
+        parts = [to_device(bits[r], dt) for r in range(4)]
+        out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        c.allreduce(parts, out, proto)
+        torch.cuda.synchronize()
+        st, status_bits = c.device_status()
+        assert st == -5 and (status_bits & 1), (st, status_bits)
+        c.clear_device_status()
+        c.set_option("debug_drop_rank", -1)
+        c.set_option("spin_timeout_us", 100_000)
+        got = run(c, bits, proto, dt)
+        check(got, oracle.allreduce(bits, dt), dt, proto, "after recovery")
+
+
+@pytest.mark.parametrize("placement", [1, 2])
+@pytest.mark.parametrize("chunk", [1024, 65536, 1 << 20])
+def test_sentinel_pipelined_chunks_and_placements(placement, chunk):
+    dt = BF16
+    n = (3 << 20) // 2 + 37  # 3 MiB + a ragged tail
+    bits = make_partials(1000, chunk, 8, "bf16", n, "normal", 1.0)
+    with comm_for(8, dt, n * 2, chunk_bytes=chunk, placement=placement) as c:
+        got = run(c, bits, "sentinel_pipelined", dt)
+        assert_exact(got, oracle.allreduce(bits, dt), dt, "chunk %d placement %d" % (chunk, placement))
+        assert (c.staging(llar.SENTINEL_PIPELINED) == 0xFF).all()
+
+
+@pytest.mark.parametrize("threads", [64, 128, 256, 512])
+@pytest.mark.parametrize("proto", ALL_PROTOCOLS)
+def test_workgroup_sizes(proto, threads):
+    dt = F32
+    n = 30000
+    bits = make_partials(1100, threads, 6, "fp32", n, "uniform", 1.0)
+    with comm_for(6, dt, n * 4, threads=threads, chunk_bytes=8192) as c:
+        got = run(c, bits, proto, dt)
+        check(got, oracle.allreduce(bits, dt), dt, proto, "threads %d" % threads)
+
+
+def test_ll128_keep_staging_matches_line_model():
+    """With integer data every atomic order gives the same staged sums: the
+    kept staging must equal the line model bit for bit (flag slot == N)."""
+    dt = BF16
+    n_ranks, n = 4, 3000
+    bits = make_partials(1200, 0, n_ranks, "bf16", n, "integer", 1.0)
+    with comm_for(n_ranks, dt, n * 2, keep_staging=1) as c:
+        run(c, bits, "ll128", dt)
+        g = models.LL128Geometry(n, n_ranks, 4)
+        stage = c.staging(llar.LL128)[: g.staging_bytes].view(np.float32).reshape(g.lines, g.slots)
+        model = models.ll128_staging_image(bits, dt, F32)
+        assert np.array_equal(stage.astype(np.float64), model)
+        assert (stage[:, 0] == n_ranks).all()
