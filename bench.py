@@ -1,0 +1,264 @@
+"""Benchmark of the emulated-rank AllReduce on one MI355X.
+
+Default run (one JSON line on stdout):
+  * value: microseconds per reduce, per call, of the AUTO protocol on N = 8
+    emulated ranks x 16 KiB bf16 (8192 elements per rank), inputs resident in
+    HBM, K back-to-back calls on one stream timed with HIP events;
+  * latency: the same reduce measured device-side (first workgroup start to
+    last workgroup end) against the single-GPU speed-of-light floor
+    2 x (L2 round trip) + (cross-XCD store visibility), all measured here;
+  * bandwidth_64MiB: the 64 MiB-per-rank reduce, effective GB/s over the
+    algorithmic bytes (N + 1) x 64 MiB, and the HBM roofline of that kernel;
+  * cpu_baseline: the CPU oracle on the same 16 KiB workload.
+
+--sweep adds the 128 B .. 64 MiB size sweep for every protocol and the
+alpha + beta * size fit (written to --sweep-out).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per reduce (16 KB bf16, N=8) vs SoL floor; GB/s at 64 MB"
+HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+N_RANKS = 8
+SMALL_BYTES = 16 << 10
+BIG_BYTES = 64 << 20
+PROTO_NAMES = {0: "auto", 1: "ll", 2: "sentinel", 3: "ll128", 4: "ll128_pipelined", 5: "sentinel_pipelined"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def device_inputs(cfg_id, n_ranks, n, dist, scale, rep=0):
+    import torch
+    from workloads import make_partials
+    bits = make_partials(cfg_id, rep, n_ranks, "bf16", n, dist, scale)
+    parts = [torch.from_numpy(bits[r].view(np.int16).copy()).view(torch.bfloat16).cuda() for r in range(n_ranks)]
+    return bits, parts
+
+
+def time_calls(comm, parts, out, proto, steps, warmup, stream):
+    """Per-call microseconds of `steps` back-to-back calls (HIP events on the
+    launch stream), after `warmup` untimed calls."""
+    import torch
+    call = comm.prepare(parts, out, proto, stream=stream)
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+    st, bits = comm.device_status()
+    if st != 0:
+        raise RuntimeError("device status %d (bits %#x) during %s" % (st, bits, proto))
+    return a.elapsed_time(b) * 1e3 / steps
+
+
+def device_side_us(comm, parts, out, proto, calls, stream):
+    """Median device-side microseconds (first workgroup start to last
+    workgroup end, wall clock) over `calls` timed calls."""
+    import torch
+    import message_allreduce_amd as llar
+    calls = min(calls, 60)
+    comm.set_option("timing", 1)
+    try:
+        with torch.cuda.stream(stream):
+            for _ in range(calls):
+                comm.allreduce(parts, out, proto, stream=stream)
+        torch.cuda.synchronize()
+        recs = comm.timing(calls)
+    finally:
+        comm.set_option("timing", 0)
+    hz = llar.llar_wallclock_hz()
+    d = sorted((t1 - t0) / hz * 1e6 for t0, t1 in recs if t1 > t0)
+    return statistics.median(d), d[0]
+
+
+def measure_floor():
+    import message_allreduce_amd as llar
+    rt = statistics.median(llar.llar_floor_measure(0) for _ in range(3))
+    stores = {}
+    for b in range(1, 8):
+        stores[b] = llar.llar_floor_measure(1, b)
+    same_xcd = llar.llar_floor_measure(1, 8)
+    t_store = statistics.mean(stores.values())
+    launch = llar.llar_floor_measure(2)
+    atomic = llar.llar_floor_measure(3)
+    floor_ns = 2 * rt + t_store
+    return {
+        "t_l2_round_trip_ns": round(rt, 1),
+        "t_store_cross_xcd_ns": round(t_store, 1),
+        "t_store_by_xcd_ns": {str(k): round(v, 1) for k, v in stores.items()},
+        "t_store_same_xcd_ns": round(same_xcd, 1),
+        "floor_us": round(floor_ns / 1e3, 4),
+        "floor_same_xcd_us": round((2 * rt + same_xcd) / 1e3, 4),
+        "empty_launch_us": round(launch / 1e3, 3),
+        "atomic_latency_ns": round(atomic, 1),
+    }
+
+
+def cpu_baseline(seconds=10.0):
+    """The oracle as it stands, timed on one host thread over repeated
+    reduces of the same 16 KiB x 8 input."""
+    import oracle
+    from workloads import make_partials
+    bits = make_partials(5, 0, N_RANKS, "bf16", SMALL_BYTES // 2, "normal", 1.0)
+    oracle.allreduce(bits, oracle.BF16)
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        oracle.allreduce(bits, oracle.BF16)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(dt / n * 1e6, 2), "unit": "us per reduce", "cores": 1, "kind": "oracle",
+            "sample": "%d reduces of the 16 KiB x 8 bf16 workload in %.1f s on one host thread" % (n, dt)}
+
+
+def run_sweep(comm_cls, args, stream):
+    import torch
+    import message_allreduce_amd as llar
+    from oracle.models import fit_alpha_beta
+    sizes = [1 << k for k in range(7, 27)]
+    res = {"sizes": sizes, "protocols": {}}
+    rows = {PROTO_NAMES[p]: [] for p in (1, 2, 3, 4, 5, 0)}
+    comm = comm_cls(N_RANKS, torch.bfloat16, BIG_BYTES)
+    try:
+        for nbytes in sizes:
+            n = nbytes // 2
+            _, parts = device_inputs(5, N_RANKS, n, "normal", 1.0, rep=nbytes)
+            out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+            steps = 200 if nbytes <= (1 << 20) else 20
+            for proto in (1, 2, 3, 4, 5, 0):
+                name = PROTO_NAMES[proto]
+                if proto in (1, 2, 3) and nbytes > (8 << 20):
+                    continue
+                try:
+                    us = time_calls(comm, parts, out, proto, steps, 10, stream)
+                    dev_med, dev_min = device_side_us(comm, parts, out, proto, 40 if nbytes <= (1 << 20) else 10, stream)
+                except llar.LlarError as e:
+                    log("sweep %s %d: %s" % (name, nbytes, e))
+                    continue
+                gbps = (N_RANKS + 1) * nbytes / (us * 1e-6) / 1e9
+                rows[name].append({"bytes": nbytes, "us_per_call": round(us, 3), "device_us": round(dev_med, 3),
+                                   "device_us_min": round(dev_min, 3), "GBps": round(gbps, 1),
+                                   "selected": PROTO_NAMES[comm.select_protocol(nbytes)] if proto == 0 else name})
+                log("sweep %-18s %9d B  %8.2f us/call  %8.2f us device  %8.1f GB/s" % (name, nbytes, us, dev_med, gbps))
+            del parts, out
+        for name, rr in rows.items():
+            if rr:
+                a, b = fit_alpha_beta([r["bytes"] for r in rr], [r["us_per_call"] for r in rr])
+                res["protocols"][name] = {"rows": rr, "alpha_us": a, "beta_us_per_byte": b}
+    finally:
+        comm.close()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--big-steps", type=int, default=50)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--sweep-out", default=os.path.join(ROOT, "gpurun_out", "sweep.json"))
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the N ranks are emulated inside a single MI355X "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import message_allreduce_amd as llar
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+
+    log("floor microbenchmarks")
+    floor = measure_floor()
+    log(json.dumps(floor))
+
+    # ---- headline: 16 KiB bf16, N = 8, AUTO
+    n_small = SMALL_BYTES // 2
+    _, parts = device_inputs(5, N_RANKS, n_small, "normal", 1.0)
+    out = torch.empty(n_small, dtype=torch.bfloat16, device="cuda")
+    comm = llar.Communicator(N_RANKS, torch.bfloat16, BIG_BYTES)
+    proto_small = comm.select_protocol(SMALL_BYTES)
+    geo_small = comm.geometry(n_small, 0)
+    log("16 KiB: protocol %s geometry %s" % (PROTO_NAMES[proto_small], geo_small))
+    torch.cuda.synchronize()
+    us = time_calls(comm, parts, out, 0, args.steps, args.warmup, stream)
+    dev_med, dev_min = device_side_us(comm, parts, out, 0, 60, stream)
+    log("16 KiB: %.3f us per call, device-side median %.3f us (min %.3f)" % (us, dev_med, dev_min))
+
+    # ---- 64 MiB bf16, N = 8, AUTO
+    n_big = BIG_BYTES // 2
+    _, parts_big = device_inputs(5, N_RANKS, n_big, "normal", 1.0)
+    out_big = torch.empty(n_big, dtype=torch.bfloat16, device="cuda")
+    proto_big = comm.select_protocol(BIG_BYTES)
+    geo_big = comm.geometry(n_big, 0)
+    us_big = time_calls(comm, parts_big, out_big, 0, args.big_steps, 5, stream)
+    alg_bytes = (N_RANKS + 1) * BIG_BYTES
+    gbps = alg_bytes / (us_big * 1e-6) / 1e9
+    log("64 MiB: protocol %s geometry %s: %.1f us, %.1f GB/s" % (PROTO_NAMES[proto_big], geo_big, us_big, gbps))
+    copy_gbps = llar.llar_floor_measure(4, 1024)
+    comm.close()
+
+    result = {
+        "metric": METRIC,
+        "value": round(us, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: N(0,1) partials drawn from seed [5, 0], resident in HBM",
+        "config": {"workload": "allreduce, N=8 emulated ranks x 16 KiB bf16 (8192 elements per rank), AUTO protocol",
+                   "n_ranks": N_RANKS, "bytes_per_rank": SMALL_BYTES, "protocol": PROTO_NAMES[proto_small],
+                   "geometry": geo_small},
+        "latency": dict(floor, **{"device_us_median": round(dev_med, 3), "device_us_min": round(dev_min, 3),
+                                  "device_over_floor": round(dev_med / floor["floor_us"], 3),
+                                  "per_call_us": round(us, 3)}),
+        "bandwidth_64MiB": {"protocol": PROTO_NAMES[proto_big], "geometry": geo_big, "us": round(us_big, 2),
+                            "GBps": round(gbps, 1), "algorithmic_bytes": alg_bytes,
+                            "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                            "copy_GBps_measured": round(copy_gbps, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "%s, 64 MiB x 8 bf16" % PROTO_NAMES[proto_big]},
+    }
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    if args.sweep:
+        log("sweep")
+        sw = run_sweep(llar.Communicator, args, stream)
+        os.makedirs(os.path.dirname(args.sweep_out), exist_ok=True)
+        with open(args.sweep_out, "w") as f:
+            json.dump(sw, f, indent=1)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -119,13 +119,22 @@ int llar_clear_device_status(llar_comm* h);
  *   "ll128_acc"        LL128 staging type: 0 = binary32 (default), 1 = the I/O type (16-bit packed)
  *   "chunk_bytes"      per-rank chunk of the pipelined protocols (0 = tuned default)
  *   "slices"           workgroups per rank (0 = tuned default)
- *   "threads"          threads per workgroup: 64, 128, 256 or 512 (0 = tuned default)
+ *   "threads"          threads per workgroup: 64, 128, 256 or 512 (0 = tuned default); the
+ *                      pipelined Sentinel splits a workgroup into producer and consumer waves
+ *                      and needs at least 128
  *   "placement"        0 = auto, 1 = spread (rank r on XCD r mod 8), 2 = local (one slice's ranks share an XCD)
  *   "timing"           1 = record device-side start/end wall-clock per call (see llar_get_timing)
  *   "keep_staging"     1 = LL128/Sentinel consumers do not reset staging (tests only; the next call is invalid)
  *   "debug_drop_rank"  tests: the producers of this rank write nothing, so consumers time out (-1 = none)
+ *   "trace"            1 = one-shot kernels record per-workgroup phase stamps (see llar_get_trace)
+ *   "device_epoch"     1 = always read the device-resident epoch; otherwise the host numbers
+ *                      stream-ordered calls and the device epoch is used only on a stream that is
+ *                      being captured into a graph (replays then never reuse an epoch)
  *   "auto_threshold_sentinel", "auto_threshold_ll128", "auto_threshold_pipelined"
  *                      AUTO size boundaries in bytes per rank
+ * llar_get_option also answers "local_placement_ok" (read-only): 1 when
+ * workgroup ids equal mod 8 were seen to share an XCD, which the local
+ * placement requires.
  * Returns LLAR_ERR_ARG for an unknown key or a bad value. */
 int llar_set_option(llar_comm* h, const char* key, long long value);
 int llar_get_option(llar_comm* h, const char* key, long long* value);
@@ -140,7 +149,8 @@ int llar_debug_copy_staging(llar_comm* h, llar_protocol protocol, void* host_dst
 /* Size in bytes of that staging region (0 if none). */
 size_t llar_staging_bytes(llar_comm* h, llar_protocol protocol);
 
-/* Current device epoch (synchronises first). */
+/* Epoch the next call will use (host-numbered, or the device-resident one
+ * when the last call read it); synchronises first. */
 int llar_get_epoch(llar_comm* h, uint32_t* epoch);
 
 /* Device-side timing of the last `count` timed calls (option "timing"):
@@ -150,6 +160,13 @@ int llar_get_epoch(llar_comm* h, uint32_t* epoch);
  * number of records written (>= 0) or an error. */
 int llar_get_timing(llar_comm* h, uint64_t* host_dst, int count);
 double llar_wallclock_hz(void);
+
+/* Phase stamps of the last one-shot call made with option "trace": for each
+ * workgroup 8 uint64 -- wall ticks at entry, epoch known, first input loaded,
+ * first store acknowledged (producer) or all slots ready (consumer), output
+ * acknowledged (consumer), exit; then xcc | rank << 8 | slice << 16; spare.
+ * Returns the number of workgroup records written (<= max_records). */
+int llar_get_trace(llar_comm* h, uint64_t* host_dst, int max_records);
 
 /* Workgroup geometry the library would launch for this call (for tests and
  * tuning): writes grid size, threads per workgroup, slices and chunks. */

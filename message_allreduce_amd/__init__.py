@@ -26,7 +26,7 @@ __all__ = [
     "llar_set_option", "llar_get_option", "llar_get_device_status", "llar_clear_device_status",
     "llar_select_protocol", "llar_debug_copy_staging", "llar_staging_bytes", "llar_get_epoch",
     "llar_get_timing", "llar_wallclock_hz", "llar_launch_geometry", "llar_floor_measure",
-    "llar_status_string", "llar_last_error", "Communicator", "EXPORTED_SYMBOLS",
+    "llar_status_string", "llar_last_error", "llar_get_trace", "Communicator", "EXPORTED_SYMBOLS",
 ]
 
 FP32, FP16, BF16 = 0, 1, 2
@@ -42,6 +42,7 @@ EXPORTED_SYMBOLS = (
     "llar_get_device_status", "llar_clear_device_status", "llar_set_option", "llar_get_option",
     "llar_select_protocol", "llar_debug_copy_staging", "llar_staging_bytes", "llar_get_epoch",
     "llar_get_timing", "llar_wallclock_hz", "llar_launch_geometry", "llar_floor_measure",
+    "llar_get_trace",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +85,7 @@ def lib() -> ctypes.CDLL:
         "llar_wallclock_hz": (ctypes.c_double, []),
         "llar_launch_geometry": (i32, [vp, sz, i32, ip, ip, ip, ip]),
         "llar_floor_measure": (i32, [i32, i32, ctypes.POINTER(ctypes.c_double)]),
+        "llar_get_trace": (i32, [vp, u64p, i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -174,6 +176,15 @@ def llar_get_timing(h: int, count: int):
     return [(arr[2 * i], arr[2 * i + 1]) for i in range(n)]
 
 
+def llar_get_trace(h: int, max_records: int = 4096):
+    """(n_workgroups, 8) uint64 phase stamps of the last traced one-shot call."""
+    import numpy as np
+    buf = np.zeros((int(max_records), 8), dtype=np.uint64)
+    n = _check(lib().llar_get_trace(h, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), int(max_records)),
+               "llar_get_trace")
+    return buf[:n]
+
+
 def llar_wallclock_hz() -> float:
     return lib().llar_wallclock_hz()
 
@@ -218,6 +229,36 @@ class Communicator:
         import torch
         if isinstance(protocol, str):
             protocol = PROTOCOLS[protocol]
+        self._validate(partials, out)
+        n = out.numel()
+        s = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+        st = llar_allreduce(self.h, [p.data_ptr() for p in partials], out.data_ptr(), n, self.dtype, protocol, s)
+        return _check(st, "llar_allreduce")
+
+    def prepare(self, partials, out, protocol=AUTO, stream=None):
+        """Validate and marshal the arguments once; return a no-argument
+        callable that issues exactly this llar_allreduce call (for tight
+        loops where per-call Python checks would dominate)."""
+        import torch
+        if isinstance(protocol, str):
+            protocol = PROTOCOLS[protocol]
+        self._validate(partials, out)
+        s = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+        fn = lib().llar_allreduce
+        arr = (ctypes.c_void_p * len(partials))(*[p.data_ptr() for p in partials])
+        args = (ctypes.c_void_p(self.h), arr, ctypes.c_void_p(out.data_ptr()), ctypes.c_size_t(out.numel()),
+                ctypes.c_int(self.dtype), ctypes.c_int(protocol), ctypes.c_void_p(s))
+        keep = (partials, out)  # the tensors stay alive as long as the callable
+
+        def call():
+            st = fn(*args)
+            if st < 0:
+                raise LlarError(st, "llar_allreduce")
+            return keep is not None
+
+        return call
+
+    def _validate(self, partials, out):
         if len(partials) != self.n_ranks:
             raise ValueError("expected %d partials" % self.n_ranks)
         n = out.numel()
@@ -226,9 +267,6 @@ class Communicator:
                 raise ValueError("partials must be contiguous device tensors of the communicator's dtype")
         if not (out.is_cuda and out.is_contiguous() and _dtype_code(out) == self.dtype):
             raise ValueError("out must be a contiguous device tensor of the communicator's dtype")
-        s = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
-        st = llar_allreduce(self.h, [p.data_ptr() for p in partials], out.data_ptr(), n, self.dtype, protocol, s)
-        return _check(st, "llar_allreduce")
 
     def set_option(self, key: str, value: int):
         return _check(llar_set_option(self.h, key, value), "llar_set_option(%s)" % key)

@@ -40,10 +40,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // ---- coherent accesses to staging -------------------------------------------
+// The buffer-load intrinsics are "read-only memory" to the compiler: inside a
+// polling loop with no store it may hoist the load out of the loop, or delete
+// a loop it cannot prove to terminate.  The empty volatile asm with a memory
+// clobber in front of every coherent load is a side effect that forces a
+// fresh load on each iteration (loads issued back to back still overlap).
 __device__ __forceinline__ u32x4 ld16_coh(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  asm volatile("" ::: "memory");
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1);
 }
+__device__ __forceinline__ u32x2 ld8_coh(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  asm volatile("" ::: "memory");
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolSc1);
+}
 __device__ __forceinline__ uint32_t ld4_coh(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  asm volatile("" ::: "memory");
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCpolSc1);
 }
 __device__ __forceinline__ void st16_coh(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
@@ -56,6 +67,11 @@ template <bool kLocal>
 __device__ __forceinline__ void st16_stage(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
   if constexpr (kLocal) st16_l2(r, off, v);
   else st16_coh(r, off, v);
+}
+template <bool kLocal>
+__device__ __forceinline__ void st8_stage(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  if constexpr (kLocal) __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpolNone);
+  else __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpolSc1);
 }
 
 // ---- ordering -----------------------------------------------------------------
@@ -101,12 +117,9 @@ __device__ __forceinline__ float round_odd_f32(double d) {
   }
   return f;
 }
-// binary32 -> bfloat16 round to nearest even on the bit pattern; NaN stays NaN.
+// binary32 -> bfloat16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return ((u >> 16) | 0x0040u) & 0xFFFFu;
-  uint32_t lsb = (u >> 16) & 1u;
-  return ((u + 0x7FFFu + lsb) >> 16) & 0xFFFFu;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ uint32_t rne_bf16(double d) { return f32_to_bf16_rne(round_odd_f32(d)); }
 __device__ __forceinline__ uint32_t rne_f16(double d) {
@@ -174,6 +187,16 @@ __device__ __forceinline__ u32x4 sentinel_canon(u32x4 v) {
   }
   return v;
 }
+// true when no element of the 8-byte unit still holds the sentinel
+template <int kKind>
+__device__ __forceinline__ bool sentinel_ready8(const u32x2& v) {
+  if constexpr (Elem<kKind>::kBytes == 4) {
+    return (v[0] != 0xFFFFFFFFu) & (v[1] != 0xFFFFFFFFu);
+  } else {
+    return ((v[0] & 0xFFFFu) != 0xFFFFu) & ((v[0] >> 16) != 0xFFFFu) & ((v[1] & 0xFFFFu) != 0xFFFFu) &
+           ((v[1] >> 16) != 0xFFFFu);
+  }
+}
 // true when no element of the vector still holds the sentinel
 template <int kKind>
 __device__ __forceinline__ bool sentinel_ready(const u32x4& v) {
@@ -202,18 +225,33 @@ struct Ctrl {
   uint64_t timing[kTimingRing][2];  // per epoch slot: first start, last end (wall ticks)
 };
 
-__device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return (e + 1u == 0u) ? 1u : e + 1u; }
+// Epochs: host-numbered calls use 1 .. 2^31-1, device-numbered (graph
+// capture) calls use 2^31 + (1 .. 2^31-1); 0 never occurs.
+__host__ __device__ __forceinline__ uint32_t next_host_epoch(uint32_t e) {
+  uint32_t n = (e + 1u) & 0x7FFFFFFFu;
+  return n == 0u ? 1u : n;
+}
+__host__ __device__ __forceinline__ uint32_t next_device_epoch(uint32_t e) {
+  return 0x80000000u | next_host_epoch(e & 0x7FFFFFFFu);
+}
 
-// Bounded poll helper: true while the wave may keep spinning.
-struct Spin {
+// Bounded poll helper.  expired() is called after every failed poll: it
+// backs off for kSleep x 64 cycles (s_sleep), so that waiting waves do not
+// flood the L2 with re-polls that the producers' traffic has to queue
+// behind, and every 16th call checks the wall-clock limit.
+template <int kSleep>
+struct SpinT {
   uint64_t t0, limit;
   uint32_t n;
-  __device__ __forceinline__ Spin(uint64_t lim) : t0(wall_ticks()), limit(lim), n(0) {}
+  __device__ __forceinline__ SpinT(uint64_t lim) : t0(wall_ticks()), limit(lim), n(0) {}
   __device__ __forceinline__ bool expired() {
+    if constexpr (kSleep > 0) __builtin_amdgcn_s_sleep(kSleep);
     if ((++n & 15u) != 0u) return false;
     return wall_ticks() - t0 > limit;
   }
 };
+using Spin = SpinT<1>;       // latency-critical polls (about 27 ns back-off)
+using SpinBulk = SpinT<8>;   // polls of the bandwidth pipeline (about 210 ns)
 
 __device__ __forceinline__ void raise_status(Ctrl* c, uint32_t bits) {
   __hip_atomic_fetch_or(&c->status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -32,6 +32,10 @@ constexpr size_t kCapLL = 8ull << 20;
 constexpr size_t kCapSentinel = 16ull << 20;
 constexpr size_t kCapLL128 = 16ull << 20;
 constexpr size_t kCapChunk = 4ull << 20;  // largest chunk of the pipelined protocols
+constexpr int kTraceMaxWgs = 4096;
+// The pipelined Sentinel keeps 4 staging buffers so that a producer may run
+// one chunk further ahead of its consumer (safe with >= 2 * lag + 2 buffers).
+constexpr uint32_t kSentinelPipeBuffers = 4;
 
 size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
 
@@ -55,6 +59,10 @@ struct llar_comm {
   Ctrl* ctrl = nullptr;
   Region ll, sent, ll128, ll128_pipe, sent_pipe;
   bool local_ok = false;  // workgroup b runs on XCD b % 8
+  uint64_t* trace = nullptr;  // kTraceMaxWgs x kTraceWords stamps of the last traced one-shot call
+  int trace_grid = 0;
+  uint32_t host_epoch = 1;         // epoch of the next host-numbered call
+  bool last_call_device = false;   // the last call read the device-resident epoch
   // options
   long long spin_timeout_us = 200000;
   long long ll128_acc = 0;
@@ -65,6 +73,8 @@ struct llar_comm {
   long long timing = 0;
   long long keep_staging = 0;
   long long debug_drop_rank = -1;
+  long long trace_on = 0;
+  long long device_epoch = 0;  // 1: always read the device-resident epoch
   long long thr_sentinel = 2048;          // AUTO: LL below (<=) this many bytes
   long long thr_ll128 = 1ll << 62;        // AUTO: one-shot Sentinel up to here (LL128 one round above)
   long long thr_pipelined = 512ll << 10;  // AUTO: pipelined Sentinel above this
@@ -93,7 +103,7 @@ void free_region(Region& r) {
 hipError_t init_ctrl(llar_comm* h) {
   Ctrl c;
   memset(&c, 0, sizeof(c));
-  c.epoch = 1u;
+  c.epoch = 0x80000001u;  // first device-numbered epoch
   for (int i = 0; i < kTimingRing; ++i) {
     c.timing[i][0] = ~0ull;
     c.timing[i][1] = 0ull;
@@ -122,6 +132,8 @@ void destroy_all(llar_comm* h) {
   free_region(h->sent_pipe);
   if (h->ctrl) (void)hipFree(h->ctrl);
   h->ctrl = nullptr;
+  if (h->trace) (void)hipFree(h->trace);
+  h->trace = nullptr;
   delete h;
 }
 
@@ -134,6 +146,7 @@ size_t effective_chunk(const llar_comm* h, int proto) {
   size_t c = (size_t)h->chunk_bytes;
   if (c == 0) c = (proto == LLAR_LL128_PIPELINED) ? (64u << 10) : (1u << 20);
   c = std::min(c, kCapChunk);
+  c = std::min(c, ceil_div(h->max_bytes, 16) * 16);  // never beyond one whole message
   c = std::max(c, (size_t)1024);
   c = (c / 16) * 16;  // whole 16-byte vectors
   return c;
@@ -142,7 +155,8 @@ size_t effective_chunk(const llar_comm* h, int proto) {
 struct Geometry {
   int kernel = 0;
   int threads = 64;
-  int slices = 1;
+  int slices = 1;       // slices that carry work
+  int grid_slices = 1;  // slices the grid covers (local placement pads to 8)
   int chunks = 1;
   uint32_t chunk_elems = 0;
   uint32_t placement = kPlaceSpread;
@@ -159,9 +173,10 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
     case LLAR_SENTINEL: {
       if (nbytes > (proto == LLAR_LL ? kCapLL : kCapSentinel)) return LLAR_ERR_UNSUPPORTED;
       g.kernel = proto == LLAR_LL ? kKernOneShotLL : kKernOneShotSentinel;
-      size_t n_vec = ceil_div(nbytes, 16);
-      g.threads = h->threads ? (int)h->threads : (n_vec <= 4096 ? 64 : 256);
-      g.slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(n_vec, (size_t)g.threads), 1, 64);
+      // the consumer works in 8-byte units: 2 per 16-byte vector
+      size_t units = 2 * ceil_div(nbytes, 16);
+      g.threads = h->threads ? (int)h->threads : 256;
+      g.slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(units, (size_t)g.threads), 1, 64);
       break;
     }
     case LLAR_LL128:
@@ -192,22 +207,31 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
       g.chunks = (int)ceil_div(n_elems, (size_t)g.chunk_elems);
       size_t vecs = ceil_div(std::min(cb, nbytes), 16);
       size_t per_owner = ceil_div(vecs, (size_t)N);
-      g.threads = h->threads ? (int)h->threads : 256;
-      g.slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(per_owner, (size_t)g.threads), 1, 32);
+      // half the waves produce, half consume: one owner-slice vector per
+      // consumer lane per chunk
+      g.threads = h->threads ? (int)h->threads : 512;
+      if (g.threads < 128) return LLAR_ERR_ARG;
+      // measured on MI355X (64 MiB x 8 bf16): 1 MiB chunks, 512 threads and
+      // 32 slices per rank (one workgroup per CU) stream best
+      g.slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(per_owner, (size_t)g.threads / 2), 1, 32);
       break;
     }
     default:
       return LLAR_ERR_ARG;
   }
-  // placement
+  // placement: local (the ranks of a slice share one XCD's L2) for the
+  // Sentinel and LL exchanges, spread (rank r on XCD r) for the atomic one
   uint32_t place = kPlaceSpread;
   if (h->placement == 2) place = kPlaceLocal;
-  else if (h->placement == 0 && proto == LLAR_SENTINEL_PIPELINED) place = kPlaceLocal;
+  else if (h->placement == 0 && proto != LLAR_LL128 && proto != LLAR_LL128_PIPELINED) place = kPlaceLocal;
+  if (place == kPlaceLocal && !h->local_ok) place = kPlaceSpread;
+  g.grid_slices = g.slices;
   if (place == kPlaceLocal) {
-    if (!h->local_ok) place = kPlaceSpread;
-    else g.slices = (int)ceil_div((size_t)g.slices, 8) * 8;
+    g.grid_slices = (int)ceil_div((size_t)g.slices, 8) * 8;
+    if (g.kernel == kKernSentinelPipe) g.kernel = kKernSentinelPipeLocal;
+    if (g.kernel == kKernOneShotLL) g.kernel = kKernOneShotLLLocal;
+    if (g.kernel == kKernOneShotSentinel) g.kernel = kKernOneShotSentinelLocal;
   }
-  if (place == kPlaceLocal && proto == LLAR_SENTINEL_PIPELINED) g.kernel = kKernSentinelPipeLocal;
   g.placement = place;
   if (g.threads != 64 && g.threads != 128 && g.threads != 256 && g.threads != 512) return LLAR_ERR_ARG;
   return LLAR_OK;
@@ -303,19 +327,22 @@ llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes) {
   size_t l_one = ceil_div(std::min(mb, kCapLL128) / h->elem, 31) + 1;
   h->ll128.parity_stride = l_one * 128;
   // LL128 pipelined: [parity][line] for the largest chunk
-  size_t l_pipe = ceil_div(std::min(mb, kCapChunk) / h->elem, 31) + 1;
+  const size_t chunk_cap = std::max(std::min(ceil_div(mb, 16) * 16, kCapChunk), (size_t)1024);
+  size_t l_pipe = ceil_div(chunk_cap / h->elem, 31) + 1;
   h->ll128_pipe.parity_stride = l_pipe * 128;
   // Sentinel pipelined: [parity][owner][sender][shard vector] 16 B
-  size_t cap = sentinel_shard_cap(std::min(mb, kCapChunk), N);
+  size_t cap = sentinel_shard_cap(chunk_cap, N);
   h->sent_pipe.parity_stride = (size_t)N * (size_t)N * cap * 16;
 
   e = hipMalloc(&h->ctrl, sizeof(Ctrl));
   if (e == hipSuccess) e = init_ctrl(h);
+  if (e == hipSuccess) e = hipMalloc(&h->trace, (size_t)kTraceMaxWgs * kTraceWords * sizeof(uint64_t));
+  if (e == hipSuccess) e = hipMemset(h->trace, 0, (size_t)kTraceMaxWgs * kTraceWords * sizeof(uint64_t));
   if (e == hipSuccess) e = alloc_region(h->ll, 2 * h->ll.parity_stride, 0);
   if (e == hipSuccess) e = alloc_region(h->sent, 2 * h->sent.parity_stride, 0xFF);
   if (e == hipSuccess) e = alloc_region(h->ll128, 2 * h->ll128.parity_stride, 0);
   if (e == hipSuccess) e = alloc_region(h->ll128_pipe, 2 * h->ll128_pipe.parity_stride, 0);
-  if (e == hipSuccess) e = alloc_region(h->sent_pipe, 2 * h->sent_pipe.parity_stride, 0xFF);
+  if (e == hipSuccess) e = alloc_region(h->sent_pipe, kSentinelPipeBuffers * h->sent_pipe.parity_stride, 0xFF);
   // every region is addressed with 32-bit offsets
   const Region* regs[] = {&h->ll, &h->sent, &h->ll128, &h->ll128_pipe, &h->sent_pipe};
   for (const Region* r : regs)
@@ -334,8 +361,15 @@ llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes) {
     if (e == hipSuccess) e = hipMemcpy(hx.data(), d, G * sizeof(uint32_t), hipMemcpyDeviceToHost);
     if (d) (void)hipFree(d);
     if (e == hipSuccess) {
+      // Workgroups are dealt to the 8 XCDs round-robin; the starting XCD may
+      // rotate from launch to launch, which the placements tolerate.  What
+      // they need: ids equal mod 8 share an XCD, and 8 consecutive ids cover
+      // 8 distinct XCDs.
       bool ok = true;
-      for (int i = 0; i < G; ++i) ok &= (hx[i] == (uint32_t)(i % 8));
+      uint32_t seen = 0;
+      for (int i = 0; i < 8; ++i) seen |= 1u << (hx[i] & 31u);
+      ok &= (seen == 0xFFu);
+      for (int i = 8; i < G; ++i) ok &= (hx[i] == hx[i % 8]);
       h->local_ok = ok;
     }
   }
@@ -370,7 +404,7 @@ int llar_launch_geometry(llar_comm* h, size_t n_elems, llar_protocol protocol, i
   Geometry g;
   int st = plan(h, n_elems, proto, g);
   if (st != LLAR_OK) return fail(st);
-  if (grid) *grid = h->n_ranks * g.slices;
+  if (grid) *grid = h->n_ranks * g.grid_slices;
   if (threads) *threads = g.threads;
   if (slices) *slices = g.slices;
   if (chunks) *chunks = g.chunks;
@@ -401,7 +435,7 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
   ls.n_ranks = h->n_ranks;
   ls.kernel = g.kernel;
   ls.threads = g.threads;
-  ls.grid = h->n_ranks * g.slices;
+  ls.grid = h->n_ranks * g.grid_slices;
 
   // every workgroup must be resident at once: consumers spin on producers
   int occ = occupancy(h->kind, h->n_ranks, g.kernel, g.threads);
@@ -409,7 +443,15 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
   if (ls.grid > occ * h->cu_count) return fail(LLAR_ERR_UNSUPPORTED);
 
   const uint64_t spin = (uint64_t)((double)h->spin_timeout_us * 1e-6 * h->wall_hz);
-  if (g.kernel == kKernOneShotLL || g.kernel == kKernOneShotSentinel) {
+  // epoch source: the host numbers stream-ordered calls; a captured call
+  // must read the device-resident epoch (its arguments repeat on replay)
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) != hipSuccess) return fail(LLAR_ERR_HIP);
+  const bool device_epoch = h->device_epoch || cap != hipStreamCaptureStatusNone;
+  const uint32_t host_epoch = device_epoch ? 0u : h->host_epoch;
+  const bool is_oneshot = g.kernel == kKernOneShotLL || g.kernel == kKernOneShotSentinel ||
+                          g.kernel == kKernOneShotLLLocal || g.kernel == kKernOneShotSentinelLocal;
+  if (is_oneshot) {
     OneShotArgs& a = ls.oneshot;
     for (int r = 0; r < h->n_ranks; ++r) a.part[r] = static_cast<const uint8_t*>(partials[r]);
     a.out = static_cast<uint8_t*>(out);
@@ -427,6 +469,9 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
     a.timing = h->timing ? 1u : 0u;
     a.keep = h->keep_staging ? 1u : 0u;
     a.drop_rank = h->debug_drop_rank < 0 ? 0xFFFFFFFFu : (uint32_t)h->debug_drop_rank;
+    a.trace = (h->trace_on && ls.grid <= kTraceMaxWgs) ? h->trace : nullptr;
+    if (a.trace) h->trace_grid = ls.grid;
+    a.host_epoch = host_epoch;
   } else {
     TwoShotArgs& a = ls.twoshot;
     for (int r = 0; r < h->n_ranks; ++r) a.part[r] = static_cast<const uint8_t*>(partials[r]);
@@ -439,26 +484,32 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
     a.n_chunks = (uint32_t)g.chunks;
     a.stage_bytes = (uint32_t)reg->bytes;
     a.parity_stride = (uint32_t)reg->parity_stride;
-    a.shard_cap = (proto == LLAR_SENTINEL_PIPELINED) ? sentinel_shard_cap(std::min(h->max_bytes, kCapChunk), h->n_ranks) : 0u;
+    a.n_buffers = (proto == LLAR_SENTINEL_PIPELINED) ? kSentinelPipeBuffers : 2u;
+    a.shard_cap = (proto == LLAR_SENTINEL_PIPELINED)
+                      ? (uint32_t)(reg->parity_stride / ((size_t)h->n_ranks * h->n_ranks * 16))
+                      : 0u;
     a.grid = (uint32_t)ls.grid;
     a.slices = (uint32_t)g.slices;
     a.placement = g.placement;
     a.timing = h->timing ? 1u : 0u;
     a.keep = h->keep_staging ? 1u : 0u;
     a.drop_rank = h->debug_drop_rank < 0 ? 0xFFFFFFFFu : (uint32_t)h->debug_drop_rank;
+    a.host_epoch = host_epoch;
     // the chunk must fit the staging that was allocated
     if (proto == LLAR_SENTINEL_PIPELINED) {
       uint32_t need = sentinel_shard_cap((size_t)g.chunk_elems * h->elem, h->n_ranks);
       if (need > a.shard_cap) return fail(LLAR_ERR_UNSUPPORTED);
     } else {
       size_t K = (g.kernel == kKernLL128Acc16) ? 63 : 31;
-      size_t lines = ceil_div(std::min<size_t>(g.chunk_elems, n_elems), K);
+      size_t lines = ceil_div((size_t)g.chunk_elems, K);  // the nominal chunk's lines
       if (lines * 128 > reg->parity_stride) return fail(LLAR_ERR_UNSUPPORTED);
     }
   }
   if (!reg->ptr) return fail(LLAR_ERR_UNSUPPORTED);
   hipError_t e = launch(ls, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(LLAR_ERR_HIP);
+  h->last_call_device = device_epoch;
+  if (!device_epoch) h->host_epoch = next_host_epoch(h->host_epoch);
   return LLAR_OK;
 }
 
@@ -495,6 +546,8 @@ static long long* option_slot(llar_comm* h, const char* key) {
       {"timing", &llar_comm::timing},
       {"keep_staging", &llar_comm::keep_staging},
       {"debug_drop_rank", &llar_comm::debug_drop_rank},
+      {"trace", &llar_comm::trace_on},
+      {"device_epoch", &llar_comm::device_epoch},
       {"auto_threshold_sentinel", &llar_comm::thr_sentinel},
       {"auto_threshold_ll128", &llar_comm::thr_ll128},
       {"auto_threshold_pipelined", &llar_comm::thr_pipelined},
@@ -516,8 +569,21 @@ int llar_set_option(llar_comm* h, const char* key, long long value) {
     return fail(LLAR_ERR_ARG);
   if (strcmp(key, "placement") == 0 && (value < 0 || value > 2)) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "placement") == 0 && value == 2 && !h->local_ok) return fail(LLAR_ERR_UNSUPPORTED);
-  if ((strcmp(key, "timing") == 0 || strcmp(key, "keep_staging") == 0) && (value < 0 || value > 1))
+  if ((strcmp(key, "timing") == 0 || strcmp(key, "keep_staging") == 0 || strcmp(key, "trace") == 0 ||
+       strcmp(key, "device_epoch") == 0) &&
+      (value < 0 || value > 1))
     return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "timing") == 0 && value == 1 && h->timing == 0) {
+    // start from a clean timing ring (the epoch and status words are kept)
+    if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
+    std::vector<uint64_t> ring(2 * kTimingRing);
+    for (int i = 0; i < kTimingRing; ++i) {
+      ring[2 * i] = ~0ull;
+      ring[2 * i + 1] = 0ull;
+    }
+    if (hipMemcpy(&h->ctrl->timing[0][0], ring.data(), ring.size() * sizeof(uint64_t), hipMemcpyHostToDevice) != hipSuccess)
+      return fail(LLAR_ERR_HIP);
+  }
   if (strcmp(key, "debug_drop_rank") == 0 && (value < -1 || value >= h->n_ranks)) return fail(LLAR_ERR_ARG);
   *slot = value;
   return LLAR_OK;
@@ -525,6 +591,10 @@ int llar_set_option(llar_comm* h, const char* key, long long value) {
 
 int llar_get_option(llar_comm* h, const char* key, long long* value) {
   if (!h || !key || !value) return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "local_placement_ok") == 0) {
+    *value = h->local_ok ? 1 : 0;
+    return LLAR_OK;
+  }
   long long* slot = option_slot(h, key);
   if (!slot) return fail(LLAR_ERR_ARG);
   *value = *slot;
@@ -549,6 +619,10 @@ int llar_debug_copy_staging(llar_comm* h, llar_protocol protocol, void* host_dst
 int llar_get_epoch(llar_comm* h, uint32_t* epoch) {
   if (!h || !epoch) return fail(LLAR_ERR_ARG);
   if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
+  if (!h->last_call_device) {
+    *epoch = h->host_epoch;
+    return LLAR_OK;
+  }
   if (hipMemcpy(epoch, &h->ctrl->epoch, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess) return fail(LLAR_ERR_HIP);
   return LLAR_OK;
 }
@@ -559,17 +633,28 @@ int llar_get_timing(llar_comm* h, uint64_t* host_dst, int count) {
   Ctrl c;
   if (hipMemcpy(&c, h->ctrl, sizeof(Ctrl), hipMemcpyDeviceToHost) != hipSuccess) return fail(LLAR_ERR_HIP);
   int n = std::min(count, kTimingRing - 1);
-  // the current epoch's slot has not run yet; the last n epochs precede it
-  uint32_t e = c.epoch;
+  // the next call's slot has not run yet; the last n epochs precede it
+  const bool dev = h->last_call_device;
+  uint32_t e = dev ? c.epoch : h->host_epoch;
   int written = 0;
   for (int i = n; i >= 1; --i) {
-    uint32_t ep = e;
-    for (int k = 0; k < i; ++k) ep = (ep == 1u) ? 0xFFFFFFFFu : ep - 1u;
+    uint32_t ep = e & 0x7FFFFFFFu;
+    for (int k = 0; k < i; ++k) ep = (ep == 1u) ? 0x7FFFFFFFu : ep - 1u;
+    if (dev) ep |= 0x80000000u;
     host_dst[2 * written] = c.timing[ep % kTimingRing][0];
     host_dst[2 * written + 1] = c.timing[ep % kTimingRing][1];
     ++written;
   }
   return written;
+}
+
+int llar_get_trace(llar_comm* h, uint64_t* host_dst, int max_records) {
+  if (!h || !host_dst || max_records < 0) return fail(LLAR_ERR_ARG);
+  if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
+  int n = std::min(max_records, h->trace_grid);
+  if (n > 0 && hipMemcpy(host_dst, h->trace, (size_t)n * kTraceWords * sizeof(uint64_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(LLAR_ERR_HIP);
+  return n;
 }
 
 double llar_wallclock_hz(void) {

@@ -29,7 +29,9 @@ enum KernelId : int {
   kKernLL128Acc16 = 3,
   kKernSentinelPipe = 4,
   kKernSentinelPipeLocal = 5,
-  kKernCount = 6
+  kKernOneShotLLLocal = 6,
+  kKernOneShotSentinelLocal = 7,
+  kKernCount = 8
 };
 
 struct OneShotArgs {
@@ -49,6 +51,8 @@ struct OneShotArgs {
   uint32_t timing;
   uint32_t keep;
   uint32_t drop_rank;    // tests: this rank's producers write nothing (0xFFFFFFFF = none)
+  uint32_t host_epoch;   // this call's epoch, or 0: read the device-resident epoch
+  uint64_t* trace;       // per-workgroup phase stamps (kTraceWords each), or null
 };
 
 struct TwoShotArgs {
@@ -63,13 +67,18 @@ struct TwoShotArgs {
   uint32_t stage_bytes;
   uint32_t parity_stride;
   uint32_t shard_cap;    // Sentinel: 16-byte vectors per (owner, sender) slot
+  uint32_t n_buffers;    // Sentinel pipeline: staging buffers (2 or 4)
   uint32_t grid;
   uint32_t slices;
   uint32_t placement;
   uint32_t timing;
   uint32_t keep;
   uint32_t drop_rank;
+  uint32_t host_epoch;
 };
+
+// phase trace of the one-shot kernel: per workgroup, thread 0 records
+constexpr int kTraceWords = 8;  // start, epoch, input, ready, out-acked, end, id, spare
 
 struct LaunchSpec {
   int kind;

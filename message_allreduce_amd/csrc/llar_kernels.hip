@@ -24,51 +24,67 @@
 namespace llar {
 
 // ---------------------------------------------------------------------------
-// shared prologue / epilogue: device-resident epoch and the arrival counter
+// shared prologue / epilogue: the call's epoch
 // ---------------------------------------------------------------------------
-// Thread 0 reads the epoch, publishes it to the workgroup through LDS and
-// takes an arrival ticket.  The workgroup that arrives last (ticket == G-1)
-// advances the epoch when it finishes: by then every workgroup of this call
-// has read the old value, and the next call starts only after this kernel.
+// Two epoch sources.  In ordinary stream-ordered use the host numbers the
+// calls and passes the epoch in the kernel arguments (host_epoch, bit 31
+// clear): nothing to read on the device.  Under graph capture the arguments
+// would repeat on every replay, so the kernel reads the device-resident epoch
+// (bit 31 set; the two ranges never meet): thread 0 reads it, publishes it
+// through LDS and takes an arrival ticket; the workgroup that arrives last
+// (ticket == G-1) advances it when it finishes -- by then every workgroup of
+// the call has read the old value, and the next call starts after this one.
+// Timing mode also counts arrivals so that the last workgroup can clear the
+// next call's timing slot.
 struct WgState {
   uint32_t epoch;
   uint32_t ticket;
+  bool counted;
 };
 
-__device__ __forceinline__ WgState wg_begin(Ctrl* ctrl, bool timing) {
+__device__ __forceinline__ WgState wg_begin(Ctrl* ctrl, uint32_t host_epoch, bool timing, bool idle) {
   __shared__ uint32_t s_epoch;
-  WgState st{0u, 0u};
+  WgState st{host_epoch, 0u, false};
+  const bool device_epoch = (host_epoch == 0u);
+  if (!device_epoch && !timing) return st;
   if (threadIdx.x == 0) {
     uint64_t t0 = wall_ticks();
-    uint32_t e = __hip_atomic_load(&ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_epoch = e;
+    uint32_t e = host_epoch;
+    if (device_epoch) {
+      e = __hip_atomic_load(&ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_epoch = e;
+    }
     st.ticket = __hip_atomic_fetch_add(&ctrl->arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (timing)
+    st.counted = true;
+    if (timing && !idle)
       __hip_atomic_fetch_min(&ctrl->timing[e % kTimingRing][0], t0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  st.epoch = s_epoch;
+  if (device_epoch) {
+    __syncthreads();
+    st.epoch = s_epoch;
+  }
   return st;
 }
 
-__device__ __forceinline__ void wg_end(Ctrl* ctrl, const WgState& st, uint32_t grid, bool timing) {
+__device__ __forceinline__ void wg_end(Ctrl* ctrl, const WgState& st, uint32_t host_epoch, uint32_t grid, bool timing,
+                                       bool idle) {
   if (timing) {
     drain_vm();
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    if (timing) {
+  if (threadIdx.x == 0 && st.counted) {
+    if (timing && !idle) {
       uint64_t t1 = wall_ticks();
       __hip_atomic_fetch_max(&ctrl->timing[st.epoch % kTimingRing][1], t1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (st.ticket == grid - 1u) {
-      uint32_t ne = next_epoch(st.epoch);
+      uint32_t ne = (host_epoch == 0u) ? next_device_epoch(st.epoch) : next_host_epoch(st.epoch);
       if (timing) {
         __hip_atomic_store(&ctrl->timing[ne % kTimingRing][0], ~0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&ctrl->timing[ne % kTimingRing][1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __hip_atomic_store(&ctrl->arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&ctrl->epoch, ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (host_epoch == 0u) __hip_atomic_store(&ctrl->epoch, ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -87,9 +103,13 @@ __device__ __forceinline__ void decode_role(uint32_t b, int n_ranks, uint32_t pl
 // ---------------------------------------------------------------------------
 // tail-safe 16-byte vector access to the caller's buffers
 // ---------------------------------------------------------------------------
+template <bool kStream = true>
 __device__ __forceinline__ u32x4 load_vec(const uint8_t* p, uint64_t v, uint64_t nbytes) {
   uint64_t off = v * 16u;
-  if (off + 16u <= nbytes) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + off));
+  if (off + 16u <= nbytes) {
+    if constexpr (kStream) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + off));
+    else return *reinterpret_cast<const u32x4*>(p + off);
+  }
   u32x4 x = {0u, 0u, 0u, 0u};
   for (uint64_t i = off; i < nbytes; i += 2u) {  // element sizes are 2 or 4 bytes
     uint32_t h = *reinterpret_cast<const uint16_t*>(p + i);
@@ -97,6 +117,29 @@ __device__ __forceinline__ u32x4 load_vec(const uint8_t* p, uint64_t v, uint64_t
     x[k >> 2] |= h << ((k & 2u) * 8u);
   }
   return x;
+}
+// 8-byte units (the one-shot consumer's granularity)
+__device__ __forceinline__ u32x2 load_unit(const uint8_t* p, uint64_t u, uint64_t nbytes) {
+  uint64_t off = u * 8u;
+  if (off + 8u <= nbytes) return *reinterpret_cast<const u32x2*>(p + off);
+  u32x2 x = {0u, 0u};
+  for (uint64_t i = off; i < nbytes; i += 2u) {
+    uint32_t h = *reinterpret_cast<const uint16_t*>(p + i);
+    uint32_t k = (uint32_t)(i - off);
+    x[k >> 2] |= h << ((k & 2u) * 8u);
+  }
+  return x;
+}
+__device__ __forceinline__ void store_unit(uint8_t* p, uint64_t u, uint64_t nbytes, u32x2 x) {
+  uint64_t off = u * 8u;
+  if (off + 8u <= nbytes) {
+    *reinterpret_cast<u32x2*>(p + off) = x;
+    return;
+  }
+  for (uint64_t i = off; i < nbytes; i += 2u) {
+    uint32_t k = (uint32_t)(i - off);
+    *reinterpret_cast<uint16_t*>(p + i) = (uint16_t)(x[k >> 2] >> ((k & 2u) * 8u));
+  }
 }
 __device__ __forceinline__ void store_vec(uint8_t* p, uint64_t v, uint64_t nbytes, u32x4 x) {
   uint64_t off = v * 16u;
@@ -113,6 +156,8 @@ __device__ __forceinline__ void store_vec(uint8_t* p, uint64_t v, uint64_t nbyte
 // Reduce one 16-byte vector: own contribution at rank position `own_rank`,
 // the others in `d[0..N-2]` ordered by rank; binary64 sum in rank order
 // starting from rank 0's value, one rounding to the output type.
+// (Array indices stay compile-time -- a runtime index would push the array
+// to scratch memory -- and the rank position is chosen with selects.)
 template <int kKind, int N>
 __device__ __forceinline__ u32x4 reduce_vec(const u32x4& own, int own_rank, const u32x4 (&d)[N > 1 ? N - 1 : 1]) {
   u32x4 out = {0u, 0u, 0u, 0u};
@@ -121,13 +166,34 @@ __device__ __forceinline__ u32x4 reduce_vec(const u32x4& own, int own_rank, cons
     double s = 0.0;
 #pragma unroll
     for (int r = 0; r < N; ++r) {
-      uint32_t bits;
-      if (r == own_rank) bits = vec_elem<kKind>(own, j);
-      else bits = vec_elem<kKind>(d[r < own_rank ? r : r - 1], j);
+      const uint32_t below = (r < N - 1) ? vec_elem<kKind>(d[r < N - 1 ? r : 0], j) : 0u;  // rank r sits at d[r]
+      const uint32_t above = (r >= 1) ? vec_elem<kKind>(d[r >= 1 ? r - 1 : 0], j) : 0u;   // rank r sits at d[r-1]
+      const uint32_t bits = (r < own_rank) ? below : (r == own_rank) ? vec_elem<kKind>(own, j) : above;
       double x = Elem<kKind>::dec(bits);
       s = (r == 0) ? x : s + x;
     }
     vec_set<kKind>(out, j, Elem<kKind>::enc(s));
+  }
+  return out;
+}
+
+// The same for an 8-byte unit (rank 0's own value first).
+template <int kKind, int N>
+__device__ __forceinline__ u32x2 reduce_unit(const u32x2& own, const u32x2 (&d)[N > 1 ? N - 1 : 1]) {
+  constexpr int kPerUnit = 8 / Elem<kKind>::kBytes;
+  u32x2 out = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < kPerUnit; ++j) {
+    auto elem = [&](const u32x2& v) -> uint32_t {
+      if constexpr (Elem<kKind>::kBytes == 4) return v[j];
+      else return (v[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+    };
+    double s = Elem<kKind>::dec(elem(own));
+#pragma unroll
+    for (int r = 1; r < N; ++r) s += Elem<kKind>::dec(elem(d[r - 1]));
+    uint32_t bits = Elem<kKind>::enc(s);
+    if constexpr (Elem<kKind>::kBytes == 4) out[j] = bits;
+    else out[j >> 1] |= (bits & 0xFFFFu) << ((j & 1) * 16);
   }
   return out;
 }
@@ -138,59 +204,82 @@ __device__ __forceinline__ u32x4 reduce_vec(const u32x4& own, int own_rank, cons
 // LL staging: [parity][rank-1][vector][2 lines of 16 B]; a line is
 // {data0, epoch, data1, epoch} so each 8-byte half carries its own flag.
 // Sentinel staging: [parity][rank-1][vector] 16 B, all-ones when empty.
-template <int kWire, int kKind, int N>
+// Phase trace (debug): thread 0 stamps the wall clock at each step; the
+// stamps after stores first wait for the stores to be acknowledged.
+__device__ __forceinline__ void trace_at(uint64_t* tr, int slot, bool drain) {
+  if (tr && threadIdx.x == 0) {
+    if (drain) drain_vm();
+    tr[blockIdx.x * kTraceWords + slot] = wall_ticks();
+  }
+}
+
+template <int kWire, int kKind, int N, bool kLocal>
 __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
-  WgState st = wg_begin(a.ctrl, a.timing);
+  const uint64_t t_entry = wall_ticks();
   int r;
   uint32_t w;
   decode_role(blockIdx.x, N, a.placement, r, w);
+  const bool idle = (w >= a.slices);
+  // slice w: 16-byte vectors [v0, v1) for producers, 8-byte units [2 v0, 2 v1)
+  // for the consumer (one LL line, or half a Sentinel slot, per lane)
+  const uint64_t v0 = idle ? 0 : (uint64_t)w * a.n_vec / a.slices;
+  const uint64_t v1 = idle ? 0 : (uint64_t)(w + 1) * a.n_vec / a.slices;
+  const bool producer = (r != 0) && !idle && (uint32_t)r != a.drop_rank;
+  const bool consumer = (r == 0) && !idle;
+  // the first input of this thread is requested before anything else
+  u32x4 first_vec = {0u, 0u, 0u, 0u};
+  u32x2 first_unit = {0u, 0u};
+  if (producer && v0 + threadIdx.x < v1) first_vec = load_vec<false>(a.part[r], v0 + threadIdx.x, a.nbytes);
+  if (consumer && 2 * v0 + threadIdx.x < 2 * v1) first_unit = load_unit(a.part[0], 2 * v0 + threadIdx.x, a.nbytes);
+  WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
+  if (a.trace && threadIdx.x == 0) a.trace[blockIdx.x * kTraceWords + 0] = t_entry;
+  trace_at(a.trace, 1, false);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.stage, a.stage_bytes);
   const uint32_t e = st.epoch;
   const uint32_t par_off = (e & 1u) * a.parity_stride;
-  const uint64_t v0 = (uint64_t)w * a.n_vec / a.slices, v1 = (uint64_t)(w + 1) * a.n_vec / a.slices;
   constexpr uint32_t kVecStage = (kWire == kWireLL) ? 32u : 16u;
 
-  if (w >= a.slices || (uint32_t)r == a.drop_rank) {
-    // idle workgroup (placement padding), or a producer silenced by a test
-  } else if (r != 0) {
-    // ---- producer of rank r
+  if (producer) {
     const uint8_t* src = a.part[r];
     const uint32_t base = par_off + (uint32_t)(r - 1) * a.rank_stride;
     for (uint64_t v = v0 + threadIdx.x; v < v1; v += blockDim.x) {
-      u32x4 x = load_vec(src, v, a.nbytes);
+      u32x4 x = (v == v0 + threadIdx.x) ? first_vec : load_vec<false>(src, v, a.nbytes);
+      if (v == v0) trace_at(a.trace, 2, true);
       uint32_t off = base + (uint32_t)v * kVecStage;
       if constexpr (kWire == kWireLL) {
-        st16_coh(rs, off, u32x4{x[0], e, x[1], e});
-        st16_coh(rs, off + 16u, u32x4{x[2], e, x[3], e});
+        st16_stage<kLocal>(rs, off, u32x4{x[0], e, x[1], e});
+        st16_stage<kLocal>(rs, off + 16u, u32x4{x[2], e, x[3], e});
       } else {
-        st16_coh(rs, off, sentinel_canon<kKind>(x));
+        st16_stage<kLocal>(rs, off, sentinel_canon<kKind>(x));
       }
+      if (v == v0) trace_at(a.trace, 3, true);
     }
-  } else {
-    // ---- consumer (rank 0)
+  } else if (consumer) {
     const uint8_t* own_src = a.part[0];
+    constexpr uint32_t kUnitStage = (kWire == kWireLL) ? 16u : 8u;
     bool dead = false;  // set after a timeout: stop waiting for anything else
-    for (uint64_t v = v0 + threadIdx.x; v < v1 && !dead; v += blockDim.x) {
-      u32x4 own = load_vec(own_src, v, a.nbytes);
+    for (uint64_t u = 2 * v0 + threadIdx.x; u < 2 * v1 && !dead; u += blockDim.x) {
+      u32x2 own = (u == 2 * v0 + threadIdx.x) ? first_unit : load_unit(own_src, u, a.nbytes);
+      if (u == 2 * v0) trace_at(a.trace, 2, true);
       // A slot that is ready stays ready for the rest of the call (LL lines
       // carry this call's epoch; a filled Sentinel slot is only reset by this
       // thread), so reload every slot until one pass sees all of them ready
       // and reduce from that pass.
-      u32x4 d[N > 1 ? N - 1 : 1];
+      u32x2 d[N > 1 ? N - 1 : 1];
       Spin spin(a.spin_limit);
       bool ok = true;
       while (true) {
         bool all = true;
 #pragma unroll
         for (int k = 0; k < N - 1; ++k) {
-          uint32_t off = par_off + (uint32_t)k * a.rank_stride + (uint32_t)v * kVecStage;
+          uint32_t off = par_off + (uint32_t)k * a.rank_stride + (uint32_t)u * kUnitStage;
           if constexpr (kWire == kWireLL) {
-            u32x4 l0 = ld16_coh(rs, off), l1 = ld16_coh(rs, off + 16u);
-            all &= (l0[1] == e) & (l0[3] == e) & (l1[1] == e) & (l1[3] == e);
-            d[k] = u32x4{l0[0], l0[2], l1[0], l1[2]};
+            u32x4 line = ld16_coh(rs, off);
+            all &= (line[1] == e) & (line[3] == e);
+            d[k] = u32x2{line[0], line[2]};
           } else {
-            d[k] = ld16_coh(rs, off);
-            all &= sentinel_ready<kKind>(d[k]);
+            d[k] = ld8_coh(rs, off);
+            all &= sentinel_ready8<kKind>(d[k]);
           }
         }
         if (all) break;
@@ -204,18 +293,24 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
         dead = true;
         continue;
       }
-      store_vec(a.out, v, a.nbytes, reduce_vec<kKind, N>(own, 0, d));
+      if (u == 2 * v0) trace_at(a.trace, 3, false);
+      store_unit(a.out, u, a.nbytes, reduce_unit<kKind, N>(own, d));
+      if (u == 2 * v0) trace_at(a.trace, 4, true);
       if constexpr (kWire == kWireSentinel) {
         if (!a.keep) {
 #pragma unroll
           for (int k = 0; k < N - 1; ++k)
-            st16_coh(rs, par_off + (uint32_t)k * a.rank_stride + (uint32_t)v * 16u,
-                     u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu});
+            st8_stage<kLocal>(rs, par_off + (uint32_t)k * a.rank_stride + (uint32_t)u * 8u,
+                              u32x2{0xFFFFFFFFu, 0xFFFFFFFFu});
         }
       }
     }
   }
-  wg_end(a.ctrl, st, a.grid, a.timing);
+  wg_end(a.ctrl, st, a.host_epoch, a.grid, a.timing, idle);
+  if (a.trace && threadIdx.x == 0) {
+    a.trace[blockIdx.x * kTraceWords + 5] = wall_ticks();
+    a.trace[blockIdx.x * kTraceWords + 6] = (uint64_t)xcc_id() | ((uint64_t)r << 8) | ((uint64_t)w << 16);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -239,10 +334,11 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
 // free again for chunk c+2.
 template <int kKind, int kAcc16, int N>
 __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
-  WgState st = wg_begin(a.ctrl, a.timing);
   int r;
   uint32_t w;
   decode_role(blockIdx.x, N, a.placement, r, w);
+  const bool idle = (w >= a.slices);
+  WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
   using E = Elem<kKind>;
   constexpr int kSlots = kAcc16 ? 64 : 32;
   constexpr int K = kSlots - 1;
@@ -253,12 +349,16 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
   uint32_t flag_full;
   if constexpr (!kAcc16) flag_full = __float_as_uint((float)N);
   else flag_full = E::from_f32((float)N);
-  bool dead = (w >= a.slices);  // idle padding workgroup, or a poll timed out
+  bool dead = idle;  // idle padding workgroup, or a poll timed out
 
   for (uint32_t c = 0; c < a.n_chunks && !__any((int)dead); ++c) {
     const uint64_t cbase = (uint64_t)c * a.chunk_elems;
     const uint32_t len = (uint32_t)min((uint64_t)a.chunk_elems, a.n - cbase);
-    const uint32_t L = (len + K - 1) / K;
+    // Lines are partitioned by the nominal chunk (not this chunk's length):
+    // a line must belong to the same (owner, slice) in every chunk, or the
+    // implicit credit of one slice would release a line another slice has
+    // not consumed yet.  Elements past the message end are masked.
+    const uint32_t L = (a.chunk_elems + K - 1) / K;
     const uint32_t poff = (c & 1u) * a.parity_stride;
 
     // ---- produce: data atomics for every owner's slice w
@@ -379,99 +479,197 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
       }
     }
   }
-  wg_end(a.ctrl, st, a.grid, a.timing);
+  wg_end(a.ctrl, st, a.host_epoch, a.grid, a.timing, idle);
 }
 
 // ---------------------------------------------------------------------------
-// two-shot Sentinel, chunked and double-buffered
+// two-shot Sentinel, chunked and double-buffered, producer/consumer waves
 // ---------------------------------------------------------------------------
 // Staging: [parity][owner s][sender rank r][vector of s's shard] 16 B,
 // all-ones when empty.  Chunk c's vectors are split into N owner shards and
-// each shard into W slices.  Workgroup (r, w), per chunk c:
-//   produce: for every owner s != r, copy rank r's vectors of slice (s, w)
-//            (sentinel-canonicalised) into [c&1][s][r];
-//   consume: for each vector of slice (r, w): read its own partial, poll the
-//            N-1 slots [c&1][r][*] until no element is the sentinel, add in
-//            binary64 in rank order, round, write `out`, reset the slots;
-//            then drain, so the resets land before this workgroup's next
-//            chunk can be seen by anyone (the credit of the two-shot LL128
-//            kernel, with the reset in place of the zeroing).
+// each shard into W slices.  Workgroup (r, w) is split in two halves:
+//   producer waves: for every chunk c, load rank r's vectors of slice (s, w)
+//            for every owner s != r, then -- once this workgroup's consumer
+//            waves have finished chunk c-1 -- store them, sentinel-
+//            canonicalised, into [c&1][s][r];
+//   consumer waves: for each vector of slice (r, w) of chunk c, read the
+//            own partial, poll the N-1 slots [c&1][r][*] until no element is
+//            the sentinel, add in binary64 in rank order, round, write `out`,
+//            reset the slots; drain (the resets are performed), then publish
+//            "chunk c done" to the producer waves through LDS.
+// The credit: the consumer finished chunk c-1 only after every peer's
+// producer stored chunk c-1, which each did only after its own consumer had
+// finished chunk c-2 -- the previous user of chunk c's parity -- and had
+// drained those resets.  Loads of chunk c+1 are issued before that wait, so
+// HBM reads keep streaming while the consumers work.
 template <int kKind, int N, bool kLocal>
 __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
-  WgState st = wg_begin(a.ctrl, a.timing);
+  constexpr int kU = 2;   // vectors per producer lane per owner per batch
+  constexpr int kUc = 2;  // vectors per consumer lane per batch
   int r;
   uint32_t w;
   decode_role(blockIdx.x, N, a.placement, r, w);
+  const bool idle = (w >= a.slices);
+  WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
   using E = Elem<kKind>;
+  __shared__ uint32_t s_done[8];  // per consumer wave: chunks finished
+  if (threadIdx.x < 8) s_done[threadIdx.x] = 0u;
+  __syncthreads();
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.stage, a.stage_bytes);
   const uint8_t* src = a.part[r];
   const uint64_t nbytes = a.n * (uint64_t)E::kBytes;
   const uint32_t chunk_vecs = (uint32_t)(((uint64_t)a.chunk_elems * E::kBytes + 15u) / 16u);
+  const uint64_t total_vecs = (nbytes + 15u) / 16u;
   const uint32_t slot_bytes = a.shard_cap * 16u;
-  bool dead = (w >= a.slices);  // idle padding workgroup, or a poll timed out
+  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
+  const uint32_t n_prod = n_waves / 2, n_cons = n_waves - n_prod;
+  // n_buf staging buffers; a producer may run credit_lag chunks further ahead
+  // of its consumer, which is safe when n_buf >= 2 * credit_lag + 2
+  const uint32_t n_buf = a.n_buffers;
+  const uint32_t lag = n_buf / 2u - 1u;
+  bool dead = idle;
 
-  for (uint32_t c = 0; c < a.n_chunks && !__any((int)dead); ++c) {
-    const uint64_t vbase = (uint64_t)c * chunk_vecs;  // first message vector of the chunk
-    const uint64_t cbytes = min((uint64_t)a.chunk_elems * E::kBytes, nbytes - (uint64_t)c * a.chunk_elems * E::kBytes);
-    const uint32_t nv = (uint32_t)((cbytes + 15u) / 16u);
-    const uint32_t poff = (c & 1u) * a.parity_stride;
-
-    // ---- produce
-    for (int s = 0; s < N; ++s) {
-      if (s == r || (uint32_t)r == a.drop_rank) continue;
-      uint32_t o0 = (uint32_t)((uint64_t)s * nv / N), o1 = (uint32_t)((uint64_t)(s + 1) * nv / N);
-      uint32_t s0 = o0 + (uint32_t)((uint64_t)w * (o1 - o0) / a.slices);
-      uint32_t s1 = o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices);
-      uint32_t slot = poff + (uint32_t)(s * N + r) * slot_bytes;
-      for (uint32_t v = s0 + threadIdx.x; v < s1; v += blockDim.x) {
-        u32x4 x = load_vec(src, vbase + v, nbytes);
-        st16_stage<kLocal>(rs, slot + (v - o0) * 16u, sentinel_canon<kKind>(x));
+  if (wave < n_prod) {
+    // ---------------- producer waves
+    const uint32_t pl = wave * 64u + lane, PL = n_prod * 64u;
+    const bool silent = ((uint32_t)r == a.drop_rank);
+    for (uint32_t c = 0; c < a.n_chunks && !dead; ++c) {
+      const uint64_t vbase = (uint64_t)c * chunk_vecs;
+      // vectors of this chunk that exist; the partition below uses the
+      // nominal chunk so that a slot keeps its (owner, slice) in every chunk
+      const uint32_t nv_real = (uint32_t)min((uint64_t)chunk_vecs, total_vecs - vbase);
+      const uint32_t nv = chunk_vecs;
+      const uint32_t poff = (c % n_buf) * a.parity_stride;
+      const uint32_t span = (nv / N + 1u) / a.slices + 2u;  // longest (owner, slice) range
+      for (uint32_t b0 = 0; b0 < span && !dead; b0 += kU * PL) {
+        u32x4 x[N > 1 ? N - 1 : 1][kU];
+        uint32_t vo[N > 1 ? N - 1 : 1][kU];  // vector offset inside the owner's shard, or ~0
+#pragma unroll
+        for (int k = 0; k < N - 1; ++k) {
+          const int s = k < r ? k : k + 1;
+          const uint32_t o0 = (uint32_t)((uint64_t)s * nv / N), o1 = (uint32_t)((uint64_t)(s + 1) * nv / N);
+          const uint32_t s0 = o0 + (uint32_t)((uint64_t)w * (o1 - o0) / a.slices);
+          const uint32_t s1 = o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices);
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const uint32_t v = s0 + b0 + pl + (uint32_t)u * PL;
+            const bool ok = (v < s1) && (v < nv_real);
+            vo[k][u] = ok ? v - o0 : ~0u;
+            x[k][u] = ok ? load_vec(src, vbase + v, nbytes) : u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+        if (b0 == 0 && c > lag) {
+          // credit: this workgroup's consumers have finished chunks 0..c-1-lag
+          Spin spin(a.spin_limit);
+          while (true) {
+            uint32_t done = ~0u;
+            for (uint32_t i = 0; i < n_cons; ++i)
+              done = min(done, __hip_atomic_load(&s_done[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+            if (done + lag >= c) break;
+            if (spin.expired()) {
+              raise_status(a.ctrl, kStatusTimeout);
+              dead = true;
+              break;
+            }
+          }
+          if (dead) break;
+        }
+        if (silent) continue;
+#pragma unroll
+        for (int k = 0; k < N - 1; ++k) {
+          const int s = k < r ? k : k + 1;
+          const uint32_t slot = poff + (uint32_t)(s * N + r) * slot_bytes;
+#pragma unroll
+          for (int u = 0; u < kU; ++u)
+            if (vo[k][u] != ~0u) st16_stage<kLocal>(rs, slot + vo[k][u] * 16u, sentinel_canon<kKind>(x[k][u]));
+        }
       }
     }
-    // ---- consume
-    {
-      uint32_t o0 = (uint32_t)((uint64_t)r * nv / N), o1 = (uint32_t)((uint64_t)(r + 1) * nv / N);
-      uint32_t s0 = o0 + (uint32_t)((uint64_t)w * (o1 - o0) / a.slices);
-      uint32_t s1 = o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices);
-      const uint32_t my = poff + (uint32_t)(r * N) * slot_bytes;
-      for (uint32_t v = s0 + threadIdx.x; v < s1; v += blockDim.x) {
-        u32x4 own = load_vec(src, vbase + v, nbytes);
-        u32x4 d[N > 1 ? N - 1 : 1];
-        Spin spin(a.spin_limit);
-        bool ok = true;
+  } else {
+    // ---------------- consumer waves
+    const uint32_t cw = wave - n_prod;
+    const uint32_t cl = cw * 64u + lane, CL = n_cons * 64u;
+    const uint32_t nv = chunk_vecs;
+    const uint32_t o0 = (uint32_t)((uint64_t)r * nv / N), o1 = (uint32_t)((uint64_t)(r + 1) * nv / N);
+    const uint32_t s0 = o0 + (uint32_t)((uint64_t)w * (o1 - o0) / a.slices);
+    const uint32_t s1n = o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices);
+    // own vectors of the first batch of the next chunk, requested early
+    u32x4 own_next[kUc];
+#pragma unroll
+    for (int u = 0; u < kUc; ++u) {
+      const uint32_t v = s0 + cl + (uint32_t)u * CL;
+      own_next[u] = (!dead && v < s1n && v < total_vecs) ? load_vec(src, v, nbytes) : u32x4{0u, 0u, 0u, 0u};
+    }
+    for (uint32_t c = 0; c < a.n_chunks && !__any((int)dead); ++c) {
+      const uint64_t vbase = (uint64_t)c * chunk_vecs;
+      const uint32_t nv_real = (uint32_t)min((uint64_t)chunk_vecs, total_vecs - vbase);
+      const uint32_t s1 = min(s1n, max(nv_real, s0));
+      const uint32_t my = (c % n_buf) * a.parity_stride + (uint32_t)(r * N) * slot_bytes;
+      for (uint32_t b0 = 0; b0 < s1 - s0 && !dead; b0 += kUc * CL) {
+        u32x4 own[kUc];
+        bool valid[kUc];
+#pragma unroll
+        for (int u = 0; u < kUc; ++u) {
+          const uint32_t v = s0 + b0 + cl + (uint32_t)u * CL;
+          valid[u] = v < s1;
+          if (b0 == 0) own[u] = own_next[u];
+          else own[u] = valid[u] ? load_vec(src, vbase + v, nbytes) : u32x4{0u, 0u, 0u, 0u};
+        }
+        u32x4 d[kUc][N > 1 ? N - 1 : 1];
+        SpinBulk spin(a.spin_limit);
         while (true) {
           bool all = true;
 #pragma unroll
-          for (int k = 0; k < N - 1; ++k) {
-            int sender = k < r ? k : k + 1;
-            d[k] = ld16_coh(rs, my + (uint32_t)sender * slot_bytes + (v - o0) * 16u);
-            all &= sentinel_ready<kKind>(d[k]);
+          for (int u = 0; u < kUc; ++u) {
+            const uint32_t v = s0 + b0 + cl + (uint32_t)u * CL;
+#pragma unroll
+            for (int k = 0; k < N - 1; ++k) {
+              const int sender = k < r ? k : k + 1;
+              d[u][k] = valid[u] ? ld16_coh(rs, my + (uint32_t)sender * slot_bytes + (v - o0) * 16u)
+                                 : u32x4{0u, 0u, 0u, 0u};
+              all &= sentinel_ready<kKind>(d[u][k]);
+            }
           }
           if (all) break;
           if (spin.expired()) {
             raise_status(a.ctrl, kStatusTimeout);
-            ok = false;
+            dead = true;
             break;
           }
         }
-        if (!ok) {
-          dead = true;
-          break;
-        }
-        store_vec(a.out, vbase + v, nbytes, reduce_vec<kKind, N>(own, r, d));
-        if (!a.keep) {
+        if (dead) break;
 #pragma unroll
-          for (int k = 0; k < N - 1; ++k) {
-            int sender = k < r ? k : k + 1;
-            st16_stage<kLocal>(rs, my + (uint32_t)sender * slot_bytes + (v - o0) * 16u,
-                               u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu});
+        for (int u = 0; u < kUc; ++u) {
+          if (!valid[u]) continue;
+          const uint32_t v = s0 + b0 + cl + (uint32_t)u * CL;
+          store_vec(a.out, vbase + v, nbytes, reduce_vec<kKind, N>(own[u], r, d[u]));
+          if (!a.keep) {
+#pragma unroll
+            for (int k = 0; k < N - 1; ++k) {
+              const int sender = k < r ? k : k + 1;
+              st16_stage<kLocal>(rs, my + (uint32_t)sender * slot_bytes + (v - o0) * 16u,
+                                 u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu});
+            }
           }
         }
       }
+      // the resets are performed before the producers may reuse the buffer
+      drain_vm();
+      if (lane == 0 && !__any((int)dead))
+        __hip_atomic_store(&s_done[cw], c + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      // request the next chunk's own vectors while the producers fill it
+      if (c + 1 < a.n_chunks) {
+        const uint64_t nb = (uint64_t)(c + 1) * chunk_vecs;
+        const uint32_t nv_next = (uint32_t)min((uint64_t)chunk_vecs, total_vecs - nb);
+#pragma unroll
+        for (int u = 0; u < kUc; ++u) {
+          const uint32_t v = s0 + cl + (uint32_t)u * CL;
+          own_next[u] = (v < s1n && v < nv_next) ? load_vec(src, nb + v, nbytes) : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
     }
-    drain_vm();
   }
-  wg_end(a.ctrl, st, a.grid, a.timing);
+  wg_end(a.ctrl, st, a.host_epoch, a.grid, a.timing, idle);
 }
 
 // ---------------------------------------------------------------------------
@@ -482,10 +680,16 @@ static hipError_t launch_n(const LaunchSpec& ls, hipStream_t stream) {
   dim3 grid(ls.grid), block(ls.threads);
   switch (ls.kernel) {
     case kKernOneShotLL:
-      hipLaunchKernelGGL((k_oneshot<kWireLL, kKind, N>), grid, block, 0, stream, ls.oneshot);
+      hipLaunchKernelGGL((k_oneshot<kWireLL, kKind, N, false>), grid, block, 0, stream, ls.oneshot);
       break;
     case kKernOneShotSentinel:
-      hipLaunchKernelGGL((k_oneshot<kWireSentinel, kKind, N>), grid, block, 0, stream, ls.oneshot);
+      hipLaunchKernelGGL((k_oneshot<kWireSentinel, kKind, N, false>), grid, block, 0, stream, ls.oneshot);
+      break;
+    case kKernOneShotLLLocal:
+      hipLaunchKernelGGL((k_oneshot<kWireLL, kKind, N, true>), grid, block, 0, stream, ls.oneshot);
+      break;
+    case kKernOneShotSentinelLocal:
+      hipLaunchKernelGGL((k_oneshot<kWireSentinel, kKind, N, true>), grid, block, 0, stream, ls.oneshot);
       break;
     case kKernLL128Acc32:
       hipLaunchKernelGGL((k_twoshot_ll128<kKind, 0, N>), grid, block, 0, stream, ls.twoshot);
@@ -539,8 +743,10 @@ static int occupancy_n(int kernel, int threads) {
   int blocks = 0;
   hipError_t err = hipErrorInvalidValue;
   switch (kernel) {
-    case kKernOneShotLL: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_oneshot<kWireLL, kKind, N>, threads, 0); break;
-    case kKernOneShotSentinel: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_oneshot<kWireSentinel, kKind, N>, threads, 0); break;
+    case kKernOneShotLL: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_oneshot<kWireLL, kKind, N, false>, threads, 0); break;
+    case kKernOneShotSentinel: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_oneshot<kWireSentinel, kKind, N, false>, threads, 0); break;
+    case kKernOneShotLLLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_oneshot<kWireLL, kKind, N, true>, threads, 0); break;
+    case kKernOneShotSentinelLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_oneshot<kWireSentinel, kKind, N, true>, threads, 0); break;
     case kKernLL128Acc32: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_ll128<kKind, 0, N>, threads, 0); break;
     case kKernLL128Acc16:
       if constexpr (kKind != kKindF32) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_ll128<kKind, 1, N>, threads, 0);

@@ -228,7 +228,8 @@ class PipelineResult:
 
 
 def check_pipeline(n_ranks: int, slices: int, chunks: int, parities: int = 2,
-                   run_ahead: bool = False, max_states: int = 2_000_000) -> PipelineResult:
+                   run_ahead: bool = False, split: bool = False, credit_lag: int = 0,
+                   max_states: int = 2_000_000) -> PipelineResult:
     """Explore every interleaving of the chunked two-shot schedule.
 
     Agents are workgroups (rank r, slice w).  Agent program, for c = 0..C-1:
@@ -239,12 +240,18 @@ def check_pipeline(n_ranks: int, slices: int, chunks: int, parities: int = 2,
     With ``run_ahead`` the agent produces chunk c+1 before consuming chunk c
     (a schedule without the credit), which must be caught.
 
+    With ``split`` each workgroup is two agents: a producer that may emit
+    chunk c only once its own consumer has finished chunk c-1 (the credit,
+    passed inside the workgroup), and a consumer that consumes in order.
+
     A line's state is (chunk it holds, contribution count).  Checked:
       no overwrite -- a contribution for chunk c only lands on a line that is
                       empty or already holds chunk c;
       no early read -- consume(c) only after N contributions of chunk c;
       progress     -- every state with unfinished agents has a move.
     """
+    if split:
+        return _check_split(n_ranks, slices, chunks, parities, max_states, credit_lag)
     agents = [(r, w) for r in range(n_ranks) for w in range(slices)]
 
     def program(c_count):
@@ -321,6 +328,68 @@ def check_pipeline(n_ranks: int, slices: int, chunks: int, parities: int = 2,
             res.deadlocks += 1
         if res.violations:
             break
+    return res
+
+
+def _check_split(n_ranks, slices, chunks, parities, max_states, credit_lag=0):
+    """Model of the wave-specialised schedule: per (rank r, slice w) a
+    producer P and a consumer C.  P emits chunk c (one contribution per
+    owner, separate steps) only when C has consumed chunks 0..c-1 (C's count
+    of finished chunks is >= c); C consumes chunk c when its line holds all N
+    contributions of chunk c.  (A weaker credit, count >= c-1, lets P
+    overwrite a peer's unconsumed chunk c-2: the checker finds it.)"""
+    pairs = [(r, w) for r in range(n_ranks) for w in range(slices)]
+    n_lines = parities * n_ranks * slices
+
+    def line_id(par, owner, w):
+        return (par * n_ranks + owner) * slices + w
+
+    # state: producer position (chunk, next owner), consumer chunks done, lines
+    init = (tuple([(0, 0)] * len(pairs)), tuple([0] * len(pairs)), tuple([(-1, 0)] * n_lines))
+    res = PipelineResult(states=0, terminal_ok=0)
+    seen, stack = set(), [init]
+    while stack:
+        st = stack.pop()
+        if st in seen:
+            continue
+        seen.add(st)
+        res.states += 1
+        if res.states > max_states:
+            raise RuntimeError("state space too large")
+        prod, cons, lines = st
+        if all(p[0] == chunks for p in prod) and all(c == chunks for c in cons):
+            res.terminal_ok += 1
+            continue
+        moved = False
+        for ai, (r, w) in enumerate(pairs):
+            c, s = prod[ai]
+            if c < chunks and cons[ai] >= c - credit_lag:
+                lid = line_id(c % parities, s, w)
+                held, cnt = lines[lid]
+                if held not in (-1, c):
+                    res.violations.append(("overwrite", (r, w), c, s, held))
+                    break
+                nl = list(lines)
+                nl[lid] = (c, cnt + 1)
+                npr = list(prod)
+                npr[ai] = (c, s + 1) if s + 1 < n_ranks else (c + 1, 0)
+                stack.append((tuple(npr), cons, tuple(nl)))
+                moved = True
+            cc = cons[ai]
+            if cc < chunks:
+                lid = line_id(cc % parities, r, w)
+                held, cnt = lines[lid]
+                if held == cc and cnt == n_ranks:
+                    nl = list(lines)
+                    nl[lid] = (-1, 0)
+                    nco = list(cons)
+                    nco[ai] = cc + 1
+                    stack.append((prod, tuple(nco), tuple(nl)))
+                    moved = True
+        if res.violations:
+            break
+        if not moved:
+            res.deadlocks += 1
     return res
 
 

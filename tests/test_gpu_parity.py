@@ -326,6 +326,12 @@ def test_workgroup_sizes(proto, threads):
     n = 30000
     bits = make_partials(1100, threads, 6, "fp32", n, "uniform", 1.0)
     with comm_for(6, dt, n * 4, threads=threads, chunk_bytes=8192) as c:
+        if proto == "sentinel_pipelined" and threads < 128:
+            # producer and consumer waves need at least two waves
+            with pytest.raises(llar.LlarError) as ei:
+                run(c, bits, proto, dt)
+            assert ei.value.status == -1
+            return
         got = run(c, bits, proto, dt)
         check(got, oracle.allreduce(bits, dt), dt, proto, "threads %d" % threads)
 
@@ -343,3 +349,87 @@ def test_ll128_keep_staging_matches_line_model():
         model = models.ll128_staging_image(bits, dt, F32)
         assert np.array_equal(stage.astype(np.float64), model)
         assert (stage[:, 0] == n_ranks).all()
+
+
+@pytest.mark.parametrize("placement", [1, 2])
+@pytest.mark.parametrize("proto", ["ll", "sentinel"])
+def test_one_shot_placements(proto, placement):
+    dt = F16
+    with comm_for(8, dt, 1 << 20, placement=placement) as c:
+        for i, n in enumerate([5, 64, 8192, 65536 + 3, 300000]):
+            bits = make_partials(1300 + placement, i, 8, "fp16", n, "normal", 1.0)
+            got = run(c, bits, proto, dt)
+            assert_exact(got, oracle.allreduce(bits, dt), dt, "%s placement %d n=%d" % (proto, placement, n))
+        if proto == "sentinel":
+            assert (c.staging(llar.SENTINEL) == 0xFF).all()
+
+
+@pytest.mark.parametrize("proto", ALL_PROTOCOLS)
+def test_device_epoch_option(proto):
+    dt = BF16
+    n = 7000
+    with comm_for(4, dt, n * 2, device_epoch=1, chunk_bytes=4096) as c:
+        for rep in range(4):
+            bits = make_partials(1400, rep, 4, "bf16", n, "normal", 1.0)
+            got = run(c, bits, proto, dt)
+            check(got, oracle.allreduce(bits, dt), dt, proto, "rep %d" % rep)
+        e = c.epoch()
+        assert e & 0x80000000
+
+
+def test_graph_capture_replays_use_fresh_epochs():
+    """Calls captured into a graph read the device-resident epoch, so every
+    replay is a new call: stale LL lines from the previous replay are
+    rejected.  Eager work (new inputs, synchronisation) sits between replays,
+    and every replay is checked against the oracle."""
+    dt = BF16
+    n, n_ranks = 4096, 8
+    c = comm_for(n_ranks, dt, n * 2, chunk_bytes=2048)
+    try:
+        parts = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(n_ranks)]
+        outs = {p: torch.empty(n, dtype=torch.bfloat16, device="cuda") for p in ALL_PROTOCOLS}
+        bits0 = make_partials(1500, 0, n_ranks, "bf16", n, "normal", 1.0)
+        for r in range(n_ranks):
+            parts[r].copy_(to_device(bits0[r], dt))
+        # warm up eagerly, then capture one call of every protocol
+        for p in ALL_PROTOCOLS:
+            c.allreduce(parts, outs[p], p)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for p in ALL_PROTOCOLS:
+                c.allreduce(parts, outs[p], p)
+        torch.cuda.synchronize()
+        for rep in range(1, 6):
+            bits = make_partials(1500, rep, n_ranks, "bf16", n, "normal", 1.0)
+            for r in range(n_ranks):
+                parts[r].copy_(to_device(bits[r], dt))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            st, sbits = c.device_status()
+            assert st == 0, (st, sbits)
+            want = oracle.allreduce(bits, dt)
+            for p in ALL_PROTOCOLS:
+                check(to_host(outs[p], dt), want, dt, p, "replay %d %s" % (rep, p))
+            # an eager call between replays (host-numbered epoch)
+            got = run(c, bits, "ll", dt)
+            assert_exact(got, want, dt, "eager after replay %d" % rep)
+    finally:
+        c.close()
+
+
+@pytest.mark.parametrize("proto", ["ll128_pipelined", "sentinel_pipelined"])
+def test_pipelined_short_last_chunk_regression(proto):
+    """A chunk that is shorter than the others reuses a parity: the lines /
+    slots must keep their (owner, slice) so the implicit credit still covers
+    them.  Sizes leave every kind of ragged last chunk; many repetitions."""
+    dt = BF16
+    chunk = 2048
+    for n_ranks in (4, 8):
+        with comm_for(n_ranks, dt, 64 * chunk, chunk_bytes=chunk) as c:
+            for i, n in enumerate([5000, 1024 * 5 + 1, 1024 * 3 + 700, 1024 * 9 + 31, 1024 * 2 + 1]):
+                for rep in range(8):
+                    bits = make_partials(1600 + i, rep, n_ranks, "bf16", n, "normal", 1.0)
+                    got = run(c, bits, proto, dt)
+                    check(got, oracle.allreduce(bits, dt), dt, proto, "N=%d n=%d rep %d" % (n_ranks, n, rep))

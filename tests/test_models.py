@@ -271,3 +271,30 @@ def test_pipeline_single_buffer_overwrites():
 def test_pipeline_without_credit_overwrites():
     r = models.check_pipeline(n_ranks=2, slices=1, chunks=4, run_ahead=True)
     assert any(v[0] == "overwrite" for v in r.violations)
+
+
+def test_pipeline_split_producer_consumer_is_safe_exhaustively():
+    for n_ranks, slices, chunks in [(2, 1, 4), (3, 1, 3), (2, 2, 3)]:
+        r = models.check_pipeline(n_ranks, slices, chunks, split=True)
+        assert not r.violations and r.deadlocks == 0 and r.terminal_ok == 1, (n_ranks, slices, chunks, r)
+
+
+def test_pipeline_split_with_one_buffer_overwrites():
+    r = models.check_pipeline(2, 1, 3, parities=1, split=True)
+    assert any(v[0] == "overwrite" for v in r.violations)
+
+
+def test_pipeline_split_with_a_weaker_credit_overwrites():
+    # emitting chunk c after the own consumer finished only chunk c-2
+    r = models.check_pipeline(3, 1, 3, split=True, credit_lag=1)
+    assert any(v[0] == "overwrite" for v in r.violations)
+
+
+def test_pipeline_credit_lag_needs_two_lag_plus_two_buffers():
+    # producing chunk c once the own consumer finished chunk c-1-lag is safe
+    # exactly when the buffer count is at least 2*lag + 2
+    for shape in [(2, 1, 6), (3, 1, 5), (2, 2, 5)]:
+        ok = models.check_pipeline(*shape, split=True, parities=4, credit_lag=1)
+        assert not ok.violations and ok.deadlocks == 0 and ok.terminal_ok == 1
+        bad = models.check_pipeline(*shape, split=True, parities=3, credit_lag=1)
+        assert any(v[0] == "overwrite" for v in bad.violations)
