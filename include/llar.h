@@ -122,16 +122,24 @@ int llar_clear_device_status(llar_comm* h);
  *   "threads"          threads per workgroup: 64, 128, 256 or 512 (0 = tuned default); the
  *                      pipelined Sentinel splits a workgroup into producer and consumer waves
  *                      and needs at least 128
+ *   "pipeline_buffers" staging buffers of the pipelined Sentinel: 2, 4 (default), 6 or 8; with B
+ *                      buffers a producer runs up to B/2 - 1 chunks ahead of its consumer
  *   "placement"        0 = auto, 1 = spread (rank r on XCD r mod 8), 2 = local (one slice's ranks share an XCD)
- *   "timing"           1 = record device-side start/end wall-clock per call (see llar_get_timing)
+ *   "timing"           1 = record device-side start/end wall-clock per call (see llar_get_timing);
+ *                      a call whose grid exceeds 4096 workgroups then fails with LLAR_ERR_UNSUPPORTED
  *   "keep_staging"     1 = LL128/Sentinel consumers do not reset staging (tests only; the next call is invalid)
  *   "debug_drop_rank"  tests: the producers of this rank write nothing, so consumers time out (-1 = none)
- *   "trace"            1 = one-shot kernels record per-workgroup phase stamps (see llar_get_trace)
+ *   "trace"            1 = one-shot kernels record per-workgroup phase stamps (see llar_get_trace),
+ *                      the pipelined Sentinel per-chunk stamps (see llar_get_pipeline_trace)
+ *   "pipeline_buffers" staging buffers of the pipelined Sentinel: 2, 4 (default), 6 or 8; with B
+ *                      buffers a producer runs up to B/2 - 1 chunks ahead of its consumer
  *   "device_epoch"     1 = always read the device-resident epoch; otherwise the host numbers
  *                      stream-ordered calls and the device epoch is used only on a stream that is
  *                      being captured into a graph (replays then never reuse an epoch)
  *   "auto_threshold_sentinel", "auto_threshold_ll128", "auto_threshold_pipelined"
- *                      AUTO size boundaries in bytes per rank
+ *                      AUTO size boundaries in bytes per rank: LL up to 64 KiB, one-shot Sentinel
+ *                      up to 512 KiB, pipelined Sentinel above; LL128 only above its own threshold
+ *                      (default: never, its atomics are slower than the Sentinel exchange here)
  * llar_get_option also answers "local_placement_ok" (read-only): 1 when
  * workgroup ids equal mod 8 were seen to share an XCD, which the local
  * placement requires.
@@ -157,7 +165,9 @@ int llar_get_epoch(llar_comm* h, uint32_t* epoch);
  * for each call, the wall-clock ticks (see llar_wallclock_hz) of the first
  * workgroup start and of the last workgroup end (after its final stores were
  * acknowledged).  Writes 2*count uint64 to host_dst, oldest first; returns the
- * number of records written (>= 0) or an error. */
+ * number of records written (>= 0) or an error.  Each workgroup stores its
+ * own span; this call reduces them (a call that recorded nothing reads as
+ * start 2^64-1, end 0). */
 int llar_get_timing(llar_comm* h, uint64_t* host_dst, int count);
 double llar_wallclock_hz(void);
 
@@ -167,6 +177,14 @@ double llar_wallclock_hz(void);
  * acknowledged (consumer), exit; then xcc | rank << 8 | slice << 16; spare.
  * Returns the number of workgroup records written (<= max_records). */
 int llar_get_trace(llar_comm* h, uint64_t* host_dst, int max_records);
+
+/* Per-chunk stamps of the last pipelined-Sentinel call made with option
+ * "trace": for each workgroup 512 uint64 -- wall ticks at which producer wave
+ * 0 was granted the credit for chunk c ([c]), issued chunk c's last stores
+ * ([128 + c]), consumer wave 0 saw chunk c's slots ready ([256 + c]) and
+ * finished chunk c ([384 + c]), for c < 128 (0 = no record).  Returns the
+ * number of workgroup records written. */
+int llar_get_pipeline_trace(llar_comm* h, uint64_t* host_dst, int max_records);
 
 /* Workgroup geometry the library would launch for this call (for tests and
  * tuning): writes grid size, threads per workgroup, slices and chunks. */

@@ -26,7 +26,7 @@ __all__ = [
     "llar_set_option", "llar_get_option", "llar_get_device_status", "llar_clear_device_status",
     "llar_select_protocol", "llar_debug_copy_staging", "llar_staging_bytes", "llar_get_epoch",
     "llar_get_timing", "llar_wallclock_hz", "llar_launch_geometry", "llar_floor_measure",
-    "llar_status_string", "llar_last_error", "llar_get_trace", "Communicator", "EXPORTED_SYMBOLS",
+    "llar_status_string", "llar_last_error", "llar_get_trace", "llar_get_pipeline_trace", "Communicator", "EXPORTED_SYMBOLS",
 ]
 
 FP32, FP16, BF16 = 0, 1, 2
@@ -42,7 +42,7 @@ EXPORTED_SYMBOLS = (
     "llar_get_device_status", "llar_clear_device_status", "llar_set_option", "llar_get_option",
     "llar_select_protocol", "llar_debug_copy_staging", "llar_staging_bytes", "llar_get_epoch",
     "llar_get_timing", "llar_wallclock_hz", "llar_launch_geometry", "llar_floor_measure",
-    "llar_get_trace",
+    "llar_get_trace", "llar_get_pipeline_trace",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
         "llar_launch_geometry": (i32, [vp, sz, i32, ip, ip, ip, ip]),
         "llar_floor_measure": (i32, [i32, i32, ctypes.POINTER(ctypes.c_double)]),
         "llar_get_trace": (i32, [vp, u64p, i32]),
+        "llar_get_pipeline_trace": (i32, [vp, u64p, i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -182,6 +183,15 @@ def llar_get_trace(h: int, max_records: int = 4096):
     buf = np.zeros((int(max_records), 8), dtype=np.uint64)
     n = _check(lib().llar_get_trace(h, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), int(max_records)),
                "llar_get_trace")
+    return buf[:n]
+
+
+def llar_get_pipeline_trace(h: int, max_records: int = 1024):
+    """(n_workgroups, 512) uint64 per-chunk stamps of the last traced pipelined call."""
+    import numpy as np
+    buf = np.zeros((int(max_records), 512), dtype=np.uint64)
+    n = _check(lib().llar_get_pipeline_trace(h, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), int(max_records)),
+               "llar_get_pipeline_trace")
     return buf[:n]
 
 

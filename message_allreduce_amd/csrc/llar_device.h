@@ -212,6 +212,7 @@ __device__ __forceinline__ bool sentinel_ready(const u32x4& v) {
 
 // ---- device control block --------------------------------------------------------------
 constexpr int kTimingRing = 64;
+constexpr int kTimingMaxWgs = 4096;  // largest grid that timing mode records
 constexpr uint32_t kStatusTimeout = 1u;
 constexpr uint32_t kStatusPlacement = 2u;
 
@@ -222,7 +223,8 @@ struct Ctrl {
   uint32_t pad1[31];
   uint32_t status;     // sticky error bits
   uint32_t pad2[31];
-  uint64_t timing[kTimingRing][2];  // per epoch slot: first start, last end (wall ticks)
+  uint32_t timing_grid[kTimingRing];  // per epoch slot: workgroups that recorded a span
+  uint64_t* timing_wg;  // [kTimingRing][kTimingMaxWgs][2]: each workgroup's start, end (wall ticks)
 };
 
 // Epochs: host-numbered calls use 1 .. 2^31-1, device-numbered (graph

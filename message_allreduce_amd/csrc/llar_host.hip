@@ -33,9 +33,11 @@ constexpr size_t kCapSentinel = 16ull << 20;
 constexpr size_t kCapLL128 = 16ull << 20;
 constexpr size_t kCapChunk = 4ull << 20;  // largest chunk of the pipelined protocols
 constexpr int kTraceMaxWgs = 4096;
-// The pipelined Sentinel keeps 4 staging buffers so that a producer may run
-// one chunk further ahead of its consumer (safe with >= 2 * lag + 2 buffers).
-constexpr uint32_t kSentinelPipeBuffers = 4;
+constexpr int kPipeTraceMaxWgs = 1024;
+// The pipelined Sentinel has up to 8 staging buffers: with B buffers a
+// producer may run B/2 - 1 chunks further ahead of its consumer (safe with
+// B >= 2 * lag + 2).  Default 4.
+constexpr uint32_t kSentinelPipeMaxBuffers = 8;
 
 size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
 
@@ -59,8 +61,11 @@ struct llar_comm {
   Ctrl* ctrl = nullptr;
   Region ll, sent, ll128, ll128_pipe, sent_pipe;
   bool local_ok = false;  // workgroup b runs on XCD b % 8
+  uint64_t* timing_wg = nullptr;  // kTimingRing x kTimingMaxWgs x 2 per-workgroup spans of timed calls
   uint64_t* trace = nullptr;  // kTraceMaxWgs x kTraceWords stamps of the last traced one-shot call
   int trace_grid = 0;
+  uint64_t* pipe_trace = nullptr;  // kPipeTraceMaxWgs x kPipeTraceWords stamps of the last traced pipeline call
+  int pipe_trace_grid = 0;
   uint32_t host_epoch = 1;         // epoch of the next host-numbered call
   bool last_call_device = false;   // the last call read the device-resident epoch
   // options
@@ -75,7 +80,8 @@ struct llar_comm {
   long long debug_drop_rank = -1;
   long long trace_on = 0;
   long long device_epoch = 0;  // 1: always read the device-resident epoch
-  long long thr_sentinel = 2048;          // AUTO: LL below (<=) this many bytes
+  long long pipe_buffers = 4;  // staging buffers of the pipelined Sentinel (2, 4, 6 or 8)
+  long long thr_sentinel = 64ll << 10;    // AUTO: LL up to (<=) this many bytes
   long long thr_ll128 = 1ll << 62;        // AUTO: one-shot Sentinel up to here (LL128 one round above)
   long long thr_pipelined = 512ll << 10;  // AUTO: pipelined Sentinel above this
 };
@@ -104,10 +110,7 @@ hipError_t init_ctrl(llar_comm* h) {
   Ctrl c;
   memset(&c, 0, sizeof(c));
   c.epoch = 0x80000001u;  // first device-numbered epoch
-  for (int i = 0; i < kTimingRing; ++i) {
-    c.timing[i][0] = ~0ull;
-    c.timing[i][1] = 0ull;
-  }
+  c.timing_wg = h->timing_wg;
   return hipMemcpy(h->ctrl, &c, sizeof(c), hipMemcpyHostToDevice);
 }
 
@@ -134,6 +137,10 @@ void destroy_all(llar_comm* h) {
   h->ctrl = nullptr;
   if (h->trace) (void)hipFree(h->trace);
   h->trace = nullptr;
+  if (h->timing_wg) (void)hipFree(h->timing_wg);
+  h->timing_wg = nullptr;
+  if (h->pipe_trace) (void)hipFree(h->pipe_trace);
+  h->pipe_trace = nullptr;
   delete h;
 }
 
@@ -334,15 +341,18 @@ llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes) {
   size_t cap = sentinel_shard_cap(chunk_cap, N);
   h->sent_pipe.parity_stride = (size_t)N * (size_t)N * cap * 16;
 
-  e = hipMalloc(&h->ctrl, sizeof(Ctrl));
+  e = hipMalloc(&h->timing_wg, (size_t)kTimingRing * kTimingMaxWgs * 2 * sizeof(uint64_t));
+  if (e == hipSuccess) e = hipMalloc(&h->ctrl, sizeof(Ctrl));
   if (e == hipSuccess) e = init_ctrl(h);
   if (e == hipSuccess) e = hipMalloc(&h->trace, (size_t)kTraceMaxWgs * kTraceWords * sizeof(uint64_t));
   if (e == hipSuccess) e = hipMemset(h->trace, 0, (size_t)kTraceMaxWgs * kTraceWords * sizeof(uint64_t));
+  if (e == hipSuccess) e = hipMalloc(&h->pipe_trace, (size_t)kPipeTraceMaxWgs * kPipeTraceWords * sizeof(uint64_t));
+  if (e == hipSuccess) e = hipMemset(h->pipe_trace, 0, (size_t)kPipeTraceMaxWgs * kPipeTraceWords * sizeof(uint64_t));
   if (e == hipSuccess) e = alloc_region(h->ll, 2 * h->ll.parity_stride, 0);
   if (e == hipSuccess) e = alloc_region(h->sent, 2 * h->sent.parity_stride, 0xFF);
   if (e == hipSuccess) e = alloc_region(h->ll128, 2 * h->ll128.parity_stride, 0);
   if (e == hipSuccess) e = alloc_region(h->ll128_pipe, 2 * h->ll128_pipe.parity_stride, 0);
-  if (e == hipSuccess) e = alloc_region(h->sent_pipe, kSentinelPipeBuffers * h->sent_pipe.parity_stride, 0xFF);
+  if (e == hipSuccess) e = alloc_region(h->sent_pipe, kSentinelPipeMaxBuffers * h->sent_pipe.parity_stride, 0xFF);
   // every region is addressed with 32-bit offsets
   const Region* regs[] = {&h->ll, &h->sent, &h->ll128, &h->ll128_pipe, &h->sent_pipe};
   for (const Region* r : regs)
@@ -441,6 +451,7 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
   int occ = occupancy(h->kind, h->n_ranks, g.kernel, g.threads);
   if (occ <= 0) return fail(LLAR_ERR_HIP);
   if (ls.grid > occ * h->cu_count) return fail(LLAR_ERR_UNSUPPORTED);
+  if (h->timing && ls.grid > kTimingMaxWgs) return fail(LLAR_ERR_UNSUPPORTED);
 
   const uint64_t spin = (uint64_t)((double)h->spin_timeout_us * 1e-6 * h->wall_hz);
   // epoch source: the host numbers stream-ordered calls; a captured call
@@ -484,7 +495,7 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
     a.n_chunks = (uint32_t)g.chunks;
     a.stage_bytes = (uint32_t)reg->bytes;
     a.parity_stride = (uint32_t)reg->parity_stride;
-    a.n_buffers = (proto == LLAR_SENTINEL_PIPELINED) ? kSentinelPipeBuffers : 2u;
+    a.n_buffers = (proto == LLAR_SENTINEL_PIPELINED) ? (uint32_t)h->pipe_buffers : 2u;
     a.shard_cap = (proto == LLAR_SENTINEL_PIPELINED)
                       ? (uint32_t)(reg->parity_stride / ((size_t)h->n_ranks * h->n_ranks * 16))
                       : 0u;
@@ -495,6 +506,11 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
     a.keep = h->keep_staging ? 1u : 0u;
     a.drop_rank = h->debug_drop_rank < 0 ? 0xFFFFFFFFu : (uint32_t)h->debug_drop_rank;
     a.host_epoch = host_epoch;
+    a.trace = nullptr;
+    if (h->trace_on && (g.kernel == kKernSentinelPipe || g.kernel == kKernSentinelPipeLocal) && ls.grid <= kPipeTraceMaxWgs) {
+      a.trace = h->pipe_trace;
+      h->pipe_trace_grid = ls.grid;
+    }
     // the chunk must fit the staging that was allocated
     if (proto == LLAR_SENTINEL_PIPELINED) {
       uint32_t need = sentinel_shard_cap((size_t)g.chunk_elems * h->elem, h->n_ranks);
@@ -548,6 +564,7 @@ static long long* option_slot(llar_comm* h, const char* key) {
       {"debug_drop_rank", &llar_comm::debug_drop_rank},
       {"trace", &llar_comm::trace_on},
       {"device_epoch", &llar_comm::device_epoch},
+      {"pipeline_buffers", &llar_comm::pipe_buffers},
       {"auto_threshold_sentinel", &llar_comm::thr_sentinel},
       {"auto_threshold_ll128", &llar_comm::thr_ll128},
       {"auto_threshold_pipelined", &llar_comm::thr_pipelined},
@@ -568,21 +585,17 @@ int llar_set_option(llar_comm* h, const char* key, long long value) {
   if (strcmp(key, "threads") == 0 && !(value == 0 || value == 64 || value == 128 || value == 256 || value == 512))
     return fail(LLAR_ERR_ARG);
   if (strcmp(key, "placement") == 0 && (value < 0 || value > 2)) return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "pipeline_buffers") == 0 && !(value == 2 || value == 4 || value == 6 || value == 8))
+    return fail(LLAR_ERR_ARG);
   if (strcmp(key, "placement") == 0 && value == 2 && !h->local_ok) return fail(LLAR_ERR_UNSUPPORTED);
   if ((strcmp(key, "timing") == 0 || strcmp(key, "keep_staging") == 0 || strcmp(key, "trace") == 0 ||
        strcmp(key, "device_epoch") == 0) &&
       (value < 0 || value > 1))
     return fail(LLAR_ERR_ARG);
   if (strcmp(key, "timing") == 0 && value == 1 && h->timing == 0) {
-    // start from a clean timing ring (the epoch and status words are kept)
+    // start from an empty timing ring (the epoch and status words are kept)
     if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
-    std::vector<uint64_t> ring(2 * kTimingRing);
-    for (int i = 0; i < kTimingRing; ++i) {
-      ring[2 * i] = ~0ull;
-      ring[2 * i + 1] = 0ull;
-    }
-    if (hipMemcpy(&h->ctrl->timing[0][0], ring.data(), ring.size() * sizeof(uint64_t), hipMemcpyHostToDevice) != hipSuccess)
-      return fail(LLAR_ERR_HIP);
+    if (hipMemset(h->ctrl->timing_grid, 0, sizeof(uint32_t) * kTimingRing) != hipSuccess) return fail(LLAR_ERR_HIP);
   }
   if (strcmp(key, "debug_drop_rank") == 0 && (value < -1 || value >= h->n_ranks)) return fail(LLAR_ERR_ARG);
   *slot = value;
@@ -632,6 +645,23 @@ int llar_get_timing(llar_comm* h, uint64_t* host_dst, int count) {
   if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
   Ctrl c;
   if (hipMemcpy(&c, h->ctrl, sizeof(Ctrl), hipMemcpyDeviceToHost) != hipSuccess) return fail(LLAR_ERR_HIP);
+  std::vector<uint64_t> wg;
+  // the call's span: first start and last end over its workgroups
+  auto span = [&](uint32_t slot, uint64_t& t0, uint64_t& t1) -> bool {
+    t0 = ~0ull;
+    t1 = 0ull;
+    const uint32_t g = c.timing_grid[slot];
+    if (g == 0u || g > (uint32_t)kTimingMaxWgs) return true;
+    wg.resize(2 * (size_t)g);
+    if (hipMemcpy(wg.data(), h->timing_wg + (size_t)slot * kTimingMaxWgs * 2, wg.size() * sizeof(uint64_t),
+                  hipMemcpyDeviceToHost) != hipSuccess)
+      return false;
+    for (uint32_t b = 0; b < g; ++b) {
+      t0 = std::min(t0, wg[2 * b]);
+      t1 = std::max(t1, wg[2 * b + 1]);
+    }
+    return true;
+  };
   int n = std::min(count, kTimingRing - 1);
   // the next call's slot has not run yet; the last n epochs precede it
   const bool dev = h->last_call_device;
@@ -641,8 +671,7 @@ int llar_get_timing(llar_comm* h, uint64_t* host_dst, int count) {
     uint32_t ep = e & 0x7FFFFFFFu;
     for (int k = 0; k < i; ++k) ep = (ep == 1u) ? 0x7FFFFFFFu : ep - 1u;
     if (dev) ep |= 0x80000000u;
-    host_dst[2 * written] = c.timing[ep % kTimingRing][0];
-    host_dst[2 * written + 1] = c.timing[ep % kTimingRing][1];
+    if (!span(ep % kTimingRing, host_dst[2 * written], host_dst[2 * written + 1])) return fail(LLAR_ERR_HIP);
     ++written;
   }
   return written;
@@ -653,6 +682,16 @@ int llar_get_trace(llar_comm* h, uint64_t* host_dst, int max_records) {
   if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
   int n = std::min(max_records, h->trace_grid);
   if (n > 0 && hipMemcpy(host_dst, h->trace, (size_t)n * kTraceWords * sizeof(uint64_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(LLAR_ERR_HIP);
+  return n;
+}
+
+int llar_get_pipeline_trace(llar_comm* h, uint64_t* host_dst, int max_records) {
+  if (!h || !host_dst || max_records < 0) return fail(LLAR_ERR_ARG);
+  if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
+  int n = std::min(max_records, h->pipe_trace_grid);
+  if (n > 0 && hipMemcpy(host_dst, h->pipe_trace, (size_t)n * kPipeTraceWords * sizeof(uint64_t),
+                         hipMemcpyDeviceToHost) != hipSuccess)
     return fail(LLAR_ERR_HIP);
   return n;
 }

@@ -75,7 +75,14 @@ struct TwoShotArgs {
   uint32_t keep;
   uint32_t drop_rank;
   uint32_t host_epoch;
+  uint64_t* trace;       // per-workgroup, per-chunk stamps (kPipeTraceWords each), or null
 };
+
+// per-chunk trace of the pipelined Sentinel: per workgroup 4 x kPipeTraceChunks
+// stamps (producer credit granted, producer stores issued, consumer slots
+// ready, consumer done) of the first kPipeTraceChunks chunks
+constexpr int kPipeTraceChunks = 128;
+constexpr int kPipeTraceWords = 4 * kPipeTraceChunks;
 
 // phase trace of the one-shot kernel: per workgroup, thread 0 records
 constexpr int kTraceWords = 8;  // start, epoch, input, ready, out-acked, end, id, spare

@@ -34,35 +34,29 @@ namespace llar {
 // through LDS and takes an arrival ticket; the workgroup that arrives last
 // (ticket == G-1) advances it when it finishes -- by then every workgroup of
 // the call has read the old value, and the next call starts after this one.
-// Timing mode also counts arrivals so that the last workgroup can clear the
-// next call's timing slot.
+// Timing mode has each workgroup store its own start and end stamps in the
+// epoch's ring slot (plain stores, no shared counter); workgroup 0 also
+// records the grid so that the reader knows how many entries belong to it.
 struct WgState {
   uint32_t epoch;
   uint32_t ticket;
   bool counted;
+  uint64_t t0;
 };
 
 __device__ __forceinline__ WgState wg_begin(Ctrl* ctrl, uint32_t host_epoch, bool timing, bool idle) {
   __shared__ uint32_t s_epoch;
-  WgState st{host_epoch, 0u, false};
-  const bool device_epoch = (host_epoch == 0u);
-  if (!device_epoch && !timing) return st;
+  WgState st{host_epoch, 0u, false, 0ull};
+  if (timing && threadIdx.x == 0) st.t0 = wall_ticks();
+  if (host_epoch != 0u) return st;
   if (threadIdx.x == 0) {
-    uint64_t t0 = wall_ticks();
-    uint32_t e = host_epoch;
-    if (device_epoch) {
-      e = __hip_atomic_load(&ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_epoch = e;
-    }
+    const uint32_t e = __hip_atomic_load(&ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_epoch = e;
     st.ticket = __hip_atomic_fetch_add(&ctrl->arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     st.counted = true;
-    if (timing && !idle)
-      __hip_atomic_fetch_min(&ctrl->timing[e % kTimingRing][0], t0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (device_epoch) {
-    __syncthreads();
-    st.epoch = s_epoch;
-  }
+  __syncthreads();
+  st.epoch = s_epoch;
   return st;
 }
 
@@ -72,20 +66,18 @@ __device__ __forceinline__ void wg_end(Ctrl* ctrl, const WgState& st, uint32_t h
     drain_vm();
     __syncthreads();
   }
-  if (threadIdx.x == 0 && st.counted) {
-    if (timing && !idle) {
-      uint64_t t1 = wall_ticks();
-      __hip_atomic_fetch_max(&ctrl->timing[st.epoch % kTimingRing][1], t1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (st.ticket == grid - 1u) {
-      uint32_t ne = (host_epoch == 0u) ? next_device_epoch(st.epoch) : next_host_epoch(st.epoch);
-      if (timing) {
-        __hip_atomic_store(&ctrl->timing[ne % kTimingRing][0], ~0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&ctrl->timing[ne % kTimingRing][1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __hip_atomic_store(&ctrl->arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (host_epoch == 0u) __hip_atomic_store(&ctrl->epoch, ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+  if (threadIdx.x != 0) return;
+  if (timing) {
+    const uint64_t t1 = wall_ticks();
+    const uint32_t slot = st.epoch % kTimingRing;
+    uint64_t* p = ctrl->timing_wg + ((size_t)slot * kTimingMaxWgs + blockIdx.x) * 2u;
+    p[0] = idle ? ~0ull : st.t0;
+    p[1] = idle ? 0ull : t1;
+    if (blockIdx.x == 0) ctrl->timing_grid[slot] = grid;
+  }
+  if (st.counted && st.ticket == grid - 1u) {
+    __hip_atomic_store(&ctrl->arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ctrl->epoch, next_device_epoch(st.epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -141,10 +133,12 @@ __device__ __forceinline__ void store_unit(uint8_t* p, uint64_t u, uint64_t nbyt
     *reinterpret_cast<uint16_t*>(p + i) = (uint16_t)(x[k >> 2] >> ((k & 2u) * 8u));
   }
 }
+template <bool kStream = false>
 __device__ __forceinline__ void store_vec(uint8_t* p, uint64_t v, uint64_t nbytes, u32x4 x) {
   uint64_t off = v * 16u;
   if (off + 16u <= nbytes) {
-    *reinterpret_cast<u32x4*>(p + off) = x;
+    if constexpr (kStream) __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p + off));
+    else *reinterpret_cast<u32x4*>(p + off) = x;
     return;
   }
   for (uint64_t i = off; i < nbytes; i += 2u) {
@@ -483,25 +477,29 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// two-shot Sentinel, chunked and double-buffered, producer/consumer waves
+// two-shot Sentinel, chunked and multi-buffered, producer/consumer waves
 // ---------------------------------------------------------------------------
-// Staging: [parity][owner s][sender rank r][vector of s's shard] 16 B,
-// all-ones when empty.  Chunk c's vectors are split into N owner shards and
-// each shard into W slices.  Workgroup (r, w) is split in two halves:
-//   producer waves: for every chunk c, load rank r's vectors of slice (s, w)
-//            for every owner s != r, then -- once this workgroup's consumer
-//            waves have finished chunk c-1 -- store them, sentinel-
-//            canonicalised, into [c&1][s][r];
-//   consumer waves: for each vector of slice (r, w) of chunk c, read the
-//            own partial, poll the N-1 slots [c&1][r][*] until no element is
-//            the sentinel, add in binary64 in rank order, round, write `out`,
-//            reset the slots; drain (the resets are performed), then publish
-//            "chunk c done" to the producer waves through LDS.
-// The credit: the consumer finished chunk c-1 only after every peer's
-// producer stored chunk c-1, which each did only after its own consumer had
-// finished chunk c-2 -- the previous user of chunk c's parity -- and had
-// drained those resets.  Loads of chunk c+1 are issued before that wait, so
-// HBM reads keep streaming while the consumers work.
+// Staging: [buffer][owner s][sender r][vector of s's shard] 16 B, all-ones
+// when empty.  Chunk c's vectors are split into N owner shards and each
+// shard into W slices; a vector keeps its (owner, slice) in every chunk
+// (the partition uses the nominal chunk, the tail of the message is masked).
+// Workgroup (r, w) is split in two halves:
+//   producer waves: for every chunk c, request rank r's vectors of slice
+//            (s, w) for every owner s != r, then -- once this workgroup's
+//            consumer waves have finished chunks 0..c-1-lag -- store them,
+//            sentinel-canonicalised, into [c % B][s][r].  The loads are
+//            issued before the credit wait, so HBM reads overlap it;
+//   consumer waves: for each vector of slice (r, w) of chunk c, poll the N-1
+//            slots [c % B][r][*], add the own partial (requested one chunk
+//            early) and the N-1 staged ones in binary64 in rank order, round,
+//            write `out`, reset the slots; drain (the resets are performed),
+//            then publish "chunk c done" to the producer waves through LDS.
+// The credit: a producer stores chunk c only after this workgroup's
+// consumers finished chunk c-1-lag.  They finished it only after every
+// peer's producer stored chunk c-1-lag, which each did only after its own
+// consumers had finished chunk c-2-2*lag and drained those resets; with
+// B >= 2*lag + 2 buffers that covers chunk c-B, the previous user of chunk
+// c's buffer.
 template <int kKind, int N, bool kLocal>
 __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   constexpr int kU = 2;   // vectors per producer lane per owner per batch
@@ -523,11 +521,16 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   const uint32_t slot_bytes = a.shard_cap * 16u;
   const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
   const uint32_t n_prod = n_waves / 2, n_cons = n_waves - n_prod;
-  // n_buf staging buffers; a producer may run credit_lag chunks further ahead
-  // of its consumer, which is safe when n_buf >= 2 * credit_lag + 2
   const uint32_t n_buf = a.n_buffers;
   const uint32_t lag = n_buf / 2u - 1u;
+  // the partition uses the nominal chunk so that a slot keeps its (owner,
+  // slice) in every chunk; vectors past the end of the message are masked
+  const uint32_t nv = chunk_vecs;
   bool dead = idle;
+  uint64_t* tr = (a.trace && !idle) ? a.trace + (uint64_t)blockIdx.x * kPipeTraceWords : nullptr;
+  auto stamp = [&](int kind, uint32_t c) {
+    if (tr && lane == 0 && c < (uint32_t)kPipeTraceChunks) tr[kind * kPipeTraceChunks + c] = wall_ticks();
+  };
 
   if (wave < n_prod) {
     // ---------------- producer waves
@@ -574,6 +577,7 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
           }
           if (dead) break;
         }
+        if (b0 == 0 && wave == 0) stamp(0, c);
         if (silent) continue;
 #pragma unroll
         for (int k = 0; k < N - 1; ++k) {
@@ -584,6 +588,7 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
             if (vo[k][u] != ~0u) st16_stage<kLocal>(rs, slot + vo[k][u] * 16u, sentinel_canon<kKind>(x[k][u]));
         }
       }
+      if (wave == 0) stamp(1, c);
     }
   } else {
     // ---------------- consumer waves
@@ -605,6 +610,7 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
       const uint32_t nv_real = (uint32_t)min((uint64_t)chunk_vecs, total_vecs - vbase);
       const uint32_t s1 = min(s1n, max(nv_real, s0));
       const uint32_t my = (c % n_buf) * a.parity_stride + (uint32_t)(r * N) * slot_bytes;
+      if (s1 == s0 && cw == 0) stamp(2, c);  // nothing of this chunk here
       for (uint32_t b0 = 0; b0 < s1 - s0 && !dead; b0 += kUc * CL) {
         u32x4 own[kUc];
         bool valid[kUc];
@@ -638,6 +644,7 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
           }
         }
         if (dead) break;
+        if (b0 == 0 && cw == 0) stamp(2, c);
 #pragma unroll
         for (int u = 0; u < kUc; ++u) {
           if (!valid[u]) continue;
@@ -655,6 +662,7 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
       }
       // the resets are performed before the producers may reuse the buffer
       drain_vm();
+      if (cw == 0) stamp(3, c);
       if (lane == 0 && !__any((int)dead))
         __hip_atomic_store(&s_done[cw], c + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       // request the next chunk's own vectors while the producers fill it

@@ -319,6 +319,38 @@ def test_sentinel_pipelined_chunks_and_placements(placement, chunk):
         assert (c.staging(llar.SENTINEL_PIPELINED) == 0xFF).all()
 
 
+@pytest.mark.parametrize("buffers", [2, 4, 6, 8])
+def test_sentinel_pipelined_buffers_and_credit_order(buffers):
+    """Every staging-buffer count gives the exact sum, and the per-chunk
+    stamps of each workgroup follow the credit rule: with B buffers the
+    producers enter chunk c only after this workgroup's consumers finished
+    chunk c - B/2 (lag B/2 - 1), and the consumers take the chunks in order."""
+    dt = BF16
+    n = (3 << 20) // 2 + 11  # 3 MiB + a ragged tail: 49 chunks of 64 KiB
+    chunk = 65536
+    bits = make_partials(1050, buffers, 8, "bf16", n, "normal", 1.0)
+    with comm_for(8, dt, n * 2, chunk_bytes=chunk, pipeline_buffers=buffers, trace=1) as c:
+        got = run(c, bits, "sentinel_pipelined", dt)
+        assert_exact(got, oracle.allreduce(bits, dt), dt, "buffers %d" % buffers)
+        assert (c.staging(llar.SENTINEL_PIPELINED) == 0xFF).all()
+        geo = c.geometry(n, llar.SENTINEL_PIPELINED)
+        chunks = geo["chunks"]
+        assert chunks == -(-(n * 2) // chunk) and chunks <= 128
+        tr = llar.llar_get_pipeline_trace(c.h).astype(np.int64)
+        assert tr.shape[0] == geo["grid"]
+        lag = buffers // 2 - 1
+        working = tr[:, 0] != 0  # padding workgroups of the local placement record nothing
+        assert working.sum() == 8 * geo["slices"]
+        credit, stored = tr[working, 0:chunks], tr[working, 128:128 + chunks]
+        ready, done = tr[working, 256:256 + chunks], tr[working, 384:384 + chunks]
+        for a_ in (credit, stored, ready, done):
+            assert (a_ > 0).all()
+        assert (stored >= credit).all()
+        assert (done >= ready).all()
+        assert (ready[:, 1:] >= done[:, :-1]).all()
+        assert (credit[:, lag + 1:] >= done[:, :chunks - lag - 1]).all()
+
+
 @pytest.mark.parametrize("threads", [64, 128, 256, 512])
 @pytest.mark.parametrize("proto", ALL_PROTOCOLS)
 def test_workgroup_sizes(proto, threads):
