@@ -118,7 +118,9 @@ int llar_clear_device_status(llar_comm* h);
  *   "spin_timeout_us"  device poll limit in microseconds (default 200000)
  *   "ll128_acc"        LL128 staging type: 0 = binary32 (default), 1 = the I/O type (16-bit packed)
  *   "chunk_bytes"      per-rank chunk of the pipelined protocols (0 = tuned default)
- *   "slices"           workgroups per rank (0 = tuned default)
+ *   "slices"           workgroups per rank (0 = tuned default); for the pipelined protocols an
+ *                      upper bound: every owner slice of a full chunk keeps at least one line
+ *                      (LL128) or vector (Sentinel), because the credit is earned by consuming
  *   "threads"          threads per workgroup: 64, 128, 256 or 512 (0 = tuned default); the
  *                      pipelined Sentinel splits a workgroup into producer and consumer waves
  *                      and needs at least 128

@@ -205,6 +205,13 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
       g.threads = h->threads ? (int)h->threads : 64;
       size_t per_wg = (size_t)(g.threads / 64) * 8;  // lines one workgroup covers per step
       g.slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(per_owner, per_wg), 1, 64);
+      if (g.chunks > 1) {
+        // the implicit credit reaches a workgroup only through lines of its
+        // own: every owner slice of a full chunk must hold at least one line
+        size_t min_owner = ceil_div(chunk_elems, K) / (size_t)N;
+        if (min_owner == 0) return LLAR_ERR_UNSUPPORTED;
+        g.slices = (int)std::min<size_t>((size_t)g.slices, min_owner);
+      }
       break;
     }
     case LLAR_SENTINEL_PIPELINED: {
@@ -221,6 +228,13 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
       // measured on MI355X (64 MiB x 8 bf16): 1 MiB chunks, 512 threads and
       // 32 slices per rank (one workgroup per CU) stream best
       g.slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(per_owner, (size_t)g.threads / 2), 1, 32);
+      if (g.chunks > 1) {
+        // the credit is earned by consuming: every owner slice of a full
+        // chunk must hold at least one vector
+        size_t min_owner = (cb / 16) / (size_t)N;
+        if (min_owner == 0) return LLAR_ERR_UNSUPPORTED;
+        g.slices = (int)std::min<size_t>((size_t)g.slices, min_owner);
+      }
       break;
     }
     default:

@@ -323,9 +323,14 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
 //   consume: for each line of slice (r, w), poll slot 0 until it reads N,
 //            read the line, round to the I/O type, write `out`, zero the line.
 // Implicit credit: finishing consume(c+1) means every rank's slice-w
-// workgroup has contributed chunk c+1, which each did only after finishing
-// its own consume(c) (zeroing its chunk-c lines), so the parity of chunk c is
-// free again for chunk c+2.
+// workgroup has contributed chunk c+1 to this workgroup's lines (every line
+// receives all N contributions), which each did only after all of its waves
+// had finished consume(c) and their zeroing stores were acknowledged (drain
+// + workgroup barrier between chunks), so the parity of chunk c is free again
+// for chunk c+2.  The credit is the workgroup's: a wave may have no line of
+// its own to consume while it produces into other owners' lines.  The host
+// keeps every owner slice of a full chunk non-empty, so every workgroup
+// receives the credit.
 template <int kKind, int kAcc16, int N>
 __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
   int r;
@@ -345,7 +350,7 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
   else flag_full = E::from_f32((float)N);
   bool dead = idle;  // idle padding workgroup, or a poll timed out
 
-  for (uint32_t c = 0; c < a.n_chunks && !__any((int)dead); ++c) {
+  for (uint32_t c = 0; c < a.n_chunks && !dead; ++c) {
     const uint64_t cbase = (uint64_t)c * a.chunk_elems;
     const uint32_t len = (uint32_t)min((uint64_t)a.chunk_elems, a.n - cbase);
     // Lines are partitioned by the nominal chunk (not this chunk's length):
@@ -353,6 +358,9 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
     // implicit credit of one slice would release a line another slice has
     // not consumed yet.  Elements past the message end are masked.
     const uint32_t L = (a.chunk_elems + K - 1) / K;
+    // lines that hold data of this chunk: producers flag and consumers poll
+    // only these (both sides agree, and a line past them stays zero)
+    const uint32_t Lr = (len + K - 1) / K;
     const uint32_t poff = (c & 1u) * a.parity_stride;
 
     // ---- produce: data atomics for every owner's slice w
@@ -360,7 +368,7 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
     for (int s = 0; s < N && !silent; ++s) {
       uint32_t o0 = (uint32_t)((uint64_t)s * L / N), o1 = (uint32_t)((uint64_t)(s + 1) * L / N);
       uint32_t l0 = o0 + (uint32_t)((uint64_t)w * (o1 - o0) / a.slices);
-      uint32_t l1 = o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices);
+      uint32_t l1 = min(o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices), Lr);
       for (uint32_t lb = l0 + wave * 8u; lb < l1; lb += n_waves * 8u) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -403,7 +411,7 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
     for (int s = 0; s < N && !silent; ++s) {
       uint32_t o0 = (uint32_t)((uint64_t)s * L / N), o1 = (uint32_t)((uint64_t)(s + 1) * L / N);
       uint32_t l0 = o0 + (uint32_t)((uint64_t)w * (o1 - o0) / a.slices);
-      uint32_t l1 = o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices);
+      uint32_t l1 = min(o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices), Lr);
       for (uint32_t lb = l0 + wave * 8u; lb < l1; lb += n_waves * 8u) {
         uint32_t line = lb + lane;
         if (lane < 8u && line < l1) {
@@ -426,7 +434,7 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
     {
       uint32_t o0 = (uint32_t)((uint64_t)r * L / N), o1 = (uint32_t)((uint64_t)(r + 1) * L / N);
       uint32_t l0 = o0 + (uint32_t)((uint64_t)w * (o1 - o0) / a.slices);
-      uint32_t l1 = o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices);
+      uint32_t l1 = min(o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices), Lr);
       const uint32_t grp = lane >> 3, j = lane & 7u;
       for (uint32_t lb = l0 + wave * 8u; lb < l1; lb += n_waves * 8u) {
         uint32_t line = lb + grp;
@@ -446,7 +454,7 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
         }
         if (!ok) {
           dead = true;
-          continue;
+          break;
         }
         u32x4 v = ld16_coh(rs, loff + j * 16u);
         if constexpr (!kAcc16) {
@@ -472,6 +480,10 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
         if (!a.keep) st16_coh(rs, loff + j * 16u, u32x4{0u, 0u, 0u, 0u});
       }
     }
+    // every wave's zeroing stores are acknowledged before any wave of this
+    // workgroup contributes to the next chunk (a workgroup-uniform exit too)
+    drain_vm();
+    dead = __syncthreads_or((int)dead) != 0;
   }
   wg_end(a.ctrl, st, a.host_epoch, a.grid, a.timing, idle);
 }

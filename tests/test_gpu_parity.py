@@ -351,6 +351,39 @@ def test_sentinel_pipelined_buffers_and_credit_order(buffers):
         assert (credit[:, lag + 1:] >= done[:, :chunks - lag - 1]).all()
 
 
+@pytest.mark.parametrize("threads", [256, 512])
+def test_ll128_pipelined_multiwave_credit_regression(threads):
+    """Workload-4 shape (N = 8, fp32, 4 MiB in 64 KiB chunks) with several
+    waves per workgroup and 8 slices: owner slices then differ by one line,
+    so a wave can produce into another owner's line while having no line of
+    its own to consume.  The credit must still hold (it is the workgroup's)."""
+    dt = F32
+    n = 1 << 20
+    bits = make_partials(1700, threads, 8, "fp32", n, "uniform", 1.0)
+    with comm_for(8, dt, n * 4, chunk_bytes=65536, threads=threads, slices=8) as c:
+        c.set_option("spin_timeout_us", 20_000)
+        for rep in range(3):
+            got = run(c, bits, "ll128_pipelined", dt)
+            assert_tol(got, oracle.allreduce(bits, dt), dt, "threads %d rep %d" % (threads, rep))
+
+
+@pytest.mark.parametrize("proto", ["ll128_pipelined", "sentinel_pipelined"])
+def test_pipelined_slices_are_clamped_to_non_empty_owner_slices(proto):
+    """Asking for more slices than the smallest owner shard of a chunk has
+    lines / vectors gives the largest safe count, and stays exact."""
+    dt = BF16
+    n_ranks, chunk = 8, 2048  # 1024 elements: 34 LL128 lines (>= 4 per owner) / 128 vectors (16 per owner)
+    n = 40 * 1024 + 77
+    bits = make_partials(1710, 0, n_ranks, "bf16", n, "normal", 1.0)
+    with comm_for(n_ranks, dt, n * 2, chunk_bytes=chunk, slices=64) as c:
+        geo = c.geometry(n, llar.PROTOCOLS[proto])
+        per_owner = (chunk // 2 + 30) // 31 // n_ranks if proto == "ll128_pipelined" else chunk // 16 // n_ranks
+        assert geo["slices"] == per_owner
+        for rep in range(3):
+            got = run(c, bits, proto, dt)
+            check(got, oracle.allreduce(bits, dt), dt, proto, "rep %d" % rep)
+
+
 @pytest.mark.parametrize("threads", [64, 128, 256, 512])
 @pytest.mark.parametrize("proto", ALL_PROTOCOLS)
 def test_workgroup_sizes(proto, threads):
