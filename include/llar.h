@@ -117,13 +117,14 @@ int llar_clear_device_status(llar_comm* h);
 /* Options (key, value).  Keys:
  *   "spin_timeout_us"  device poll limit in microseconds (default 200000)
  *   "ll128_acc"        LL128 staging type: 0 = binary32 (default), 1 = the I/O type (16-bit packed)
- *   "chunk_bytes"      per-rank chunk of the pipelined protocols (0 = tuned default)
+ *   "chunk_bytes"      per-rank chunk of the pipelined protocols (0 = tuned default: 128 KiB for
+ *                      LL128, 1 MiB for the Sentinel; clamped to [1 KiB, 4 MiB] and to the message)
  *   "slices"           workgroups per rank (0 = tuned default); for the pipelined protocols an
  *                      upper bound: every owner slice of a full chunk keeps at least one line
  *                      (LL128) or vector (Sentinel), because the credit is earned by consuming
- *   "threads"          threads per workgroup: 64, 128, 256 or 512 (0 = tuned default); the
- *                      pipelined Sentinel splits a workgroup into producer and consumer waves
- *                      and needs at least 128
+ *   "threads"          threads per workgroup: 64, 128, 256 or 512, or 1024 for the slot-handshake
+ *                      Sentinel (0 = tuned default); the pipelined Sentinel splits a workgroup into
+ *                      producer and consumer waves and needs at least 128
  *   "pipeline_buffers" staging buffers of the pipelined Sentinel: 2, 4 (default), 6 or 8; with B
  *                      buffers a producer runs up to B/2 - 1 chunks ahead of its consumer
  *   "placement"        0 = auto, 1 = spread (rank r on XCD r mod 8), 2 = local (one slice's ranks share an XCD)

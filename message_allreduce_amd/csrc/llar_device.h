@@ -35,8 +35,18 @@ constexpr int kCpolNt = 2;
 constexpr int kCpolSc1 = 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // The inputs are uniform, but after divergent code (a thread-0 branch) the
+  // compiler may no longer prove it; a descriptor it believes divergent is
+  // kept in VGPRs and every buffer access becomes a readfirstlane loop, which
+  // also hides the memory counters from its wait analysis.  readfirstlane
+  // states the uniformity outright.
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* const ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
   // word3 0x00020000: raw (untyped) 32-bit data format for gfx9-family buffers
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)n, 0x00020000);
 }
 
 // ---- coherent accesses to staging -------------------------------------------
@@ -187,6 +197,11 @@ __device__ __forceinline__ u32x4 sentinel_canon(u32x4 v) {
   }
   return v;
 }
+// true when the whole 16-byte slot holds the sentinel (a consumer's reset
+// has fully landed); a slot that is partly reset is not empty yet
+__device__ __forceinline__ bool sentinel_is_empty(const u32x4& v) {
+  return (v[0] & v[1] & v[2] & v[3]) == 0xFFFFFFFFu;
+}
 // true when no element of the 8-byte unit still holds the sentinel
 template <int kKind>
 __device__ __forceinline__ bool sentinel_ready8(const u32x2& v) {
@@ -215,6 +230,14 @@ constexpr int kTimingRing = 64;
 constexpr int kTimingMaxWgs = 4096;  // largest grid that timing mode records
 constexpr uint32_t kStatusTimeout = 1u;
 constexpr uint32_t kStatusPlacement = 2u;
+
+// Kernel arguments live in memory; the scalar loads that fetch them miss a
+// cold scalar cache at launch.  Loads that the compiler sinks into later
+// branches, or chains behind one another, each cost a memory round trip on
+// the critical path.  Naming the uniform values a kernel needs in one empty
+// asm statement at entry makes them live there, so their loads are issued
+// together and waited for once.
+#define LLAR_UNIFORM_AT_ENTRY(...) asm volatile("" ::__VA_ARGS__)
 
 struct Ctrl {
   uint32_t epoch;      // current call's epoch, 1..2^32-1 (0 = never written)

@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <new>
+#include <numeric>
 #include <vector>
 
 #include "llar.h"
@@ -81,6 +82,8 @@ struct llar_comm {
   long long trace_on = 0;
   long long device_epoch = 0;  // 1: always read the device-resident epoch
   long long pipe_buffers = 4;  // staging buffers of the pipelined Sentinel (2, 4, 6 or 8)
+  long long sentinel_credit = 0;  // pipelined Sentinel: 0 = workgroup credit, 1 = slot handshake
+  long long cons_waves = 0;       // slot handshake: consumer waves per workgroup (0 = a quarter)
   long long thr_sentinel = 64ll << 10;    // AUTO: LL up to (<=) this many bytes
   long long thr_ll128 = 1ll << 62;        // AUTO: one-shot Sentinel up to here (LL128 one round above)
   long long thr_pipelined = 512ll << 10;  // AUTO: pipelined Sentinel above this
@@ -151,7 +154,7 @@ uint32_t sentinel_shard_cap(size_t chunk_bytes, int n_ranks) {
 
 size_t effective_chunk(const llar_comm* h, int proto) {
   size_t c = (size_t)h->chunk_bytes;
-  if (c == 0) c = (proto == LLAR_LL128_PIPELINED) ? (64u << 10) : (1u << 20);
+  if (c == 0) c = (proto == LLAR_LL128_PIPELINED) ? (128u << 10) : (1u << 20);
   c = std::min(c, kCapChunk);
   c = std::min(c, ceil_div(h->max_bytes, 16) * 16);  // never beyond one whole message
   c = std::max(c, (size_t)1024);
@@ -203,8 +206,10 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
       size_t lines = ceil_div(std::min(chunk_elems, n_elems), K);
       size_t per_owner = ceil_div(lines, (size_t)N);
       g.threads = h->threads ? (int)h->threads : 64;
-      size_t per_wg = (size_t)(g.threads / 64) * 8;  // lines one workgroup covers per step
-      g.slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(per_owner, per_wg), 1, 64);
+      // measured on MI355X: the atomic exchange is latency-bound per
+      // workgroup, so the most workgroups win -- one per line of an owner's
+      // shard, up to 64 per rank
+      g.slices = h->slices ? (int)h->slices : clampi((long long)per_owner, 1, 64);
       if (g.chunks > 1) {
         // the implicit credit reaches a workgroup only through lines of its
         // own: every owner slice of a full chunk must hold at least one line
@@ -216,14 +221,14 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
     }
     case LLAR_SENTINEL_PIPELINED: {
       size_t cb = effective_chunk(h, proto);
-      g.kernel = kKernSentinelPipe;
+      g.kernel = h->sentinel_credit ? kKernSentinelHs : kKernSentinelPipe;
       g.chunk_elems = (uint32_t)(cb / h->elem);
       g.chunks = (int)ceil_div(n_elems, (size_t)g.chunk_elems);
       size_t vecs = ceil_div(std::min(cb, nbytes), 16);
       size_t per_owner = ceil_div(vecs, (size_t)N);
       // half the waves produce, half consume: one owner-slice vector per
       // consumer lane per chunk
-      g.threads = h->threads ? (int)h->threads : 512;
+      g.threads = h->threads ? (int)h->threads : (h->sentinel_credit ? 1024 : 512);
       if (g.threads < 128) return LLAR_ERR_ARG;
       // measured on MI355X (64 MiB x 8 bf16): 1 MiB chunks, 512 threads and
       // 32 slices per rank (one workgroup per CU) stream best
@@ -250,11 +255,14 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
   if (place == kPlaceLocal) {
     g.grid_slices = (int)ceil_div((size_t)g.slices, 8) * 8;
     if (g.kernel == kKernSentinelPipe) g.kernel = kKernSentinelPipeLocal;
+    if (g.kernel == kKernSentinelHs) g.kernel = kKernSentinelHsLocal;
     if (g.kernel == kKernOneShotLL) g.kernel = kKernOneShotLLLocal;
     if (g.kernel == kKernOneShotSentinel) g.kernel = kKernOneShotSentinelLocal;
   }
   g.placement = place;
-  if (g.threads != 64 && g.threads != 128 && g.threads != 256 && g.threads != 512) return LLAR_ERR_ARG;
+  if (g.threads != 64 && g.threads != 128 && g.threads != 256 && g.threads != 512 && g.threads != 1024)
+    return LLAR_ERR_ARG;
+  if (g.threads == 1024 && g.kernel != kKernSentinelHs && g.kernel != kKernSentinelHsLocal) return LLAR_ERR_ARG;
   return LLAR_OK;
 }
 
@@ -490,6 +498,8 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
     a.rank_stride = (uint32_t)reg->rank_stride;
     a.grid = (uint32_t)ls.grid;
     a.slices = (uint32_t)g.slices;
+    a.vq = a.n_vec / a.slices;
+    a.vr = a.n_vec % a.slices;
     a.placement = g.placement;
     a.timing = h->timing ? 1u : 0u;
     a.keep = h->keep_staging ? 1u : 0u;
@@ -513,6 +523,34 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
     a.shard_cap = (proto == LLAR_SENTINEL_PIPELINED)
                       ? (uint32_t)(reg->parity_stride / ((size_t)h->n_ranks * h->n_ranks * 16))
                       : 0u;
+    if (g.kernel == kKernSentinelHs || g.kernel == kKernSentinelHsLocal) {
+      // Slot handshake: the chunk-c and chunk-(c - B) uses of a slot are
+      // consumer items c*n_bat + b and (c - B)*n_bat + b, taken by consumer
+      // wave item % n_cons, and producer items kH times those (plus the
+      // owner group), taken by producer wave item % n_prod.  A slot keeps one
+      // producer lane and one consumer lane only if n_prod divides
+      // B*n_bat*kH and n_cons divides B*n_bat: B is the smallest multiple of
+      // the least such period that is at least the requested buffer count.
+      const uint32_t nv = (uint32_t)((size_t)g.chunk_elems * h->elem / 16);
+      const uint32_t span = (uint32_t)ceil_div(ceil_div(nv, (size_t)h->n_ranks), (size_t)g.slices);
+      const uint32_t n_bat = (span + 63u) / 64u;
+      const uint32_t n_waves = (uint32_t)g.threads / 64u;
+      uint32_t n_cons = n_waves >= 4 ? n_waves / 4 : 1u;
+      if (h->cons_waves > 0) n_cons = (uint32_t)h->cons_waves;
+      if (n_cons >= n_waves) return fail(LLAR_ERR_ARG);
+      const uint32_t n_prod = n_waves - n_cons;
+      a.cons_waves = n_cons;
+      // producer items split a consumer item into kH owner groups
+      const uint32_t kg = (uint32_t)(h->n_ranks + 1) / 2u, kh = ((uint32_t)h->n_ranks + kg - 1u) / kg;
+      const uint32_t b_prod = n_prod / std::gcd(n_prod, n_bat * kh);
+      const uint32_t b_cons = n_cons / std::gcd(n_cons, n_bat);
+      const uint32_t b0 = std::lcm(b_prod, b_cons);
+      a.n_buffers = b0 * (uint32_t)ceil_div((size_t)h->pipe_buffers, (size_t)b0);
+      a.shard_cap = sentinel_shard_cap((size_t)g.chunk_elems * h->elem, h->n_ranks);
+      const size_t stride = (size_t)h->n_ranks * h->n_ranks * a.shard_cap * 16;
+      if (stride * a.n_buffers > reg->bytes) return fail(LLAR_ERR_UNSUPPORTED);
+      a.parity_stride = (uint32_t)stride;
+    }
     a.grid = (uint32_t)ls.grid;
     a.slices = (uint32_t)g.slices;
     a.placement = g.placement;
@@ -521,7 +559,9 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
     a.drop_rank = h->debug_drop_rank < 0 ? 0xFFFFFFFFu : (uint32_t)h->debug_drop_rank;
     a.host_epoch = host_epoch;
     a.trace = nullptr;
-    if (h->trace_on && (g.kernel == kKernSentinelPipe || g.kernel == kKernSentinelPipeLocal) && ls.grid <= kPipeTraceMaxWgs) {
+    const bool pipe_kernel = g.kernel == kKernSentinelPipe || g.kernel == kKernSentinelPipeLocal ||
+                             g.kernel == kKernSentinelHs || g.kernel == kKernSentinelHsLocal;
+    if (h->trace_on && pipe_kernel && ls.grid <= kPipeTraceMaxWgs) {
       a.trace = h->pipe_trace;
       h->pipe_trace_grid = ls.grid;
     }
@@ -579,6 +619,8 @@ static long long* option_slot(llar_comm* h, const char* key) {
       {"trace", &llar_comm::trace_on},
       {"device_epoch", &llar_comm::device_epoch},
       {"pipeline_buffers", &llar_comm::pipe_buffers},
+      {"sentinel_credit", &llar_comm::sentinel_credit},
+      {"consumer_waves", &llar_comm::cons_waves},
       {"auto_threshold_sentinel", &llar_comm::thr_sentinel},
       {"auto_threshold_ll128", &llar_comm::thr_ll128},
       {"auto_threshold_pipelined", &llar_comm::thr_pipelined},
@@ -596,11 +638,14 @@ int llar_set_option(llar_comm* h, const char* key, long long value) {
   if (strcmp(key, "ll128_acc") == 0 && (value < 0 || value > 1)) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "chunk_bytes") == 0 && (value < 0 || (size_t)value > kCapChunk)) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "slices") == 0 && (value < 0 || value > 1024)) return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "threads") == 0 && !(value == 0 || value == 64 || value == 128 || value == 256 || value == 512))
+  if (strcmp(key, "threads") == 0 && !(value == 0 || value == 64 || value == 128 || value == 256 || value == 512 ||
+                                        value == 1024))
     return fail(LLAR_ERR_ARG);
   if (strcmp(key, "placement") == 0 && (value < 0 || value > 2)) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "pipeline_buffers") == 0 && !(value == 2 || value == 4 || value == 6 || value == 8))
     return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "sentinel_credit") == 0 && (value < 0 || value > 1)) return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "consumer_waves") == 0 && (value < 0 || value > 15)) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "placement") == 0 && value == 2 && !h->local_ok) return fail(LLAR_ERR_UNSUPPORTED);
   if ((strcmp(key, "timing") == 0 || strcmp(key, "keep_staging") == 0 || strcmp(key, "trace") == 0 ||
        strcmp(key, "device_epoch") == 0) &&

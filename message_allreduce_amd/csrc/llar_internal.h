@@ -31,7 +31,9 @@ enum KernelId : int {
   kKernSentinelPipeLocal = 5,
   kKernOneShotLLLocal = 6,
   kKernOneShotSentinelLocal = 7,
-  kKernCount = 8
+  kKernSentinelHs = 8,
+  kKernSentinelHsLocal = 9,
+  kKernCount = 10
 };
 
 struct OneShotArgs {
@@ -42,6 +44,7 @@ struct OneShotArgs {
   uint64_t nbytes;       // bytes per rank
   uint64_t spin_limit;   // wall-clock ticks
   uint32_t n_vec;        // 16-byte vectors per rank (last one may be partial)
+  uint32_t vq, vr;       // slice w holds vq vectors, plus one more when w < vr
   uint32_t stage_bytes;  // size of the staging region (buffer descriptor bound)
   uint32_t parity_stride;
   uint32_t rank_stride;  // bytes per sending rank per parity
@@ -67,7 +70,8 @@ struct TwoShotArgs {
   uint32_t stage_bytes;
   uint32_t parity_stride;
   uint32_t shard_cap;    // Sentinel: 16-byte vectors per (owner, sender) slot
-  uint32_t n_buffers;    // Sentinel pipeline: staging buffers (2 or 4)
+  uint32_t n_buffers;    // Sentinel pipeline: staging buffers
+  uint32_t cons_waves;   // Sentinel slot handshake: consumer waves per workgroup
   uint32_t grid;
   uint32_t slices;
   uint32_t placement;

@@ -81,69 +81,76 @@ __device__ __forceinline__ void wg_end(Ctrl* ctrl, const WgState& st, uint32_t h
   }
 }
 
-__device__ __forceinline__ void decode_role(uint32_t b, int n_ranks, uint32_t placement, int& r, uint32_t& w) {
-  if (placement == kPlaceLocal) {
-    uint32_t x = b & 7u, q = b >> 3;
-    r = (int)(q % (uint32_t)n_ranks);
-    w = (q / (uint32_t)n_ranks) * 8u + x;
+// Role of workgroup b under a placement known at compile time (no kernel
+// argument is needed to find it).
+template <bool kLocal, int N>
+__device__ __forceinline__ void decode_role_t(uint32_t b, int& r, uint32_t& w) {
+  if constexpr (kLocal) {
+    const uint32_t x = b & 7u, q = b >> 3;
+    r = (int)(q % (uint32_t)N);
+    w = (q / (uint32_t)N) * 8u + x;
   } else {
-    r = (int)(b % (uint32_t)n_ranks);
-    w = b / (uint32_t)n_ranks;
+    r = (int)(b % (uint32_t)N);
+    w = b / (uint32_t)N;
   }
 }
 
 // ---------------------------------------------------------------------------
 // tail-safe 16-byte vector access to the caller's buffers
 // ---------------------------------------------------------------------------
+// Only the last vector of a message can be partial; its elements (2 or 4
+// bytes) are moved as halfwords.  Those paths are fully unrolled: a loop of
+// loads or stores with a run-time trip count would leave the compiler unable
+// to count outstanding memory operations, and every later wait in the
+// kernel would then drain all of them (vmcnt(0)) instead of only the ones it
+// needs, which serialises the software pipelines.
 template <bool kStream = true>
 __device__ __forceinline__ u32x4 load_vec(const uint8_t* p, uint64_t v, uint64_t nbytes) {
-  uint64_t off = v * 16u;
+  const uint64_t off = v * 16u;
   if (off + 16u <= nbytes) {
     if constexpr (kStream) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + off));
     else return *reinterpret_cast<const u32x4*>(p + off);
   }
   u32x4 x = {0u, 0u, 0u, 0u};
-  for (uint64_t i = off; i < nbytes; i += 2u) {  // element sizes are 2 or 4 bytes
-    uint32_t h = *reinterpret_cast<const uint16_t*>(p + i);
-    uint32_t k = (uint32_t)(i - off);
-    x[k >> 2] |= h << ((k & 2u) * 8u);
+#pragma unroll
+  for (uint32_t k = 0; k < 16u; k += 2u) {
+    if (off + k < nbytes) x[k >> 2] |= (uint32_t)(*reinterpret_cast<const uint16_t*>(p + off + k)) << ((k & 2u) * 8u);
   }
   return x;
 }
 // 8-byte units (the one-shot consumer's granularity)
 __device__ __forceinline__ u32x2 load_unit(const uint8_t* p, uint64_t u, uint64_t nbytes) {
-  uint64_t off = u * 8u;
+  const uint64_t off = u * 8u;
   if (off + 8u <= nbytes) return *reinterpret_cast<const u32x2*>(p + off);
   u32x2 x = {0u, 0u};
-  for (uint64_t i = off; i < nbytes; i += 2u) {
-    uint32_t h = *reinterpret_cast<const uint16_t*>(p + i);
-    uint32_t k = (uint32_t)(i - off);
-    x[k >> 2] |= h << ((k & 2u) * 8u);
+#pragma unroll
+  for (uint32_t k = 0; k < 8u; k += 2u) {
+    if (off + k < nbytes) x[k >> 2] |= (uint32_t)(*reinterpret_cast<const uint16_t*>(p + off + k)) << ((k & 2u) * 8u);
   }
   return x;
 }
 __device__ __forceinline__ void store_unit(uint8_t* p, uint64_t u, uint64_t nbytes, u32x2 x) {
-  uint64_t off = u * 8u;
+  const uint64_t off = u * 8u;
   if (off + 8u <= nbytes) {
     *reinterpret_cast<u32x2*>(p + off) = x;
     return;
   }
-  for (uint64_t i = off; i < nbytes; i += 2u) {
-    uint32_t k = (uint32_t)(i - off);
-    *reinterpret_cast<uint16_t*>(p + i) = (uint16_t)(x[k >> 2] >> ((k & 2u) * 8u));
+#pragma unroll
+  for (uint32_t k = 0; k < 8u; k += 2u) {
+    if (off + k < nbytes) *reinterpret_cast<uint16_t*>(p + off + k) = (uint16_t)(x[k >> 2] >> ((k & 2u) * 8u));
   }
 }
 template <bool kStream = false>
 __device__ __forceinline__ void store_vec(uint8_t* p, uint64_t v, uint64_t nbytes, u32x4 x) {
-  uint64_t off = v * 16u;
+  const uint64_t off = v * 16u;
   if (off + 16u <= nbytes) {
     if constexpr (kStream) __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p + off));
     else *reinterpret_cast<u32x4*>(p + off) = x;
     return;
   }
-  for (uint64_t i = off; i < nbytes; i += 2u) {
-    uint32_t k = (uint32_t)(i - off);
-    *reinterpret_cast<uint16_t*>(p + i) = (uint16_t)(x[k >> 2] >> ((k & 2u) * 8u));
+#pragma unroll
+  for (uint32_t k = 0; k < 16u; k += 2u) {
+    if (off + k < nbytes) *reinterpret_cast<uint16_t*>(p + off + k) = (uint16_t)(x[k >> 2] >> ((k & 2u) * 8u));
   }
 }
 
@@ -166,6 +173,20 @@ __device__ __forceinline__ u32x4 reduce_vec(const u32x4& own, int own_rank, cons
       double x = Elem<kKind>::dec(bits);
       s = (r == 0) ? x : s + x;
     }
+    vec_set<kKind>(out, j, Elem<kKind>::enc(s));
+  }
+  return out;
+}
+
+// The same with every rank's value staged: d[0..N-1] in rank order.
+template <int kKind, int N>
+__device__ __forceinline__ u32x4 reduce_all(const u32x4 (&d)[N]) {
+  u32x4 out = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < Elem<kKind>::kPerVec; ++j) {
+    double s = Elem<kKind>::dec(vec_elem<kKind>(d[0], j));
+#pragma unroll
+    for (int r = 1; r < N; ++r) s += Elem<kKind>::dec(vec_elem<kKind>(d[r], j));
     vec_set<kKind>(out, j, Elem<kKind>::enc(s));
   }
   return out;
@@ -212,61 +233,71 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
   const uint64_t t_entry = wall_ticks();
   int r;
   uint32_t w;
-  decode_role(blockIdx.x, N, a.placement, r, w);
-  const bool idle = (w >= a.slices);
+  decode_role_t<kLocal, N>(blockIdx.x, r, w);
+  // every kernel argument used below, requested at entry as one batch
+  const uint8_t* const src = a.part[r];
+  uint8_t* const out = a.out;
+  uint8_t* const stage = a.stage;
+  Ctrl* const ctrl = a.ctrl;
+  uint64_t* const trace = a.trace;
+  const uint64_t nbytes = a.nbytes, spin_limit = a.spin_limit;
+  const uint32_t slices = a.slices, vq = a.vq, vr = a.vr, stage_bytes = a.stage_bytes;
+  const uint32_t parity_stride = a.parity_stride, rank_stride = a.rank_stride, grid = a.grid;
+  const uint32_t timing = a.timing, keep = a.keep, drop_rank = a.drop_rank, host_epoch = a.host_epoch;
+  LLAR_UNIFORM_AT_ENTRY("s"(src), "s"(out), "s"(stage), "s"(ctrl), "s"(trace), "s"(nbytes), "s"(spin_limit),
+                        "s"(slices), "s"(vq), "s"(vr), "s"(stage_bytes), "s"(parity_stride), "s"(rank_stride),
+                        "s"(grid), "s"(timing), "s"(keep), "s"(drop_rank), "s"(host_epoch));
+  const bool idle = (w >= slices);
   // slice w: 16-byte vectors [v0, v1) for producers, 8-byte units [2 v0, 2 v1)
   // for the consumer (one LL line, or half a Sentinel slot, per lane)
-  const uint64_t v0 = idle ? 0 : (uint64_t)w * a.n_vec / a.slices;
-  const uint64_t v1 = idle ? 0 : (uint64_t)(w + 1) * a.n_vec / a.slices;
-  const bool producer = (r != 0) && !idle && (uint32_t)r != a.drop_rank;
+  const uint32_t v0 = idle ? 0u : w * vq + min(w, vr);
+  const uint32_t v1 = idle ? 0u : v0 + vq + (w < vr ? 1u : 0u);
+  const bool producer = (r != 0) && !idle && (uint32_t)r != drop_rank;
   const bool consumer = (r == 0) && !idle;
   // the first input of this thread is requested before anything else
   u32x4 first_vec = {0u, 0u, 0u, 0u};
   u32x2 first_unit = {0u, 0u};
-  if (producer && v0 + threadIdx.x < v1) first_vec = load_vec<false>(a.part[r], v0 + threadIdx.x, a.nbytes);
-  if (consumer && 2 * v0 + threadIdx.x < 2 * v1) first_unit = load_unit(a.part[0], 2 * v0 + threadIdx.x, a.nbytes);
-  WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
-  if (a.trace && threadIdx.x == 0) a.trace[blockIdx.x * kTraceWords + 0] = t_entry;
-  trace_at(a.trace, 1, false);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.stage, a.stage_bytes);
+  if (producer && v0 + threadIdx.x < v1) first_vec = load_vec<false>(src, v0 + threadIdx.x, nbytes);
+  if (consumer && 2 * v0 + threadIdx.x < 2 * v1) first_unit = load_unit(src, 2 * v0 + threadIdx.x, nbytes);
+  WgState st = wg_begin(ctrl, host_epoch, timing, idle);
+  if (trace && threadIdx.x == 0) trace[blockIdx.x * kTraceWords + 0] = t_entry;
+  trace_at(trace, 1, false);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(stage, stage_bytes);
   const uint32_t e = st.epoch;
-  const uint32_t par_off = (e & 1u) * a.parity_stride;
+  const uint32_t par_off = (e & 1u) * parity_stride;
   constexpr uint32_t kVecStage = (kWire == kWireLL) ? 32u : 16u;
-
   if (producer) {
-    const uint8_t* src = a.part[r];
-    const uint32_t base = par_off + (uint32_t)(r - 1) * a.rank_stride;
-    for (uint64_t v = v0 + threadIdx.x; v < v1; v += blockDim.x) {
-      u32x4 x = (v == v0 + threadIdx.x) ? first_vec : load_vec<false>(src, v, a.nbytes);
-      if (v == v0) trace_at(a.trace, 2, true);
-      uint32_t off = base + (uint32_t)v * kVecStage;
+    const uint32_t base = par_off + (uint32_t)(r - 1) * rank_stride;
+    for (uint32_t v = v0 + threadIdx.x; v < v1; v += blockDim.x) {
+      u32x4 x = (v == v0 + threadIdx.x) ? first_vec : load_vec<false>(src, v, nbytes);
+      if (v == v0) trace_at(trace, 2, true);
+      uint32_t off = base + v * kVecStage;
       if constexpr (kWire == kWireLL) {
         st16_stage<kLocal>(rs, off, u32x4{x[0], e, x[1], e});
         st16_stage<kLocal>(rs, off + 16u, u32x4{x[2], e, x[3], e});
       } else {
         st16_stage<kLocal>(rs, off, sentinel_canon<kKind>(x));
       }
-      if (v == v0) trace_at(a.trace, 3, true);
+      if (v == v0) trace_at(trace, 3, true);
     }
   } else if (consumer) {
-    const uint8_t* own_src = a.part[0];
     constexpr uint32_t kUnitStage = (kWire == kWireLL) ? 16u : 8u;
     bool dead = false;  // set after a timeout: stop waiting for anything else
-    for (uint64_t u = 2 * v0 + threadIdx.x; u < 2 * v1 && !dead; u += blockDim.x) {
-      u32x2 own = (u == 2 * v0 + threadIdx.x) ? first_unit : load_unit(own_src, u, a.nbytes);
-      if (u == 2 * v0) trace_at(a.trace, 2, true);
+    for (uint32_t u = 2 * v0 + threadIdx.x; u < 2 * v1 && !dead; u += blockDim.x) {
+      u32x2 own = (u == 2 * v0 + threadIdx.x) ? first_unit : load_unit(src, u, nbytes);
+      if (u == 2 * v0) trace_at(trace, 2, true);
       // A slot that is ready stays ready for the rest of the call (LL lines
       // carry this call's epoch; a filled Sentinel slot is only reset by this
       // thread), so reload every slot until one pass sees all of them ready
       // and reduce from that pass.
       u32x2 d[N > 1 ? N - 1 : 1];
-      Spin spin(a.spin_limit);
+      Spin spin(spin_limit);
       bool ok = true;
       while (true) {
         bool all = true;
 #pragma unroll
         for (int k = 0; k < N - 1; ++k) {
-          uint32_t off = par_off + (uint32_t)k * a.rank_stride + (uint32_t)u * kUnitStage;
+          uint32_t off = par_off + (uint32_t)k * rank_stride + u * kUnitStage;
           if constexpr (kWire == kWireLL) {
             u32x4 line = ld16_coh(rs, off);
             all &= (line[1] == e) & (line[3] == e);
@@ -278,7 +309,7 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
         }
         if (all) break;
         if (spin.expired()) {
-          raise_status(a.ctrl, kStatusTimeout);
+          raise_status(ctrl, kStatusTimeout);
           ok = false;
           break;
         }
@@ -287,23 +318,22 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
         dead = true;
         continue;
       }
-      if (u == 2 * v0) trace_at(a.trace, 3, false);
-      store_unit(a.out, u, a.nbytes, reduce_unit<kKind, N>(own, d));
-      if (u == 2 * v0) trace_at(a.trace, 4, true);
+      if (u == 2 * v0) trace_at(trace, 3, false);
+      store_unit(out, u, nbytes, reduce_unit<kKind, N>(own, d));
+      if (u == 2 * v0) trace_at(trace, 4, true);
       if constexpr (kWire == kWireSentinel) {
-        if (!a.keep) {
+        if (!keep) {
 #pragma unroll
           for (int k = 0; k < N - 1; ++k)
-            st8_stage<kLocal>(rs, par_off + (uint32_t)k * a.rank_stride + (uint32_t)u * 8u,
-                              u32x2{0xFFFFFFFFu, 0xFFFFFFFFu});
+            st8_stage<kLocal>(rs, par_off + (uint32_t)k * rank_stride + u * 8u, u32x2{0xFFFFFFFFu, 0xFFFFFFFFu});
         }
       }
     }
   }
-  wg_end(a.ctrl, st, a.host_epoch, a.grid, a.timing, idle);
-  if (a.trace && threadIdx.x == 0) {
-    a.trace[blockIdx.x * kTraceWords + 5] = wall_ticks();
-    a.trace[blockIdx.x * kTraceWords + 6] = (uint64_t)xcc_id() | ((uint64_t)r << 8) | ((uint64_t)w << 16);
+  wg_end(ctrl, st, host_epoch, grid, timing, idle);
+  if (trace && threadIdx.x == 0) {
+    trace[blockIdx.x * kTraceWords + 5] = wall_ticks();
+    trace[blockIdx.x * kTraceWords + 6] = (uint64_t)xcc_id() | ((uint64_t)r << 8) | ((uint64_t)w << 16);
   }
 }
 
@@ -333,9 +363,21 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
 // receives the credit.
 template <int kKind, int kAcc16, int N>
 __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
-  int r;
-  uint32_t w;
-  decode_role(blockIdx.x, N, a.placement, r, w);
+  // every kernel argument, requested at entry as one batch: the partial of
+  // this workgroup's rank under both placements, the placement picks one
+  int r_l, r_s;
+  uint32_t w_l, w_s;
+  decode_role_t<true, N>(blockIdx.x, r_l, w_l);
+  decode_role_t<false, N>(blockIdx.x, r_s, w_s);
+  const uint8_t* const src_l = a.part[r_l];
+  const uint8_t* const src_s = a.part[r_s];
+  LLAR_UNIFORM_AT_ENTRY("s"(src_l), "s"(src_s), "s"(a.out), "s"(a.stage), "s"(a.ctrl), "s"(a.n), "s"(a.spin_limit),
+                        "s"(a.chunk_elems), "s"(a.n_chunks), "s"(a.stage_bytes), "s"(a.parity_stride), "s"(a.grid),
+                        "s"(a.slices), "s"(a.placement), "s"(a.timing), "s"(a.keep), "s"(a.drop_rank),
+                        "s"(a.host_epoch));
+  const bool local = (a.placement == kPlaceLocal);
+  const int r = local ? r_l : r_s;
+  const uint32_t w = local ? w_l : w_s;
   const bool idle = (w >= a.slices);
   WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
   using E = Elem<kKind>;
@@ -343,7 +385,7 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
   constexpr int K = kSlots - 1;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.stage, a.stage_bytes);
   const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
-  const uint8_t* src = a.part[r];
+  const uint8_t* src = local ? src_l : src_s;
   // flag value N in the staging type
   uint32_t flag_full;
   if constexpr (!kAcc16) flag_full = __float_as_uint((float)N);
@@ -518,7 +560,13 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   constexpr int kUc = 2;  // vectors per consumer lane per batch
   int r;
   uint32_t w;
-  decode_role(blockIdx.x, N, a.placement, r, w);
+  decode_role_t<kLocal, N>(blockIdx.x, r, w);
+  // every kernel argument, requested at entry as one batch
+  const uint8_t* src = a.part[r];
+  LLAR_UNIFORM_AT_ENTRY("s"(src), "s"(a.out), "s"(a.stage), "s"(a.ctrl), "s"(a.n), "s"(a.spin_limit),
+                        "s"(a.chunk_elems), "s"(a.n_chunks), "s"(a.stage_bytes), "s"(a.parity_stride),
+                        "s"(a.shard_cap), "s"(a.n_buffers), "s"(a.grid), "s"(a.slices), "s"(a.timing), "s"(a.keep),
+                        "s"(a.drop_rank), "s"(a.host_epoch), "s"(a.trace));
   const bool idle = (w >= a.slices);
   WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
   using E = Elem<kKind>;
@@ -526,7 +574,6 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   if (threadIdx.x < 8) s_done[threadIdx.x] = 0u;
   __syncthreads();
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.stage, a.stage_bytes);
-  const uint8_t* src = a.part[r];
   const uint64_t nbytes = a.n * (uint64_t)E::kBytes;
   const uint32_t chunk_vecs = (uint32_t)(((uint64_t)a.chunk_elems * E::kBytes + 15u) / 16u);
   const uint64_t total_vecs = (nbytes + 15u) / 16u;
@@ -693,6 +740,263 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// two-shot Sentinel, chunked, slot handshake (the reset is the credit)
+// ---------------------------------------------------------------------------
+// Staging: [buffer][owner s][sender r][vector of s's shard] 16 B, all-ones
+// when empty; chunk c uses buffer c % B.  The partition into owner shards
+// and slices uses the nominal chunk, so a slot keeps its (owner, slice) in
+// every chunk.  Every rank stages its whole slice, its own shard included,
+// so consumers never load HBM (a wave's vector memory operations retire in
+// order: one HBM load queued before a poll would delay the poll's answer by
+// an HBM latency).
+// Every slot has one producer lane and one consumer lane, the same in every
+// chunk, and alternates empty -> full (data, never all-ones) -> empty:
+//   producer lane: stores chunk c's vector into the slot only after reading
+//            the slot as empty -- the owner's consumer has taken chunk c - B
+//            out of it and reset it (for c < B: unused in this call);
+//   consumer lane: polls the N slots of its vector until all are full, adds
+//            them in binary64 in rank order, rounds, writes `out` and resets
+//            the slots to empty.
+// The reset the producer reads is the owner's permission to send the next
+// piece through that slot (a per-slot credit): no workgroup waits for a
+// whole chunk, and no store is drained before a credit.  Only the slot's own
+// producer can fill an empty slot, so a producer may read the slot state as
+// early as it likes -- it does so together with the input loads of the work
+// item, one item ahead.  A lane's own store to a slot is ordered before its
+// own later load of that slot (same lane, same address), so a producer never
+// mistakes the empty state it has overwritten for a fresh reset, and a
+// consumer never reads data it has consumed.
+// Producers keep one work item in flight per wave and rely on the number of
+// producer waves (three quarters of a 1024-thread workgroup) for memory
+// parallelism.
+// The hot loops contain no branch around a memory operation: lanes without
+// a vector use an offset past the end of the buffer (loads return zero,
+// stores are dropped), and the one partial vector at the end of a message
+// is moved after the loops.  The compiler can then wait for exactly the
+// operations each step needs instead of draining every outstanding load.
+template <int kKind, int N, bool kLocal>
+__global__ void __launch_bounds__(1024) k_twoshot_sentinel_hs(TwoShotArgs a) {
+  constexpr uint32_t kOff = 0x80000000u;  // an offset past every buffer
+  int r;
+  uint32_t w;
+  decode_role_t<kLocal, N>(blockIdx.x, r, w);
+  // every kernel argument, requested at entry as one batch
+  const uint8_t* src = a.part[r];
+  LLAR_UNIFORM_AT_ENTRY("s"(src), "s"(a.out), "s"(a.stage), "s"(a.ctrl), "s"(a.n), "s"(a.spin_limit),
+                        "s"(a.chunk_elems), "s"(a.n_chunks), "s"(a.stage_bytes), "s"(a.parity_stride),
+                        "s"(a.shard_cap), "s"(a.n_buffers), "s"(a.grid), "s"(a.slices), "s"(a.timing), "s"(a.keep),
+                        "s"(a.drop_rank), "s"(a.host_epoch), "s"(a.cons_waves));
+  const bool idle = (w >= a.slices);
+  WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
+  using E = Elem<kKind>;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.stage, a.stage_bytes);
+  const uint64_t nbytes = a.n * (uint64_t)E::kBytes;
+  const uint32_t chunk_vecs = (uint32_t)(((uint64_t)a.chunk_elems * E::kBytes) / 16u);  // chunks are whole vectors
+  const uint64_t full_vecs = nbytes / 16u;          // whole vectors of the message
+  const bool has_tail = (nbytes % 16u) != 0u;       // vector full_vecs is partial
+  const uint64_t total_vecs = full_vecs + (has_tail ? 1u : 0u);
+  const uint32_t slot_bytes = a.shard_cap * 16u;
+  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
+  // the host splits the waves: n_cons consume (staging reads only), the
+  // rest produce
+  const uint32_t n_cons = a.cons_waves, n_prod = n_waves - n_cons;
+  const uint32_t n_buf = a.n_buffers;
+  const uint32_t nv = chunk_vecs;
+  const uint32_t reset_off = a.keep ? kOff : 0u;  // tests: keep the staged data
+  const u32x4 kEmpty = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  // owner s's shard of a chunk is [o0, o1) = [s*nv/N, (s+1)*nv/N); slice w
+  // of it is the span-long piece starting at w*span, clamped to the shard
+  // (the last slices may be short or empty: this protocol's credit is per
+  // slot, nothing waits for a slice)
+  const uint32_t span = ((nv + N - 1u) / N + a.slices - 1u) / a.slices;
+  auto shard = [&](uint32_t s, uint32_t& o0, uint32_t& s0, uint32_t& s1) {
+    o0 = s * nv / (uint32_t)N;
+    const uint32_t o1 = (s + 1u) * nv / (uint32_t)N;
+    s0 = min(o0 + w * span, o1);
+    s1 = min(s0 + span, o1);
+  };
+  bool dead = idle;
+
+  // Consumer work items are (chunk c, 64-vector batch b of the slice);
+  // producer items split each of those into kH groups of kG owners.  A wave
+  // takes every n-th item of its role, so different waves work on different
+  // chunks at once and a slice that is short per chunk still keeps many
+  // waves busy.
+  constexpr int kG = (N + 1) / 2, kH = (N + kG - 1) / kG;
+  const uint32_t n_bat = (span + 63u) / 64u;
+  const uint32_t n_items = dead ? 0u : a.n_chunks * n_bat;  // consumer items
+  if (wave < n_prod) {
+    // ---------------- producer waves: rank r's slice (s, w) of every owner s
+    const bool silent = ((uint32_t)r == a.drop_rank);
+    const uint32_t n_pitems = (dead || silent) ? 0u : n_items * kH;
+    struct Set {
+      u32x4 x[kG];       // input vectors
+      u32x4 chk[kG];     // slot state read when the inputs were requested
+      uint32_t off[kG];  // slot offsets, or kOff
+    };
+    auto issue = [&](uint32_t pitem, Set& S) {
+      const uint32_t item = pitem / kH, h = pitem % kH;
+      const uint32_t c = item / n_bat, b0 = (item % n_bat) * 64u;
+      // this chunk's whole vectors of the partial as a buffer view, so a
+      // lane past the end reads zero without a branch
+      const uint64_t cb = (uint64_t)c * nv * 16u;
+      const uint64_t avail = full_vecs * 16u > cb ? full_vecs * 16u - cb : 0u;
+      const uint32_t nfull = (uint32_t)min(avail, (uint64_t)nv * 16u);
+      const __amdgpu_buffer_rsrc_t rin = make_rsrc(src + cb, nfull);
+      const uint32_t boff = (c % n_buf) * a.parity_stride + (uint32_t)r * slot_bytes;
+      uint32_t vin[kG];
+#pragma unroll
+      for (int g = 0; g < kG; ++g) {
+        const uint32_t s = h * kG + (uint32_t)g;
+        uint32_t o0, s0, s1;
+        shard(min(s, (uint32_t)N - 1u), o0, s0, s1);
+        const uint32_t v = s0 + b0 + lane;
+        const bool ok = (s < (uint32_t)N) && (v < s1) && (v * 16u < nfull);
+        S.off[g] = ok ? boff + (s * N) * slot_bytes + (v - o0) * 16u : kOff;
+        vin[g] = ok ? v * 16u : kOff;
+      }
+#pragma unroll
+      for (int g = 0; g < kG; ++g) S.chk[g] = ld16_coh(rs, S.off[g]);
+#pragma unroll
+      for (int g = 0; g < kG; ++g) S.x[g] = __builtin_amdgcn_raw_buffer_load_b128(rin, vin[g], 0, kCpolNt);
+      // keep these loads here: the compiler would otherwise sink them to
+      // their first use and only one item would be in flight
+      asm volatile("" ::: "memory");
+    };
+    auto commit = [&](const Set& S) -> bool {
+      uint32_t need = 0u;
+#pragma unroll
+      for (int g = 0; g < kG; ++g)
+        if (S.off[g] != kOff && !sentinel_is_empty(S.chk[g])) need |= 1u << g;
+      if (need != 0u) {
+        // a slot still held chunk c - B when it was read: read it again
+        SpinBulk spin(a.spin_limit);
+        while (need != 0u) {
+          if (spin.expired()) {
+            raise_status(a.ctrl, kStatusTimeout);
+            return false;
+          }
+#pragma unroll
+          for (int g = 0; g < kG; ++g)
+            if ((need >> g) & 1u)
+              if (sentinel_is_empty(ld16_coh(rs, S.off[g]))) need &= ~(1u << g);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < kG; ++g) st16_stage<kLocal>(rs, S.off[g], sentinel_canon<kKind>(S.x[g]));
+      return true;
+    };
+    // two items in flight per wave: the next item's loads are issued before
+    // this item is stored, so waiting for them never waits for stores
+    Set A, B;
+    uint32_t item = wave;
+    if (item < n_pitems) issue(item, A);
+    for (; item < n_pitems; item += 2u * n_prod) {
+      if (item + n_prod < n_pitems) issue(item + n_prod, B);
+      if (!commit(A)) {
+        dead = true;
+        break;
+      }
+      if (item + n_prod >= n_pitems) break;
+      if (item + 2u * n_prod < n_pitems) issue(item + 2u * n_prod, A);
+      if (!commit(B)) {
+        dead = true;
+        break;
+      }
+    }
+    // the partial last vector, by the lane that owns its position
+    if (has_tail && !dead && !silent) {
+      const uint32_t c = (uint32_t)(full_vecs / nv), v = (uint32_t)(full_vecs % nv);
+      for (uint32_t s = 0; s < (uint32_t)N; ++s) {
+        uint32_t o0, s0, s1;
+        shard(s, o0, s0, s1);
+        if (v < s0 || v >= s1) continue;
+        const uint32_t pitem = (c * n_bat + (v - s0) / 64u) * kH + s / kG;
+        if (pitem % n_prod != wave || (v - s0) % 64u != lane) continue;
+        const u32x4 x = load_vec<false>(src, full_vecs, nbytes);
+        const uint32_t off = (c % n_buf) * a.parity_stride + (uint32_t)(s * N + r) * slot_bytes + (v - o0) * 16u;
+        SpinBulk spin(a.spin_limit);
+        while (!sentinel_is_empty(ld16_coh(rs, off))) {
+          if (spin.expired()) {
+            raise_status(a.ctrl, kStatusTimeout);
+            break;
+          }
+        }
+        st16_stage<kLocal>(rs, off, sentinel_canon<kKind>(x));
+      }
+    }
+  } else {
+    // ---------------- consumer waves: owner r's slice w, staging only
+    const uint32_t cw = wave - n_prod;
+    uint32_t o0, s0, s1n;
+    shard((uint32_t)r, o0, s0, s1n);
+    for (uint32_t item = cw; item < n_items && !dead; item += n_cons) {
+      const uint32_t c = item / n_bat, b0 = (item % n_bat) * 64u;
+      const uint64_t vbase = (uint64_t)c * nv;
+      // whole vectors of this chunk in the slice; the partial one comes last
+      const uint32_t fr = (uint32_t)min((uint64_t)nv, full_vecs > vbase ? full_vecs - vbase : 0u);
+      const uint32_t s1 = min(s1n, max(fr, s0));
+      if (s0 + b0 >= s1) continue;  // nothing of this item here (wave-uniform)
+      const uint32_t my = (c % n_buf) * a.parity_stride + (uint32_t)(r * N) * slot_bytes;
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out + vbase * 16u, (uint32_t)((uint64_t)fr * 16u));
+      const uint32_t v = s0 + b0 + lane;
+      const uint32_t so = v < s1 ? my + (v - o0) * 16u : kOff;  // sender 0's slot, or kOff
+      const uint32_t oo = v < s1 ? v * 16u : kOff;
+      u32x4 d[N];
+      SpinBulk spin(a.spin_limit);
+      while (true) {
+        bool all = true;
+#pragma unroll
+        for (int s = 0; s < N; ++s) {
+          d[s] = ld16_coh(rs, so == kOff ? kOff : so + (uint32_t)s * slot_bytes);
+          all &= (so == kOff) | sentinel_ready<kKind>(d[s]);
+        }
+        if (__all((int)all)) break;
+        if (spin.expired()) {
+          raise_status(a.ctrl, kStatusTimeout);
+          dead = true;
+          break;
+        }
+      }
+      if (dead) break;
+      __builtin_amdgcn_raw_buffer_store_b128(reduce_all<kKind, N>(d), ro, oo, 0, kCpolNone);
+#pragma unroll
+      for (int s = 0; s < N; ++s)
+        st16_stage<kLocal>(rs, so == kOff ? kOff : so + (uint32_t)s * slot_bytes + reset_off, kEmpty);
+    }
+    // the partial last vector, by the lane that owns its position
+    if (has_tail && !dead) {
+      const uint32_t c = (uint32_t)(full_vecs / nv), v = (uint32_t)(full_vecs % nv);
+      if (v >= s0 && v < s1n && (c * n_bat + (v - s0) / 64u) % n_cons == cw && (v - s0) % 64u == lane) {
+        const uint32_t base = (c % n_buf) * a.parity_stride + (uint32_t)(r * N) * slot_bytes + (v - o0) * 16u;
+        u32x4 d[N];
+        SpinBulk spin(a.spin_limit);
+        while (true) {
+          bool all = true;
+#pragma unroll
+          for (int s = 0; s < N; ++s) {
+            d[s] = ld16_coh(rs, base + (uint32_t)s * slot_bytes);
+            all &= sentinel_ready<kKind>(d[s]);
+          }
+          if (all) break;
+          if (spin.expired()) {
+            raise_status(a.ctrl, kStatusTimeout);
+            dead = true;
+            break;
+          }
+        }
+        if (!dead) {
+          store_vec(a.out, full_vecs, nbytes, reduce_all<kKind, N>(d));
+#pragma unroll
+          for (int s = 0; s < N; ++s) st16_stage<kLocal>(rs, base + (uint32_t)s * slot_bytes + reset_off, kEmpty);
+        }
+      }
+    }
+  }
+  wg_end(a.ctrl, st, a.host_epoch, a.grid, a.timing, idle);
+}
+
+// ---------------------------------------------------------------------------
 // launchers (host side, one instantiation per (dtype, N))
 // ---------------------------------------------------------------------------
 template <int kKind, int N>
@@ -726,6 +1030,12 @@ static hipError_t launch_n(const LaunchSpec& ls, hipStream_t stream) {
       break;
     case kKernSentinelPipeLocal:
       hipLaunchKernelGGL((k_twoshot_sentinel<kKind, N, true>), grid, block, 0, stream, ls.twoshot);
+      break;
+    case kKernSentinelHs:
+      hipLaunchKernelGGL((k_twoshot_sentinel_hs<kKind, N, false>), grid, block, 0, stream, ls.twoshot);
+      break;
+    case kKernSentinelHsLocal:
+      hipLaunchKernelGGL((k_twoshot_sentinel_hs<kKind, N, true>), grid, block, 0, stream, ls.twoshot);
       break;
     default:
       return hipErrorInvalidValue;
@@ -773,6 +1083,8 @@ static int occupancy_n(int kernel, int threads) {
       break;
     case kKernSentinelPipe: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_sentinel<kKind, N, false>, threads, 0); break;
     case kKernSentinelPipeLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_sentinel<kKind, N, true>, threads, 0); break;
+    case kKernSentinelHs: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_sentinel_hs<kKind, N, false>, threads, 0); break;
+    case kKernSentinelHsLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_sentinel_hs<kKind, N, true>, threads, 0); break;
     default: break;
   }
   return err == hipSuccess ? blocks : 0;

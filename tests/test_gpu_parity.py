@@ -384,6 +384,73 @@ def test_pipelined_slices_are_clamped_to_non_empty_owner_slices(proto):
             check(got, oracle.allreduce(bits, dt), dt, proto, "rep %d" % rep)
 
 
+# --------------------------------------------------------------------------- slot handshake (sentinel_credit = 1)
+@pytest.mark.parametrize("placement", [1, 2])
+@pytest.mark.parametrize("chunk,threads,cons", [(1024, 0, 0), (4096, 512, 2), (65536, 0, 0), (1 << 20, 256, 1),
+                                                (262144, 1024, 8)])
+def test_sentinel_handshake_exact(placement, chunk, threads, cons):
+    """The pipelined Sentinel whose credit is the slot reset itself: exact
+    for every chunk size, wave split and placement, a ragged tail vector,
+    fresh inputs on every call, and every slot empty again afterwards."""
+    dt = BF16
+    n = (3 << 20) // 2 + 37  # 3 MiB + 74 bytes: the last vector is partial
+    with comm_for(8, dt, n * 2, sentinel_credit=1, chunk_bytes=chunk, threads=threads, consumer_waves=cons,
+                  placement=placement) as c:
+        for rep in range(2):
+            bits = make_partials(1800 + placement, chunk + rep, 8, "bf16", n, "normal", 1.0)
+            got = run(c, bits, "sentinel_pipelined", dt)
+            assert_exact(got, oracle.allreduce(bits, dt), dt, "chunk %d rep %d" % (chunk, rep))
+        assert (c.staging(llar.SENTINEL_PIPELINED) == 0xFF).all()
+
+
+@pytest.mark.parametrize("n_ranks", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_sentinel_handshake_every_rank_count(n_ranks):
+    dt = BF16
+    n = 5001
+    with comm_for(n_ranks, dt, n * 2, sentinel_credit=1, chunk_bytes=2048) as c:
+        for rep in range(3):
+            bits = make_partials(1900 + n_ranks, rep, n_ranks, "bf16", n, "normal", 0.5)
+            got = run(c, bits, "sentinel_pipelined", dt)
+            assert_exact(got, oracle.allreduce(bits, dt), dt, "N=%d rep %d" % (n_ranks, rep))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_sentinel_handshake_ragged_sizes_and_slices(dtype):
+    """Sizes around every vector and chunk boundary, and slice counts that
+    give one, several or a fraction of a 64-vector batch per chunk (the
+    buffer count then changes with the wave period)."""
+    dt = CODE[dtype]
+    n_ranks = 8 if dtype != "fp32" else 5
+    sizes = [1, 7, 9, 63, 65, 1000, 4097, 20001, 70001]
+    with comm_for(n_ranks, dt, 70001 * 4, sentinel_credit=1, chunk_bytes=8192) as c:
+        for slices in (1, 3, 7, 32):
+            c.set_option("slices", slices)
+            for i, n in enumerate(sizes):
+                bits = make_partials(2000 + dt, slices * 100 + i, n_ranks, dtype, n, "normal", 1.0)
+                got = run(c, bits, "sentinel_pipelined", dt)
+                assert_exact(got, oracle.allreduce(bits, dt), dt, "slices %d n=%d" % (slices, n))
+
+
+def test_sentinel_handshake_lost_contribution_times_out_and_recovers():
+    dt = BF16
+    n = 40000
+    bits = make_partials(2100, 0, 4, "bf16", n, "normal", 1.0)
+    with comm_for(4, dt, n * 2, sentinel_credit=1, chunk_bytes=4096) as c:
+        c.set_option("spin_timeout_us", 2000)
+        c.set_option("debug_drop_rank", 1)
+        parts = [to_device(bits[r], dt) for r in range(4)]
+        out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        c.allreduce(parts, out, "sentinel_pipelined")
+        torch.cuda.synchronize()
+        st, status_bits = c.device_status()
+        assert st == -5 and (status_bits & 1), (st, status_bits)
+        c.clear_device_status()
+        c.set_option("debug_drop_rank", -1)
+        c.set_option("spin_timeout_us", 100_000)
+        got = run(c, bits, "sentinel_pipelined", dt)
+        assert_exact(got, oracle.allreduce(bits, dt), dt, "after recovery")
+
+
 @pytest.mark.parametrize("threads", [64, 128, 256, 512])
 @pytest.mark.parametrize("proto", ALL_PROTOCOLS)
 def test_workgroup_sizes(proto, threads):
