@@ -959,7 +959,7 @@ __global__ void __launch_bounds__(1024) k_twoshot_sentinel_hs(TwoShotArgs a) {
         }
       }
       if (dead) break;
-      __builtin_amdgcn_raw_buffer_store_b128(reduce_all<kKind, N>(d), ro, oo, 0, kCpolNone);
+      __builtin_amdgcn_raw_buffer_store_b128(reduce_all<kKind, N>(d), ro, oo, 0, kCpolNt);
 #pragma unroll
       for (int s = 0; s < N; ++s)
         st16_stage<kLocal>(rs, so == kOff ? kOff : so + (uint32_t)s * slot_bytes + reset_off, kEmpty);
