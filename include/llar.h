@@ -98,6 +98,31 @@ llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes);
 int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t n_elems,
                    llar_dtype dtype, llar_protocol protocol, void* stream);
 
+/* Point-to-point copy: recv_buf[i] = send_buf[i] for i < n_elems, moved by
+ * one sending rank to one receiving rank through the LL or Sentinel staging
+ * of this communicator -- the stage-to-stage activation transfer of pipeline
+ * parallelism (the pwwt.cn small-message latency article, section 1.1, the
+ * PP item, and section 3.3: a 4096 x FP16 hidden state, 8 KB per token).
+ * The same one-shot exchange as llar_allreduce with a single producer, and
+ * the receiver writes what arrived instead of a sum.
+ *
+ * send_buf, recv_buf: device pointers to n_elems elements, 16-byte aligned,
+ *   not overlapping.  dtype must equal the create-time dtype and
+ *   n_elems * sizeof(dtype) <= max_bytes.  n_elems == 0 is a no-op.
+ * protocol: LLAR_LL, LLAR_SENTINEL or LLAR_AUTO (LL up to the
+ *   "thr_sentinel" size, else Sentinel); any other value is LLAR_ERR_ARG.
+ *   Messages above 8 MiB (LL) or 16 MiB (Sentinel) return
+ *   LLAR_ERR_UNSUPPORTED.
+ * Result: LL delivers every bit pattern unchanged.  The Sentinel cannot carry
+ *   its own all-ones pattern: the sender replaces it by the pattern one below
+ *   (still a negative NaN of the same payload class), exactly as the
+ *   AllReduce's Sentinel producer does; every other pattern arrives
+ *   unchanged.
+ * Errors, epochs and stream rules are those of llar_allreduce; the call
+ *   shares the communicator's staging and epoch with it. */
+int llar_send_recv(llar_comm* h, const void* send_buf, void* recv_buf, size_t n_elems,
+                   llar_dtype dtype, llar_protocol protocol, void* stream);
+
 /* Free all resources (synchronises the device first).  NULL is a no-op. */
 int llar_destroy(llar_comm* h);
 
@@ -134,8 +159,6 @@ int llar_clear_device_status(llar_comm* h);
  *   "debug_drop_rank"  tests: the producers of this rank write nothing, so consumers time out (-1 = none)
  *   "trace"            1 = one-shot kernels record per-workgroup phase stamps (see llar_get_trace),
  *                      the pipelined Sentinel per-chunk stamps (see llar_get_pipeline_trace)
- *   "pipeline_buffers" staging buffers of the pipelined Sentinel: 2, 4 (default), 6 or 8; with B
- *                      buffers a producer runs up to B/2 - 1 chunks ahead of its consumer
  *   "device_epoch"     1 = always read the device-resident epoch; otherwise the host numbers
  *                      stream-ordered calls and the device epoch is used only on a stream that is
  *                      being captured into a graph (replays then never reuse an epoch)

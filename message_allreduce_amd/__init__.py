@@ -11,6 +11,7 @@ Python names mirror the C ABI::
 
     h = llar_create(n_ranks, dtype, max_bytes)
     llar_allreduce(h, partials, out, n_elems, dtype, protocol, stream)
+    llar_send_recv(h, send, recv, n_elems, dtype, protocol, stream)
     llar_destroy(h)
 
 and ``Communicator`` wraps them for torch tensors.
@@ -23,7 +24,7 @@ import os
 __all__ = [
     "FP32", "FP16", "BF16", "AUTO", "LL", "SENTINEL", "LL128", "LL128_PIPELINED", "SENTINEL_PIPELINED",
     "PROTOCOLS", "LlarError", "lib", "library_path", "llar_create", "llar_allreduce", "llar_destroy",
-    "llar_set_option", "llar_get_option", "llar_get_device_status", "llar_clear_device_status",
+    "llar_send_recv", "llar_set_option", "llar_get_option", "llar_get_device_status", "llar_clear_device_status",
     "llar_select_protocol", "llar_debug_copy_staging", "llar_staging_bytes", "llar_get_epoch",
     "llar_get_timing", "llar_wallclock_hz", "llar_launch_geometry", "llar_floor_measure",
     "llar_status_string", "llar_last_error", "llar_get_trace", "llar_get_pipeline_trace", "Communicator", "EXPORTED_SYMBOLS",
@@ -42,7 +43,7 @@ EXPORTED_SYMBOLS = (
     "llar_get_device_status", "llar_clear_device_status", "llar_set_option", "llar_get_option",
     "llar_select_protocol", "llar_debug_copy_staging", "llar_staging_bytes", "llar_get_epoch",
     "llar_get_timing", "llar_wallclock_hz", "llar_launch_geometry", "llar_floor_measure",
-    "llar_get_trace", "llar_get_pipeline_trace",
+    "llar_get_trace", "llar_get_pipeline_trace", "llar_send_recv",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,6 +71,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "llar_create": (vp, [i32, i32, sz]),
         "llar_allreduce": (i32, [vp, ctypes.POINTER(vp), vp, sz, i32, i32, vp]),
+        "llar_send_recv": (i32, [vp, vp, vp, sz, i32, i32, vp]),
         "llar_destroy": (i32, [vp]),
         "llar_last_error": (i32, []),
         "llar_status_string": (ctypes.c_char_p, [i32]),
@@ -115,6 +117,12 @@ def llar_allreduce(h: int, partials, out: int, n_elems: int, dtype: int, protoco
     arr = (ctypes.c_void_p * len(partials))(*[int(p) for p in partials])
     return lib().llar_allreduce(h, arr, ctypes.c_void_p(int(out)), int(n_elems), int(dtype), int(protocol),
                                 ctypes.c_void_p(int(stream)))
+
+
+def llar_send_recv(h: int, send: int, recv: int, n_elems: int, dtype: int, protocol: int, stream: int) -> int:
+    """send, recv: device pointers (ints)."""
+    return lib().llar_send_recv(h, ctypes.c_void_p(int(send)), ctypes.c_void_p(int(recv)), int(n_elems), int(dtype),
+                                int(protocol), ctypes.c_void_p(int(stream)))
 
 
 def llar_destroy(h: int) -> int:
@@ -244,6 +252,22 @@ class Communicator:
         s = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
         st = llar_allreduce(self.h, [p.data_ptr() for p in partials], out.data_ptr(), n, self.dtype, protocol, s)
         return _check(st, "llar_allreduce")
+
+    def send_recv(self, send, recv, protocol=AUTO, stream=None):
+        """Copy ``send`` into ``recv`` (``recv.numel()`` elements) from one
+        sending rank to one receiving rank over the LL or Sentinel wire."""
+        import torch
+        if isinstance(protocol, str):
+            protocol = PROTOCOLS[protocol]
+        n = recv.numel()
+        for t, what in ((send, "send"), (recv, "recv")):
+            if not (t.is_cuda and t.is_contiguous() and _dtype_code(t) == self.dtype):
+                raise ValueError("%s must be a contiguous device tensor of the communicator's dtype" % what)
+        if send.numel() < n:
+            raise ValueError("send holds fewer elements than recv")
+        s = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+        st = llar_send_recv(self.h, send.data_ptr(), recv.data_ptr(), n, self.dtype, protocol, s)
+        return _check(st, "llar_send_recv")
 
     def prepare(self, partials, out, protocol=AUTO, stream=None):
         """Validate and marshal the arguments once; return a no-argument

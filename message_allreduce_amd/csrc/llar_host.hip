@@ -443,34 +443,26 @@ int llar_launch_geometry(llar_comm* h, size_t n_elems, llar_protocol protocol, i
   return LLAR_OK;
 }
 
-int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t n_elems, llar_dtype dtype,
-                   llar_protocol protocol, void* stream) {
-  if (!h || !partials) return fail(LLAR_ERR_ARG);
-  if ((int)dtype != h->kind) return fail(LLAR_ERR_ARG);
-  if (n_elems == 0) return LLAR_OK;
-  if (!out || !aligned16(out)) return fail(LLAR_ERR_ARG);
-  if (n_elems > h->max_bytes / h->elem) return fail(LLAR_ERR_ARG);
-  for (int r = 0; r < h->n_ranks; ++r)
-    if (!partials[r] || !aligned16(partials[r])) return fail(LLAR_ERR_ARG);
-  if ((int)protocol < 0 || (int)protocol > LLAR_SENTINEL_PIPELINED) return fail(LLAR_ERR_ARG);
+namespace {
 
+// Issue one call of the planned kernel.  `n_launch` ranks take part (the
+// communicator's rank count, or two for a point-to-point copy); `parts`
+// holds their input pointers.
+int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_t n_elems, int proto,
+          const Geometry& g, hipStream_t stream) {
   const size_t nbytes = n_elems * h->elem;
-  const int proto = protocol == LLAR_AUTO ? auto_protocol(h, nbytes) : (int)protocol;
-  Geometry g;
-  int st = plan(h, n_elems, proto, g);
-  if (st != LLAR_OK) return fail(st);
   const Region* reg = region_of(h, proto);
 
   LaunchSpec ls;
   memset(&ls, 0, sizeof(ls));
   ls.kind = h->kind;
-  ls.n_ranks = h->n_ranks;
+  ls.n_ranks = n_launch;
   ls.kernel = g.kernel;
   ls.threads = g.threads;
-  ls.grid = h->n_ranks * g.grid_slices;
+  ls.grid = n_launch * g.grid_slices;
 
   // every workgroup must be resident at once: consumers spin on producers
-  int occ = occupancy(h->kind, h->n_ranks, g.kernel, g.threads);
+  int occ = occupancy(h->kind, n_launch, g.kernel, g.threads);
   if (occ <= 0) return fail(LLAR_ERR_HIP);
   if (ls.grid > occ * h->cu_count) return fail(LLAR_ERR_UNSUPPORTED);
   if (h->timing && ls.grid > kTimingMaxWgs) return fail(LLAR_ERR_UNSUPPORTED);
@@ -479,14 +471,16 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
   // epoch source: the host numbers stream-ordered calls; a captured call
   // must read the device-resident epoch (its arguments repeat on replay)
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) != hipSuccess) return fail(LLAR_ERR_HIP);
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return fail(LLAR_ERR_HIP);
   const bool device_epoch = h->device_epoch || cap != hipStreamCaptureStatusNone;
   const uint32_t host_epoch = device_epoch ? 0u : h->host_epoch;
   const bool is_oneshot = g.kernel == kKernOneShotLL || g.kernel == kKernOneShotSentinel ||
-                          g.kernel == kKernOneShotLLLocal || g.kernel == kKernOneShotSentinelLocal;
+                          g.kernel == kKernOneShotLLLocal || g.kernel == kKernOneShotSentinelLocal ||
+                          g.kernel == kKernP2PLL || g.kernel == kKernP2PSentinel || g.kernel == kKernP2PLLLocal ||
+                          g.kernel == kKernP2PSentinelLocal;
   if (is_oneshot) {
     OneShotArgs& a = ls.oneshot;
-    for (int r = 0; r < h->n_ranks; ++r) a.part[r] = static_cast<const uint8_t*>(partials[r]);
+    for (int r = 0; r < n_launch; ++r) a.part[r] = static_cast<const uint8_t*>(parts[r]);
     a.out = static_cast<uint8_t*>(out);
     a.stage = reg->ptr;
     a.ctrl = h->ctrl;
@@ -509,7 +503,7 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
     a.host_epoch = host_epoch;
   } else {
     TwoShotArgs& a = ls.twoshot;
-    for (int r = 0; r < h->n_ranks; ++r) a.part[r] = static_cast<const uint8_t*>(partials[r]);
+    for (int r = 0; r < n_launch; ++r) a.part[r] = static_cast<const uint8_t*>(parts[r]);
     a.out = static_cast<uint8_t*>(out);
     a.stage = reg->ptr;
     a.ctrl = h->ctrl;
@@ -576,11 +570,59 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
     }
   }
   if (!reg->ptr) return fail(LLAR_ERR_UNSUPPORTED);
-  hipError_t e = launch(ls, static_cast<hipStream_t>(stream));
+  hipError_t e = launch(ls, stream);
   if (e != hipSuccess) return fail(LLAR_ERR_HIP);
   h->last_call_device = device_epoch;
   if (!device_epoch) h->host_epoch = next_host_epoch(h->host_epoch);
   return LLAR_OK;
+}
+
+}  // namespace
+
+int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t n_elems, llar_dtype dtype,
+                   llar_protocol protocol, void* stream) {
+  if (!h || !partials) return fail(LLAR_ERR_ARG);
+  if ((int)dtype != h->kind) return fail(LLAR_ERR_ARG);
+  if (n_elems == 0) return LLAR_OK;
+  if (!out || !aligned16(out)) return fail(LLAR_ERR_ARG);
+  if (n_elems > h->max_bytes / h->elem) return fail(LLAR_ERR_ARG);
+  for (int r = 0; r < h->n_ranks; ++r)
+    if (!partials[r] || !aligned16(partials[r])) return fail(LLAR_ERR_ARG);
+  if ((int)protocol < 0 || (int)protocol > LLAR_SENTINEL_PIPELINED) return fail(LLAR_ERR_ARG);
+
+  const size_t nbytes = n_elems * h->elem;
+  const int proto = protocol == LLAR_AUTO ? auto_protocol(h, nbytes) : (int)protocol;
+  Geometry g;
+  int st = plan(h, n_elems, proto, g);
+  if (st != LLAR_OK) return fail(st);
+  return issue(h, partials, h->n_ranks, out, n_elems, proto, g, static_cast<hipStream_t>(stream));
+}
+
+int llar_send_recv(llar_comm* h, const void* send_buf, void* recv_buf, size_t n_elems, llar_dtype dtype,
+                   llar_protocol protocol, void* stream) {
+  if (!h) return fail(LLAR_ERR_ARG);
+  if ((int)dtype != h->kind) return fail(LLAR_ERR_ARG);
+  if (n_elems == 0) return LLAR_OK;
+  if (!send_buf || !recv_buf || !aligned16(send_buf) || !aligned16(recv_buf)) return fail(LLAR_ERR_ARG);
+  if (n_elems > h->max_bytes / h->elem) return fail(LLAR_ERR_ARG);
+  if (protocol != LLAR_AUTO && protocol != LLAR_LL && protocol != LLAR_SENTINEL) return fail(LLAR_ERR_ARG);
+  const size_t nbytes = n_elems * h->elem;
+  int proto = (int)protocol;
+  if (protocol == LLAR_AUTO) proto = ((long long)nbytes <= h->thr_sentinel && nbytes <= kCapLL) ? LLAR_LL : LLAR_SENTINEL;
+  Geometry g;
+  int st = plan(h, n_elems, proto, g);
+  if (st != LLAR_OK) return fail(st);
+  // the one-shot exchange with a single producer, in copy mode
+  switch (g.kernel) {
+    case kKernOneShotLL: g.kernel = kKernP2PLL; break;
+    case kKernOneShotSentinel: g.kernel = kKernP2PSentinel; break;
+    case kKernOneShotLLLocal: g.kernel = kKernP2PLLLocal; break;
+    case kKernOneShotSentinelLocal: g.kernel = kKernP2PSentinelLocal; break;
+    default: return fail(LLAR_ERR_ARG);
+  }
+  // rank 1 sends; rank 0 receives and reads no input of its own
+  const void* parts[2] = {send_buf, send_buf};
+  return issue(h, parts, 2, recv_buf, n_elems, proto, g, static_cast<hipStream_t>(stream));
 }
 
 int llar_get_device_status(llar_comm* h, uint32_t* bits) {

@@ -33,7 +33,12 @@ enum KernelId : int {
   kKernOneShotSentinelLocal = 7,
   kKernSentinelHs = 8,
   kKernSentinelHsLocal = 9,
-  kKernCount = 10
+  // point-to-point: one sender, one receiver (two ranks), copy instead of sum
+  kKernP2PLL = 10,
+  kKernP2PSentinel = 11,
+  kKernP2PLLLocal = 12,
+  kKernP2PSentinelLocal = 13,
+  kKernCount = 14
 };
 
 struct OneShotArgs {

@@ -228,7 +228,9 @@ __device__ __forceinline__ void trace_at(uint64_t* tr, int slot, bool drain) {
   }
 }
 
-template <int kWire, int kKind, int N, bool kLocal>
+// kCopy (point-to-point, N = 2): rank 1 sends, rank 0 writes what arrived
+// instead of a sum and reads no partial of its own.
+template <int kWire, int kKind, int N, bool kLocal, bool kCopy = false>
 __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
   const uint64_t t_entry = wall_ticks();
   int r;
@@ -258,7 +260,7 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
   u32x4 first_vec = {0u, 0u, 0u, 0u};
   u32x2 first_unit = {0u, 0u};
   if (producer && v0 + threadIdx.x < v1) first_vec = load_vec<false>(src, v0 + threadIdx.x, nbytes);
-  if (consumer && 2 * v0 + threadIdx.x < 2 * v1) first_unit = load_unit(src, 2 * v0 + threadIdx.x, nbytes);
+  if (!kCopy && consumer && 2 * v0 + threadIdx.x < 2 * v1) first_unit = load_unit(src, 2 * v0 + threadIdx.x, nbytes);
   WgState st = wg_begin(ctrl, host_epoch, timing, idle);
   if (trace && threadIdx.x == 0) trace[blockIdx.x * kTraceWords + 0] = t_entry;
   trace_at(trace, 1, false);
@@ -284,7 +286,8 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
     constexpr uint32_t kUnitStage = (kWire == kWireLL) ? 16u : 8u;
     bool dead = false;  // set after a timeout: stop waiting for anything else
     for (uint32_t u = 2 * v0 + threadIdx.x; u < 2 * v1 && !dead; u += blockDim.x) {
-      u32x2 own = (u == 2 * v0 + threadIdx.x) ? first_unit : load_unit(src, u, nbytes);
+      u32x2 own = {0u, 0u};
+      if constexpr (!kCopy) own = (u == 2 * v0 + threadIdx.x) ? first_unit : load_unit(src, u, nbytes);
       if (u == 2 * v0) trace_at(trace, 2, true);
       // A slot that is ready stays ready for the rest of the call (LL lines
       // carry this call's epoch; a filled Sentinel slot is only reset by this
@@ -319,7 +322,8 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
         continue;
       }
       if (u == 2 * v0) trace_at(trace, 3, false);
-      store_unit(out, u, nbytes, reduce_unit<kKind, N>(own, d));
+      if constexpr (kCopy) store_unit(out, u, nbytes, d[0]);
+      else store_unit(out, u, nbytes, reduce_unit<kKind, N>(own, d));
       if (u == 2 * v0) trace_at(trace, 4, true);
       if constexpr (kWire == kWireSentinel) {
         if (!keep) {
@@ -1034,6 +1038,23 @@ static hipError_t launch_n(const LaunchSpec& ls, hipStream_t stream) {
     case kKernSentinelHs:
       hipLaunchKernelGGL((k_twoshot_sentinel_hs<kKind, N, false>), grid, block, 0, stream, ls.twoshot);
       break;
+    case kKernP2PLL:
+    case kKernP2PSentinel:
+    case kKernP2PLLLocal:
+    case kKernP2PSentinelLocal:
+      if constexpr (N == 2) {
+        if (ls.kernel == kKernP2PLL)
+          hipLaunchKernelGGL((k_oneshot<kWireLL, kKind, 2, false, true>), grid, block, 0, stream, ls.oneshot);
+        else if (ls.kernel == kKernP2PSentinel)
+          hipLaunchKernelGGL((k_oneshot<kWireSentinel, kKind, 2, false, true>), grid, block, 0, stream, ls.oneshot);
+        else if (ls.kernel == kKernP2PLLLocal)
+          hipLaunchKernelGGL((k_oneshot<kWireLL, kKind, 2, true, true>), grid, block, 0, stream, ls.oneshot);
+        else
+          hipLaunchKernelGGL((k_oneshot<kWireSentinel, kKind, 2, true, true>), grid, block, 0, stream, ls.oneshot);
+      } else {
+        return hipErrorInvalidValue;
+      }
+      break;
     case kKernSentinelHsLocal:
       hipLaunchKernelGGL((k_twoshot_sentinel_hs<kKind, N, true>), grid, block, 0, stream, ls.twoshot);
       break;
@@ -1084,6 +1105,13 @@ static int occupancy_n(int kernel, int threads) {
     case kKernSentinelPipe: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_sentinel<kKind, N, false>, threads, 0); break;
     case kKernSentinelPipeLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_sentinel<kKind, N, true>, threads, 0); break;
     case kKernSentinelHs: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_sentinel_hs<kKind, N, false>, threads, 0); break;
+    case kKernP2PLL:
+    case kKernP2PSentinel:
+    case kKernP2PLLLocal:
+    case kKernP2PSentinelLocal:
+      // the copy kernels use no more resources than the two-rank one-shot ones
+      if constexpr (N == 2) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_oneshot<kWireSentinel, kKind, 2, false, true>, threads, 0);
+      break;
     case kKernSentinelHsLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_sentinel_hs<kKind, N, true>, threads, 0); break;
     default: break;
   }

@@ -106,6 +106,34 @@ def sentinel_reset(n_elems: int, dtype: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# Point-to-point transfer over the LL and Sentinel wires
+# ----------------------------------------------------------------------------
+def p2p_transfer(send_bits: np.ndarray, dtype: int, wire: str, epoch: int = 1) -> np.ndarray:
+    """What the receiver of a one-producer LL or Sentinel transfer writes out.
+
+    The pwwt.cn small-message latency article (section 1.1, the pipeline
+    parallel item; section 3.3, an 8 KB hidden state per token) has pipeline
+    stages pass activations by send/recv; the LL and Sentinel paragraphs of
+    the agihunt.info summary give the two wires.  LL: pack the payload with
+    the epoch, unpack it once both flags carry that epoch.  Sentinel: the
+    producer canonicalises, the receiver waits until no element holds the
+    sentinel and takes the staged value.
+    """
+    b = np.ascontiguousarray(np.asarray(send_bits, dtype=BITS_DTYPE[dtype]))
+    nbytes = b.size * ELEM_BYTES[dtype]
+    if wire == "ll":
+        valid, payload = ll_unpack(ll_pack(ll_payload_words(b), epoch), epoch)
+        assert valid.all()
+        raw = np.ascontiguousarray(payload).reshape(-1).view(np.uint8)[:nbytes]
+        return raw.view(BITS_DTYPE[dtype]).copy()
+    if wire == "sentinel":
+        staged = sentinel_canon(b, dtype)
+        assert sentinel_ready(staged, dtype).all()
+        return staged
+    raise ValueError("unknown wire %r" % (wire,))
+
+
+# ----------------------------------------------------------------------------
 # LL128 atomic two-shot
 # ----------------------------------------------------------------------------
 LL128_LINE_BYTES = 128

@@ -63,6 +63,7 @@ def test_null_handle_is_rejected_without_touching_the_gpu(L):
     import message_allreduce_amd as m
     assert L.llar_allreduce(None, None, None, 16, 0, 0, None) == -1
     assert L.llar_destroy(None) == 0
+    assert L.llar_send_recv(None, None, None, 16, 0, 1, None) == -1
     assert L.llar_set_option(None, b"timing", 1) == -1
     assert L.llar_get_device_status(None, None) == -1
     assert L.llar_staging_bytes(None, 1) == 0

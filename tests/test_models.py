@@ -145,6 +145,48 @@ def test_workload_3_is_sentinel_free():
         assert not (p == models.SENTINEL_BITS[F16]).any()
 
 
+# --------------------------------------------------------------------------- point-to-point
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_p2p_ll_delivers_every_16bit_pattern_unchanged(dt):
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for n in (65536, 65535, 1, 3):       # ragged: a last line only partly filled
+        got = models.p2p_transfer(allb[:n], dt, "ll", epoch=7)
+        assert got.dtype == allb.dtype and np.array_equal(got, allb[:n])
+
+
+def test_p2p_ll_delivers_fp32_bits_unchanged():
+    g = np.random.default_rng(11)
+    b = g.integers(0, 2**32, size=100_003, dtype=np.uint64).astype(np.uint32)
+    b[:4] = [models.SENTINEL_BITS[F32], 0x7FC00000, 0x80000000, 0x7F800000]
+    assert np.array_equal(models.p2p_transfer(b, F32, "ll", epoch=0xFFFFFFFF), b)
+
+
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_p2p_sentinel_moves_only_the_sentinel_exhaustive_16bit(dt):
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = models.p2p_transfer(allb, dt, "sentinel")
+    s = models.SENTINEL_BITS[dt]
+    moved = got != allb
+    assert moved.sum() == 1 and allb[moved][0] == s
+    assert oracle.is_nan_bits(got[moved], dt).all() and (got[moved] & 0x8000).all()
+
+
+@pytest.mark.parametrize("dt", [F32, F16, BF16])
+@pytest.mark.parametrize("wire", ["ll", "sentinel"])
+def test_p2p_equals_a_two_rank_sum_with_negative_zero(dt, wire):
+    # x + (-0) == x for every x (IEEE 754 section 6.3), so a copy is the
+    # two-rank AllReduce of the message and a negative-zero partial; the C
+    # oracle's binary64 sum checks the model independently (NaN as a class)
+    g = np.random.default_rng(40 + dt)
+    nb = {F32: 32, F16: 16, BF16: 16}[dt]
+    b = g.integers(0, 2**nb, size=20_001, dtype=np.uint64).astype(oracle.BITS_DTYPE[dt])
+    b[::101] = models.SENTINEL_BITS[dt]
+    neg0 = np.full_like(b, 1 << (nb - 1))
+    want = oracle.allreduce(np.stack([neg0, b]), dt)
+    got = models.p2p_transfer(b, dt, wire)
+    assert oracle.same_result(got, want, dt).all()
+
+
 # --------------------------------------------------------------------------- LL128
 def test_ll128_lane_grouping_matches_page(pages):
     p = pages["ll128"]

@@ -101,3 +101,13 @@ def make_partials(cfg_id: int, rep: int, n_ranks: int, dtype: str, n_elems: int,
 def workload_partials(w: Workload, rep: int, n_elems: Optional[int] = None) -> np.ndarray:
     n = w.n_elems if n_elems is None else n_elems
     return make_partials(w.cfg_id, rep, w.n_ranks, w.dtype, n, w.dist, w.scale)
+
+
+def random_bits(cfg_id: int, rep: int, n_elems: int, dtype: str) -> np.ndarray:
+    """n_elems element bit patterns drawn uniformly over every pattern of the
+    I/O type (NaNs, infinities, subnormals and the all-ones pattern
+    included), seeded by [cfg_id, rep]: the payload of a pure data move."""
+    rng = np.random.default_rng([int(cfg_id), int(rep)])
+    width = 32 if dtype == "fp32" else 16
+    b = rng.integers(0, 1 << width, size=n_elems, dtype=np.uint64)
+    return b.astype(np.uint32 if width == 32 else np.uint16)
