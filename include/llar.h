@@ -123,6 +123,51 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
 int llar_send_recv(llar_comm* h, const void* send_buf, void* recv_buf, size_t n_elems,
                    llar_dtype dtype, llar_protocol protocol, void* stream);
 
+/* ReduceScatter: every rank keeps one segment of the element-wise sum (the
+ * yololab.net article on network architecture for LLM inference, the table
+ * in its All-Reduce / All-Gather / Reduce-Scatter section; the first half of
+ * the two-shot AllReduce in the agihunt.info summary's two-shot LL128
+ * paragraph).  For every rank j and i < recv_count:
+ *
+ *   outs[j][i] = partials[0][j*recv_count + i] + ... + partials[N-1][j*recv_count + i]
+ *
+ * partials: host array of N device pointers, each N * recv_count elements.
+ * outs:     host array of N device pointers, each recv_count elements; outs[j]
+ *           may be partials[j] + j*recv_count (in place) but must not
+ *           overlap any other block that is read.
+ * One launch in which every rank sends its copy of segment j to rank j over
+ * the LL or Sentinel wire and rank j sums what arrived with its own copy, in
+ * binary64 in rank order with one rounding (deterministic, the same
+ * arithmetic as the LL and Sentinel AllReduce).
+ * protocol: LLAR_LL, LLAR_SENTINEL or LLAR_AUTO (LL while N * recv_count *
+ *   sizeof(dtype) is within the "thr_sentinel" size); others: LLAR_ERR_ARG.
+ * Limits: N * recv_count * sizeof(dtype) <= max_bytes (else LLAR_ERR_ARG),
+ *   and <= 8 MiB (LL) or 16 MiB (Sentinel) (else LLAR_ERR_UNSUPPORTED).
+ *   recv_count need not be a multiple of 16 bytes.  recv_count == 0 is a
+ *   no-op.  Pointers 16-byte aligned.  Errors, epochs and stream rules are
+ *   those of llar_allreduce, whose staging and epoch this call shares. */
+int llar_reduce_scatter(llar_comm* h, const void* const* partials, void* const* outs, size_t recv_count,
+                        llar_dtype dtype, llar_protocol protocol, void* stream);
+
+/* AllGather: every receiving rank holds every rank's fragment (same table of
+ * the yololab.net article; the second half of the two-shot AllReduce).  For
+ * every receiving rank j < n_outs, every rank k and i < send_count:
+ *
+ *   outs[j][k*send_count + i] = inputs[k][i]
+ *
+ * inputs: host array of N device pointers, each send_count elements.
+ * outs:   host array of n_outs device pointers, each N * send_count elements.
+ * n_outs: N (every rank's copy -- the replicated result an AllGather leaves
+ *         on all ranks) or 1 (rank 0's copy only); others: LLAR_ERR_ARG.
+ * Wire: LL moves every bit pattern unchanged.  The Sentinel wire cannot
+ *   carry its all-ones pattern, which arrives as the pattern one below (a
+ *   negative NaN still); the receiver applies the same to its own fragment,
+ *   so every copy is identical.
+ * protocol, limits (N * send_count * sizeof(dtype)), errors and streams as
+ *   for llar_reduce_scatter. */
+int llar_all_gather(llar_comm* h, const void* const* inputs, void* const* outs, int n_outs, size_t send_count,
+                    llar_dtype dtype, llar_protocol protocol, void* stream);
+
 /* Free all resources (synchronises the device first).  NULL is a no-op. */
 int llar_destroy(llar_comm* h);
 

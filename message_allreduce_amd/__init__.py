@@ -12,6 +12,8 @@ Python names mirror the C ABI::
     h = llar_create(n_ranks, dtype, max_bytes)
     llar_allreduce(h, partials, out, n_elems, dtype, protocol, stream)
     llar_send_recv(h, send, recv, n_elems, dtype, protocol, stream)
+    llar_reduce_scatter(h, partials, outs, recv_count, dtype, protocol, stream)
+    llar_all_gather(h, inputs, outs, n_outs, send_count, dtype, protocol, stream)
     llar_destroy(h)
 
 and ``Communicator`` wraps them for torch tensors.
@@ -24,7 +26,7 @@ import os
 __all__ = [
     "FP32", "FP16", "BF16", "AUTO", "LL", "SENTINEL", "LL128", "LL128_PIPELINED", "SENTINEL_PIPELINED",
     "PROTOCOLS", "LlarError", "lib", "library_path", "llar_create", "llar_allreduce", "llar_destroy",
-    "llar_send_recv", "llar_set_option", "llar_get_option", "llar_get_device_status", "llar_clear_device_status",
+    "llar_send_recv", "llar_reduce_scatter", "llar_all_gather", "llar_set_option", "llar_get_option", "llar_get_device_status", "llar_clear_device_status",
     "llar_select_protocol", "llar_debug_copy_staging", "llar_staging_bytes", "llar_get_epoch",
     "llar_get_timing", "llar_wallclock_hz", "llar_launch_geometry", "llar_floor_measure",
     "llar_status_string", "llar_last_error", "llar_get_trace", "llar_get_pipeline_trace", "Communicator", "EXPORTED_SYMBOLS",
@@ -43,7 +45,7 @@ EXPORTED_SYMBOLS = (
     "llar_get_device_status", "llar_clear_device_status", "llar_set_option", "llar_get_option",
     "llar_select_protocol", "llar_debug_copy_staging", "llar_staging_bytes", "llar_get_epoch",
     "llar_get_timing", "llar_wallclock_hz", "llar_launch_geometry", "llar_floor_measure",
-    "llar_get_trace", "llar_get_pipeline_trace", "llar_send_recv",
+    "llar_get_trace", "llar_get_pipeline_trace", "llar_send_recv", "llar_reduce_scatter", "llar_all_gather",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +74,8 @@ def lib() -> ctypes.CDLL:
         "llar_create": (vp, [i32, i32, sz]),
         "llar_allreduce": (i32, [vp, ctypes.POINTER(vp), vp, sz, i32, i32, vp]),
         "llar_send_recv": (i32, [vp, vp, vp, sz, i32, i32, vp]),
+        "llar_reduce_scatter": (i32, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), sz, i32, i32, vp]),
+        "llar_all_gather": (i32, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, sz, i32, i32, vp]),
         "llar_destroy": (i32, [vp]),
         "llar_last_error": (i32, []),
         "llar_status_string": (ctypes.c_char_p, [i32]),
@@ -123,6 +127,22 @@ def llar_send_recv(h: int, send: int, recv: int, n_elems: int, dtype: int, proto
     """send, recv: device pointers (ints)."""
     return lib().llar_send_recv(h, ctypes.c_void_p(int(send)), ctypes.c_void_p(int(recv)), int(n_elems), int(dtype),
                                 int(protocol), ctypes.c_void_p(int(stream)))
+
+
+def _ptrs(seq):
+    return (ctypes.c_void_p * len(seq))(*[int(p) for p in seq])
+
+
+def llar_reduce_scatter(h: int, partials, outs, recv_count: int, dtype: int, protocol: int, stream: int) -> int:
+    """partials, outs: sequences of device pointers (ints)."""
+    return lib().llar_reduce_scatter(h, _ptrs(partials), _ptrs(outs), int(recv_count), int(dtype), int(protocol),
+                                     ctypes.c_void_p(int(stream)))
+
+
+def llar_all_gather(h: int, inputs, outs, send_count: int, dtype: int, protocol: int, stream: int) -> int:
+    """inputs, outs: sequences of device pointers (ints); len(outs) is n_outs."""
+    return lib().llar_all_gather(h, _ptrs(inputs), _ptrs(outs), len(outs), int(send_count), int(dtype),
+                                 int(protocol), ctypes.c_void_p(int(stream)))
 
 
 def llar_destroy(h: int) -> int:
@@ -268,6 +288,45 @@ class Communicator:
         s = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
         st = llar_send_recv(self.h, send.data_ptr(), recv.data_ptr(), n, self.dtype, protocol, s)
         return _check(st, "llar_send_recv")
+
+    def reduce_scatter(self, partials, outs, protocol=AUTO, stream=None):
+        """outs[j] (``outs[j].numel()`` elements, the same for every j) gets
+        segment j of the sum of ``partials``."""
+        import torch
+        if isinstance(protocol, str):
+            protocol = PROTOCOLS[protocol]
+        if len(partials) != self.n_ranks or len(outs) != self.n_ranks:
+            raise ValueError("expected %d partials and %d outputs" % (self.n_ranks, self.n_ranks))
+        count = outs[0].numel()
+        self._check_tensors(partials, self.n_ranks * count, "partials")
+        self._check_tensors(outs, count, "outs")
+        s = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+        st = llar_reduce_scatter(self.h, [p.data_ptr() for p in partials], [o.data_ptr() for o in outs], count,
+                                 self.dtype, protocol, s)
+        return _check(st, "llar_reduce_scatter")
+
+    def all_gather(self, inputs, outs, protocol=AUTO, stream=None):
+        """Every tensor of ``outs`` (N of them, or one: rank 0's copy) gets
+        the N fragments ``inputs`` (``inputs[0].numel()`` elements each)
+        back to back."""
+        import torch
+        if isinstance(protocol, str):
+            protocol = PROTOCOLS[protocol]
+        if len(inputs) != self.n_ranks or len(outs) not in (1, self.n_ranks):
+            raise ValueError("expected %d inputs and 1 or %d outputs" % (self.n_ranks, self.n_ranks))
+        count = inputs[0].numel()
+        self._check_tensors(inputs, count, "inputs")
+        self._check_tensors(outs, self.n_ranks * count, "outs")
+        s = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+        st = llar_all_gather(self.h, [p.data_ptr() for p in inputs], [o.data_ptr() for o in outs], count,
+                             self.dtype, protocol, s)
+        return _check(st, "llar_all_gather")
+
+    def _check_tensors(self, ts, min_numel, what):
+        for t in ts:
+            if not (t.is_cuda and t.is_contiguous() and t.numel() >= min_numel and _dtype_code(t) == self.dtype):
+                raise ValueError("%s must be contiguous device tensors of the communicator's dtype with at least "
+                                 "%d elements" % (what, min_numel))
 
     def prepare(self, partials, out, protocol=AUTO, stream=None):
         """Validate and marshal the arguments once; return a no-argument

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libllar.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["llar_kernels.hip", "llar_host.hip", "llar_floor.hip"]
+SOURCES = ["llar_kernels.hip", "llar_multi.hip", "llar_host.hip", "llar_floor.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

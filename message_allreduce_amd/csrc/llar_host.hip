@@ -345,11 +345,13 @@ llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes) {
   const int N = n_ranks;
   const size_t mb = h->max_bytes;
   // LL: [parity][rank 1..N-1][vector][2 x 16 B]
-  size_t ll_vec = ceil_div(std::min(mb, kCapLL), 16);
+  // (N spare vectors per rank: N blocks of a ReduceScatter or AllGather,
+  // each rounded up to whole vectors, fit in (N - 1) rank slots)
+  size_t ll_vec = ceil_div(std::min(mb, kCapLL), 16) + (size_t)N;
   h->ll.rank_stride = ll_vec * 32;
   h->ll.parity_stride = h->ll.rank_stride * (size_t)std::max(N - 1, 1);
   // Sentinel one-shot: [parity][rank 1..N-1][vector] 16 B
-  size_t s_vec = ceil_div(std::min(mb, kCapSentinel), 16);
+  size_t s_vec = ceil_div(std::min(mb, kCapSentinel), 16) + (size_t)N;
   h->sent.rank_stride = s_vec * 16;
   h->sent.parity_stride = h->sent.rank_stride * (size_t)std::max(N - 1, 1);
   // LL128 one round: [parity][line] 128 B, binary32 staging needs the most lines
@@ -445,6 +447,23 @@ int llar_launch_geometry(llar_comm* h, size_t n_elems, llar_protocol protocol, i
 
 namespace {
 
+uint64_t spin_ticks(const llar_comm* h) { return (uint64_t)((double)h->spin_timeout_us * 1e-6 * h->wall_hz); }
+
+// Epoch source of a call: the host numbers stream-ordered calls; a captured
+// call must read the device-resident epoch (its arguments repeat on replay).
+bool call_epoch(const llar_comm* h, hipStream_t stream, bool& device_epoch, uint32_t& host_epoch) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return false;
+  device_epoch = h->device_epoch || cap != hipStreamCaptureStatusNone;
+  host_epoch = device_epoch ? 0u : h->host_epoch;
+  return true;
+}
+
+void finish_call(llar_comm* h, bool device_epoch) {
+  h->last_call_device = device_epoch;
+  if (!device_epoch) h->host_epoch = next_host_epoch(h->host_epoch);
+}
+
 // Issue one call of the planned kernel.  `n_launch` ranks take part (the
 // communicator's rank count, or two for a point-to-point copy); `parts`
 // holds their input pointers.
@@ -467,13 +486,10 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
   if (ls.grid > occ * h->cu_count) return fail(LLAR_ERR_UNSUPPORTED);
   if (h->timing && ls.grid > kTimingMaxWgs) return fail(LLAR_ERR_UNSUPPORTED);
 
-  const uint64_t spin = (uint64_t)((double)h->spin_timeout_us * 1e-6 * h->wall_hz);
-  // epoch source: the host numbers stream-ordered calls; a captured call
-  // must read the device-resident epoch (its arguments repeat on replay)
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return fail(LLAR_ERR_HIP);
-  const bool device_epoch = h->device_epoch || cap != hipStreamCaptureStatusNone;
-  const uint32_t host_epoch = device_epoch ? 0u : h->host_epoch;
+  const uint64_t spin = spin_ticks(h);
+  bool device_epoch = false;
+  uint32_t host_epoch = 0;
+  if (!call_epoch(h, stream, device_epoch, host_epoch)) return fail(LLAR_ERR_HIP);
   const bool is_oneshot = g.kernel == kKernOneShotLL || g.kernel == kKernOneShotSentinel ||
                           g.kernel == kKernOneShotLLLocal || g.kernel == kKernOneShotSentinelLocal ||
                           g.kernel == kKernP2PLL || g.kernel == kKernP2PSentinel || g.kernel == kKernP2PLLLocal ||
@@ -572,8 +588,88 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
   if (!reg->ptr) return fail(LLAR_ERR_UNSUPPORTED);
   hipError_t e = launch(ls, stream);
   if (e != hipSuccess) return fail(LLAR_ERR_HIP);
-  h->last_call_device = device_epoch;
-  if (!device_epoch) h->host_epoch = next_host_epoch(h->host_epoch);
+  finish_call(h, device_epoch);
+  return LLAR_OK;
+}
+
+// ReduceScatter (gather = false) or AllGather (gather = true) of `count`
+// elements per block over the LL or Sentinel wire: one launch in which every
+// rank sends to and receives from every other rank.  `n_recv` ranks receive
+// (N, or 1 for an AllGather seen by rank 0 only).
+int run_multi(llar_comm* h, const void* const* ins, void* const* outs, int n_recv, size_t count, llar_dtype dtype,
+              llar_protocol protocol, bool gather, hipStream_t stream) {
+  if (!h || !ins || !outs) return fail(LLAR_ERR_ARG);
+  if ((int)dtype != h->kind) return fail(LLAR_ERR_ARG);
+  const int N = h->n_ranks;
+  if (n_recv != N && !(gather && n_recv == 1)) return fail(LLAR_ERR_ARG);
+  if (protocol != LLAR_AUTO && protocol != LLAR_LL && protocol != LLAR_SENTINEL) return fail(LLAR_ERR_ARG);
+  if (count == 0) return LLAR_OK;
+  if (count > h->max_bytes / h->elem / (size_t)N) return fail(LLAR_ERR_ARG);
+  for (int r = 0; r < N; ++r)
+    if (!ins[r] || !aligned16(ins[r])) return fail(LLAR_ERR_ARG);
+  for (int r = 0; r < n_recv; ++r)
+    if (!outs[r] || !aligned16(outs[r])) return fail(LLAR_ERR_ARG);
+  const size_t blk = count * h->elem;
+  const size_t total = blk * (size_t)N;
+  int proto = (int)protocol;
+  if (protocol == LLAR_AUTO) proto = ((long long)total <= h->thr_sentinel && total <= kCapLL) ? LLAR_LL : LLAR_SENTINEL;
+  if (total > (proto == LLAR_LL ? kCapLL : kCapSentinel)) return fail(LLAR_ERR_UNSUPPORTED);
+  const Region* reg = region_of(h, proto);
+  if (!reg->ptr) return fail(LLAR_ERR_UNSUPPORTED);
+
+  const int threads = h->threads ? (int)h->threads : 256;
+  if (threads != 64 && threads != 128 && threads != 256 && threads != 512) return fail(LLAR_ERR_ARG);
+  const size_t nv = ceil_div(blk, 16);
+  const int slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(2 * nv, (size_t)threads), 1, 64);
+  uint32_t place = (h->placement == 1 || !h->local_ok) ? kPlaceSpread : kPlaceLocal;
+  const int grid_slices = place == kPlaceLocal ? (int)ceil_div((size_t)slices, 8) * 8 : slices;
+  int kernel;
+  if (gather) kernel = proto == LLAR_LL ? kKernAgLL : kKernAgSentinel;
+  else kernel = proto == LLAR_LL ? kKernRsLL : kKernRsSentinel;
+  if (place == kPlaceLocal) kernel += kKernRsLLLocal - kKernRsLL;
+
+  // staging: N receivers x (N - 1) sender slots per parity
+  const size_t slot_stride = nv * (proto == LLAR_LL ? 32 : 16);
+  if ((size_t)N * (size_t)std::max(N - 1, 1) * slot_stride > reg->parity_stride) return fail(LLAR_ERR_UNSUPPORTED);
+
+  LaunchSpec ls;
+  memset(&ls, 0, sizeof(ls));
+  ls.kind = h->kind;
+  ls.n_ranks = N;
+  ls.kernel = kernel;
+  ls.threads = threads;
+  ls.grid = N * grid_slices;
+  int occ = occupancy(h->kind, N, kernel, threads);
+  if (occ <= 0) return fail(LLAR_ERR_HIP);
+  if (ls.grid > occ * h->cu_count) return fail(LLAR_ERR_UNSUPPORTED);
+  if (h->timing && ls.grid > kTimingMaxWgs) return fail(LLAR_ERR_UNSUPPORTED);
+
+  bool device_epoch = false;
+  uint32_t host_epoch = 0;
+  if (!call_epoch(h, stream, device_epoch, host_epoch)) return fail(LLAR_ERR_HIP);
+  MultiArgs& a = ls.multi;
+  for (int r = 0; r < N; ++r) a.in[r] = static_cast<const uint8_t*>(ins[r]);
+  for (int r = 0; r < n_recv; ++r) a.out[r] = static_cast<uint8_t*>(outs[r]);
+  a.stage = reg->ptr;
+  a.ctrl = h->ctrl;
+  a.blk = blk;
+  a.spin_limit = spin_ticks(h);
+  a.vq = (uint32_t)(nv / (size_t)slices);
+  a.vr = (uint32_t)(nv % (size_t)slices);
+  a.stage_bytes = (uint32_t)reg->bytes;
+  a.parity_stride = (uint32_t)reg->parity_stride;
+  a.slot_stride = (uint32_t)slot_stride;
+  a.n_recv = (uint32_t)n_recv;
+  a.aligned = (blk % 16 == 0) ? 1u : 0u;
+  a.grid = (uint32_t)ls.grid;
+  a.slices = (uint32_t)slices;
+  a.timing = h->timing ? 1u : 0u;
+  a.keep = h->keep_staging ? 1u : 0u;
+  a.drop_rank = h->debug_drop_rank < 0 ? 0xFFFFFFFFu : (uint32_t)h->debug_drop_rank;
+  a.host_epoch = host_epoch;
+  hipError_t e = launch(ls, stream);
+  if (e != hipSuccess) return fail(LLAR_ERR_HIP);
+  finish_call(h, device_epoch);
   return LLAR_OK;
 }
 
@@ -623,6 +719,17 @@ int llar_send_recv(llar_comm* h, const void* send_buf, void* recv_buf, size_t n_
   // rank 1 sends; rank 0 receives and reads no input of its own
   const void* parts[2] = {send_buf, send_buf};
   return issue(h, parts, 2, recv_buf, n_elems, proto, g, static_cast<hipStream_t>(stream));
+}
+
+int llar_reduce_scatter(llar_comm* h, const void* const* partials, void* const* outs, size_t recv_count,
+                        llar_dtype dtype, llar_protocol protocol, void* stream) {
+  return run_multi(h, partials, outs, h ? h->n_ranks : 0, recv_count, dtype, protocol, false,
+                   static_cast<hipStream_t>(stream));
+}
+
+int llar_all_gather(llar_comm* h, const void* const* inputs, void* const* outs, int n_outs, size_t send_count,
+                    llar_dtype dtype, llar_protocol protocol, void* stream) {
+  return run_multi(h, inputs, outs, n_outs, send_count, dtype, protocol, true, static_cast<hipStream_t>(stream));
 }
 
 int llar_get_device_status(llar_comm* h, uint32_t* bits) {

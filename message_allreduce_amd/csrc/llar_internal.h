@@ -38,8 +38,18 @@ enum KernelId : int {
   kKernP2PSentinel = 11,
   kKernP2PLLLocal = 12,
   kKernP2PSentinelLocal = 13,
-  kKernCount = 14
+  // ReduceScatter and AllGather: every rank sends and receives
+  kKernRsLL = 14,
+  kKernRsSentinel = 15,
+  kKernAgLL = 16,
+  kKernAgSentinel = 17,
+  kKernRsLLLocal = 18,
+  kKernRsSentinelLocal = 19,
+  kKernAgLLLocal = 20,
+  kKernAgSentinelLocal = 21,
+  kKernCount = 22
 };
+constexpr int kKernFirstMulti = kKernRsLL;
 
 struct OneShotArgs {
   const uint8_t* part[8];
@@ -87,6 +97,32 @@ struct TwoShotArgs {
   uint64_t* trace;       // per-workgroup, per-chunk stamps (kPipeTraceWords each), or null
 };
 
+// ReduceScatter / AllGather over the LL or Sentinel wire.  A block is what
+// one sender hands one receiver: RS -- the sender's copy of the receiver's
+// segment; AG -- the sender's whole fragment.  Staging per parity:
+// [receiver][sender slot 0..N-2][block], sender k at slot k of receiver j
+// when k < j, slot k-1 when k > j.
+struct MultiArgs {
+  const uint8_t* in[8];   // RS: N blocks per rank; AG: one fragment per rank
+  uint8_t* out[8];        // RS: one segment per rank; AG: N fragments per receiving rank
+  uint8_t* stage;
+  Ctrl* ctrl;
+  uint64_t blk;           // bytes per block
+  uint64_t spin_limit;
+  uint32_t vq, vr;        // slice w holds vq 16-byte vectors of a block, plus one when w < vr
+  uint32_t stage_bytes;
+  uint32_t parity_stride;
+  uint32_t slot_stride;   // staging bytes per (receiver, sender) slot
+  uint32_t n_recv;        // receiving ranks 0..n_recv-1: N, or 1 for an AllGather seen by rank 0
+  uint32_t aligned;       // blk is a multiple of 16 bytes: whole-vector accesses
+  uint32_t grid;
+  uint32_t slices;
+  uint32_t timing;
+  uint32_t keep;
+  uint32_t drop_rank;
+  uint32_t host_epoch;
+};
+
 // per-chunk trace of the pipelined Sentinel: per workgroup 4 x kPipeTraceChunks
 // stamps (producer credit granted, producer stores issued, consumer slots
 // ready, consumer done) of the first kPipeTraceChunks chunks
@@ -104,10 +140,14 @@ struct LaunchSpec {
   int threads;
   OneShotArgs oneshot;
   TwoShotArgs twoshot;
+  MultiArgs multi;
 };
 
 hipError_t launch(const LaunchSpec& ls, hipStream_t stream);
 int occupancy(int kind, int n_ranks, int kernel, int threads);
+// the ReduceScatter / AllGather kernels (kernel ids from kKernFirstMulti)
+hipError_t launch_multi(const LaunchSpec& ls, hipStream_t stream);
+int occupancy_multi(int kind, int n_ranks, int kernel, int threads);
 hipError_t launch_xcc_probe(uint32_t* out, int grid, hipStream_t stream);
 
 }  // namespace llar

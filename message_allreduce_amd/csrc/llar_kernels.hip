@@ -24,78 +24,6 @@
 namespace llar {
 
 // ---------------------------------------------------------------------------
-// shared prologue / epilogue: the call's epoch
-// ---------------------------------------------------------------------------
-// Two epoch sources.  In ordinary stream-ordered use the host numbers the
-// calls and passes the epoch in the kernel arguments (host_epoch, bit 31
-// clear): nothing to read on the device.  Under graph capture the arguments
-// would repeat on every replay, so the kernel reads the device-resident epoch
-// (bit 31 set; the two ranges never meet): thread 0 reads it, publishes it
-// through LDS and takes an arrival ticket; the workgroup that arrives last
-// (ticket == G-1) advances it when it finishes -- by then every workgroup of
-// the call has read the old value, and the next call starts after this one.
-// Timing mode has each workgroup store its own start and end stamps in the
-// epoch's ring slot (plain stores, no shared counter); workgroup 0 also
-// records the grid so that the reader knows how many entries belong to it.
-struct WgState {
-  uint32_t epoch;
-  uint32_t ticket;
-  bool counted;
-  uint64_t t0;
-};
-
-__device__ __forceinline__ WgState wg_begin(Ctrl* ctrl, uint32_t host_epoch, bool timing, bool idle) {
-  __shared__ uint32_t s_epoch;
-  WgState st{host_epoch, 0u, false, 0ull};
-  if (timing && threadIdx.x == 0) st.t0 = wall_ticks();
-  if (host_epoch != 0u) return st;
-  if (threadIdx.x == 0) {
-    const uint32_t e = __hip_atomic_load(&ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_epoch = e;
-    st.ticket = __hip_atomic_fetch_add(&ctrl->arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    st.counted = true;
-  }
-  __syncthreads();
-  st.epoch = s_epoch;
-  return st;
-}
-
-__device__ __forceinline__ void wg_end(Ctrl* ctrl, const WgState& st, uint32_t host_epoch, uint32_t grid, bool timing,
-                                       bool idle) {
-  if (timing) {
-    drain_vm();
-    __syncthreads();
-  }
-  if (threadIdx.x != 0) return;
-  if (timing) {
-    const uint64_t t1 = wall_ticks();
-    const uint32_t slot = st.epoch % kTimingRing;
-    uint64_t* p = ctrl->timing_wg + ((size_t)slot * kTimingMaxWgs + blockIdx.x) * 2u;
-    p[0] = idle ? ~0ull : st.t0;
-    p[1] = idle ? 0ull : t1;
-    if (blockIdx.x == 0) ctrl->timing_grid[slot] = grid;
-  }
-  if (st.counted && st.ticket == grid - 1u) {
-    __hip_atomic_store(&ctrl->arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&ctrl->epoch, next_device_epoch(st.epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// Role of workgroup b under a placement known at compile time (no kernel
-// argument is needed to find it).
-template <bool kLocal, int N>
-__device__ __forceinline__ void decode_role_t(uint32_t b, int& r, uint32_t& w) {
-  if constexpr (kLocal) {
-    const uint32_t x = b & 7u, q = b >> 3;
-    r = (int)(q % (uint32_t)N);
-    w = (q / (uint32_t)N) * 8u + x;
-  } else {
-    r = (int)(b % (uint32_t)N);
-    w = b / (uint32_t)N;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // tail-safe 16-byte vector access to the caller's buffers
 // ---------------------------------------------------------------------------
 // Only the last vector of a message can be partial; its elements (2 or 4
@@ -1080,6 +1008,7 @@ static hipError_t launch_kind(const LaunchSpec& ls, hipStream_t stream) {
 }
 
 hipError_t launch(const LaunchSpec& ls, hipStream_t stream) {
+  if (ls.kernel >= kKernFirstMulti) return launch_multi(ls, stream);
   switch (ls.kind) {
     case kKindF32: return launch_kind<kKindF32>(ls, stream);
     case kKindF16: return launch_kind<kKindF16>(ls, stream);
@@ -1134,6 +1063,7 @@ static int occupancy_kind(int n_ranks, int kernel, int threads) {
 }
 
 int occupancy(int kind, int n_ranks, int kernel, int threads) {
+  if (kernel >= kKernFirstMulti) return occupancy_multi(kind, n_ranks, kernel, threads);
   switch (kind) {
     case kKindF32: return occupancy_kind<kKindF32>(n_ranks, kernel, threads);
     case kKindF16: return occupancy_kind<kKindF16>(n_ranks, kernel, threads);

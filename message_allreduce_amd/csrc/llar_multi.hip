@@ -1,0 +1,299 @@
+// llar_multi.hip -- ReduceScatter and AllGather over the LL and Sentinel
+// wires, N ranks emulated inside one GPU.
+//
+// Definitions (yololab.net article on network architecture for LLM
+// inference, the table of the section on All-Reduce, All-Gather and
+// Reduce-Scatter): after a ReduceScatter every rank keeps one segment of the
+// element-wise sum; after an AllGather every rank holds every rank's
+// fragment.  They are the two halves of the two-shot AllReduce of "Every
+// Microsecond Matters" (agihunt.info summary, two-shot LL128 paragraph).
+//
+// One launch, every rank both sends and receives.  Workgroup (rank r,
+// slice w) first puts slice w of each of its blocks into the staging slot
+// the receiving rank reads (no wait: producers never block), then polls its
+// own N-1 slots for slice w and writes its output.  The wires are those of
+// the one-shot AllReduce: LL lines {data0, epoch, data1, epoch} (LL
+// paragraph), or a Sentinel-prefilled slot that the receiver resets after
+// use (Sentinel paragraph).  Every workgroup of the grid is resident at once
+// (the host checks occupancy), so a receiver's poll always ends: the data
+// arrives, or the bounded poll expires and latches a timeout.
+//
+// Blocks need not be a multiple of 16 bytes: then the accesses to the
+// caller's buffers (which start at block multiples) move halfwords, and the
+// last vector of a block is zero-padded in staging.
+#include "llar_device.h"
+#include "llar_internal.h"
+
+namespace llar {
+namespace {
+
+// ---- caller-buffer access at a byte offset, clipped at `end` ----------------
+// `off` is a multiple of the element size; whole vectors (or units) are moved
+// only when the block size keeps them 16-byte aligned.
+__device__ __forceinline__ u32x4 load16_at(const uint8_t* p, uint64_t off, uint64_t end, bool aligned) {
+  if (aligned && off + 16u <= end) return *reinterpret_cast<const u32x4*>(p + off);
+  u32x4 x = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (uint32_t k = 0; k < 16u; k += 2u) {
+    if (off + k < end) x[k >> 2] |= (uint32_t)(*reinterpret_cast<const uint16_t*>(p + off + k)) << ((k & 2u) * 8u);
+  }
+  return x;
+}
+__device__ __forceinline__ u32x2 load8_at(const uint8_t* p, uint64_t off, uint64_t end, bool aligned) {
+  if (aligned && off + 8u <= end) return *reinterpret_cast<const u32x2*>(p + off);
+  u32x2 x = {0u, 0u};
+#pragma unroll
+  for (uint32_t k = 0; k < 8u; k += 2u) {
+    if (off + k < end) x[k >> 2] |= (uint32_t)(*reinterpret_cast<const uint16_t*>(p + off + k)) << ((k & 2u) * 8u);
+  }
+  return x;
+}
+__device__ __forceinline__ void store8_at(uint8_t* p, uint64_t off, uint64_t end, bool aligned, u32x2 x) {
+  if (aligned && off + 8u <= end) {
+    *reinterpret_cast<u32x2*>(p + off) = x;
+    return;
+  }
+#pragma unroll
+  for (uint32_t k = 0; k < 8u; k += 2u) {
+    if (off + k < end) *reinterpret_cast<uint16_t*>(p + off + k) = (uint16_t)(x[k >> 2] >> ((k & 2u) * 8u));
+  }
+}
+
+// Reduce an 8-byte unit with the receiver's own value at rank position
+// `own_rank` and the senders' values in d[0..N-2] ordered by rank: binary64
+// sum in rank order starting from rank 0's value, one rounding.  Indices into
+// d stay compile-time; the own position is chosen with selects.
+template <int kKind, int N>
+__device__ __forceinline__ u32x2 reduce_unit_at(const u32x2& own, int own_rank, const u32x2 (&d)[N > 1 ? N - 1 : 1]) {
+  constexpr int kPerUnit = 8 / Elem<kKind>::kBytes;
+  u32x2 out = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < kPerUnit; ++j) {
+    auto elem = [&](const u32x2& v) -> uint32_t {
+      if constexpr (Elem<kKind>::kBytes == 4) return v[j];
+      else return (v[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+    };
+    double s = 0.0;
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+      const uint32_t below = (r < N - 1) ? elem(d[r < N - 1 ? r : 0]) : 0u;  // rank r at d[r]
+      const uint32_t above = (r >= 1) ? elem(d[r >= 1 ? r - 1 : 0]) : 0u;   // rank r at d[r-1]
+      const uint32_t bits = (r < own_rank) ? below : (r == own_rank) ? elem(own) : above;
+      const double x = Elem<kKind>::dec(bits);
+      s = (r == 0) ? x : s + x;
+    }
+    const uint32_t bits = Elem<kKind>::enc(s);
+    if constexpr (Elem<kKind>::kBytes == 4) out[j] = bits;
+    else out[j >> 1] |= (bits & 0xFFFFu) << ((j & 1) * 16);
+  }
+  return out;
+}
+
+template <int kKind>
+__device__ __forceinline__ u32x2 sentinel_canon8(const u32x2& v) {
+  const u32x4 c = sentinel_canon<kKind>(u32x4{v[0], v[1], 0u, 0u});
+  return u32x2{c[0], c[1]};
+}
+
+template <int kWire, int kKind, int N, bool kGather, bool kLocal>
+__global__ void __launch_bounds__(512) k_multi(MultiArgs a) {
+  int r;
+  uint32_t w;
+  decode_role_t<kLocal, N>(blockIdx.x, r, w);
+  const uint8_t* const src = a.in[r];
+  uint8_t* const out = a.out[r];
+  uint8_t* const stage = a.stage;
+  Ctrl* const ctrl = a.ctrl;
+  const uint64_t blk = a.blk, spin_limit = a.spin_limit;
+  const uint32_t vq = a.vq, vr = a.vr, stage_bytes = a.stage_bytes, parity_stride = a.parity_stride;
+  const uint32_t slot_stride = a.slot_stride, n_recv = a.n_recv, grid = a.grid, slices = a.slices;
+  const uint32_t timing = a.timing, keep = a.keep, drop_rank = a.drop_rank, host_epoch = a.host_epoch;
+  const bool aligned = a.aligned != 0u;
+  LLAR_UNIFORM_AT_ENTRY("s"(src), "s"(out), "s"(stage), "s"(ctrl), "s"(blk), "s"(spin_limit), "s"(vq), "s"(vr),
+                        "s"(stage_bytes), "s"(parity_stride), "s"(slot_stride), "s"(n_recv), "s"(grid), "s"(slices),
+                        "s"(timing), "s"(keep), "s"(drop_rank), "s"(host_epoch));
+  const bool idle = (w >= slices);
+  const uint32_t v0 = idle ? 0u : w * vq + min(w, vr);
+  const uint32_t v1 = idle ? 0u : v0 + vq + (w < vr ? 1u : 0u);
+  WgState st = wg_begin(ctrl, host_epoch, timing, idle);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(stage, stage_bytes);
+  const uint32_t e = st.epoch;
+  const uint32_t par_off = (e & 1u) * parity_stride;
+  constexpr uint32_t kVecStage = (kWire == kWireLL) ? 32u : 16u;
+  constexpr uint32_t kUnitStage = (kWire == kWireLL) ? 16u : 8u;
+
+  // ---- send: slice w of this rank's block for every receiver -----------------
+  if (!idle && (uint32_t)r != drop_rank) {
+    for (uint32_t v = v0 + threadIdx.x; v < v1; v += blockDim.x) {
+      // every load first, then every store
+      u32x4 x[kGather ? 1 : N];
+#pragma unroll
+      for (int j = 0; j < (kGather ? 1 : N); ++j) {
+        const uint64_t base = kGather ? 0u : (uint64_t)j * blk;
+        const bool wanted = kGather || (j != r && (uint32_t)j < n_recv);
+        x[j] = wanted ? load16_at(src, base + (uint64_t)v * 16u, base + blk, aligned) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        if (j == r || (uint32_t)j >= n_recv) continue;
+        const u32x4 y = x[kGather ? 0 : j];
+        const uint32_t slot = (uint32_t)j * (uint32_t)(N - 1) + (uint32_t)(r < j ? r : r - 1);
+        const uint32_t off = par_off + slot * slot_stride + v * kVecStage;
+        if constexpr (kWire == kWireLL) {
+          st16_stage<kLocal>(rs, off, u32x4{y[0], e, y[1], e});
+          st16_stage<kLocal>(rs, off + 16u, u32x4{y[2], e, y[3], e});
+        } else {
+          st16_stage<kLocal>(rs, off, sentinel_canon<kKind>(y));
+        }
+      }
+    }
+  }
+
+  // ---- receive: slice w from every other rank ---------------------------------
+  if (!idle && (uint32_t)r < n_recv) {
+    const uint64_t own_base = kGather ? 0u : (uint64_t)r * blk;
+    const uint32_t my_slots = par_off + (uint32_t)r * (uint32_t)(N - 1) * slot_stride;
+    bool dead = false;  // set after a timeout: stop waiting for anything else
+    for (uint32_t u = 2u * v0 + threadIdx.x; u < 2u * v1 && !dead; u += blockDim.x) {
+      const u32x2 own = load8_at(src, own_base + (uint64_t)u * 8u, own_base + blk, aligned);
+      u32x2 d[N > 1 ? N - 1 : 1];
+      d[0] = u32x2{0u, 0u};
+      Spin spin(spin_limit);
+      bool ok = true;
+      while (true) {
+        bool all = true;
+#pragma unroll
+        for (int k = 0; k < N - 1; ++k) {
+          const uint32_t off = my_slots + (uint32_t)k * slot_stride + u * kUnitStage;
+          if constexpr (kWire == kWireLL) {
+            const u32x4 line = ld16_coh(rs, off);
+            all &= (line[1] == e) & (line[3] == e);
+            d[k] = u32x2{line[0], line[2]};
+          } else {
+            d[k] = ld8_coh(rs, off);
+            all &= sentinel_ready8<kKind>(d[k]);
+          }
+        }
+        if (all) break;
+        if (spin.expired()) {
+          raise_status(ctrl, kStatusTimeout);
+          ok = false;
+          break;
+        }
+      }
+      if (!ok) {
+        dead = true;
+        continue;
+      }
+      if constexpr (kGather) {
+        // fragment k lands at k * blk: the own one at r, slot k's sender at
+        // k (k < r) or k + 1 (k >= r); the Sentinel wire canonicalises every
+        // fragment, the own one included, so all receivers agree
+        const u32x2 mine = (kWire == kWireSentinel) ? sentinel_canon8<kKind>(own) : own;
+        store8_at(out, (uint64_t)r * blk + (uint64_t)u * 8u, (uint64_t)(r + 1) * blk, aligned, mine);
+#pragma unroll
+        for (int k = 0; k < N - 1; ++k) {
+          const uint64_t s = (uint64_t)(k < r ? k : k + 1);
+          store8_at(out, s * blk + (uint64_t)u * 8u, (s + 1u) * blk, aligned, d[k]);
+        }
+      } else {
+        store8_at(out, (uint64_t)u * 8u, blk, aligned, reduce_unit_at<kKind, N>(own, r, d));
+      }
+      if constexpr (kWire == kWireSentinel) {
+        if (!keep) {
+#pragma unroll
+          for (int k = 0; k < N - 1; ++k)
+            st8_stage<kLocal>(rs, my_slots + (uint32_t)k * slot_stride + u * 8u, u32x2{0xFFFFFFFFu, 0xFFFFFFFFu});
+        }
+      }
+    }
+  }
+  wg_end(ctrl, st, host_epoch, grid, timing, idle);
+}
+
+template <int kKind, int N>
+hipError_t launch_multi_n(const LaunchSpec& ls, hipStream_t stream) {
+  const dim3 grid(ls.grid), block(ls.threads);
+  switch (ls.kernel) {
+    case kKernRsLL: hipLaunchKernelGGL((k_multi<kWireLL, kKind, N, false, false>), grid, block, 0, stream, ls.multi); break;
+    case kKernRsSentinel: hipLaunchKernelGGL((k_multi<kWireSentinel, kKind, N, false, false>), grid, block, 0, stream, ls.multi); break;
+    case kKernAgLL: hipLaunchKernelGGL((k_multi<kWireLL, kKind, N, true, false>), grid, block, 0, stream, ls.multi); break;
+    case kKernAgSentinel: hipLaunchKernelGGL((k_multi<kWireSentinel, kKind, N, true, false>), grid, block, 0, stream, ls.multi); break;
+    case kKernRsLLLocal: hipLaunchKernelGGL((k_multi<kWireLL, kKind, N, false, true>), grid, block, 0, stream, ls.multi); break;
+    case kKernRsSentinelLocal: hipLaunchKernelGGL((k_multi<kWireSentinel, kKind, N, false, true>), grid, block, 0, stream, ls.multi); break;
+    case kKernAgLLLocal: hipLaunchKernelGGL((k_multi<kWireLL, kKind, N, true, true>), grid, block, 0, stream, ls.multi); break;
+    case kKernAgSentinelLocal: hipLaunchKernelGGL((k_multi<kWireSentinel, kKind, N, true, true>), grid, block, 0, stream, ls.multi); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int kKind, int N>
+int occupancy_multi_n(int kernel, int threads) {
+  int blocks = 0;
+  hipError_t err = hipErrorInvalidValue;
+  switch (kernel) {
+    case kKernRsLL: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_multi<kWireLL, kKind, N, false, false>, threads, 0); break;
+    case kKernRsSentinel: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_multi<kWireSentinel, kKind, N, false, false>, threads, 0); break;
+    case kKernAgLL: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_multi<kWireLL, kKind, N, true, false>, threads, 0); break;
+    case kKernAgSentinel: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_multi<kWireSentinel, kKind, N, true, false>, threads, 0); break;
+    case kKernRsLLLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_multi<kWireLL, kKind, N, false, true>, threads, 0); break;
+    case kKernRsSentinelLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_multi<kWireSentinel, kKind, N, false, true>, threads, 0); break;
+    case kKernAgLLLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_multi<kWireLL, kKind, N, true, true>, threads, 0); break;
+    case kKernAgSentinelLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_multi<kWireSentinel, kKind, N, true, true>, threads, 0); break;
+    default: break;
+  }
+  return err == hipSuccess ? blocks : 0;
+}
+
+template <int kKind>
+hipError_t launch_multi_kind(const LaunchSpec& ls, hipStream_t stream) {
+  switch (ls.n_ranks) {
+    case 1: return launch_multi_n<kKind, 1>(ls, stream);
+    case 2: return launch_multi_n<kKind, 2>(ls, stream);
+    case 3: return launch_multi_n<kKind, 3>(ls, stream);
+    case 4: return launch_multi_n<kKind, 4>(ls, stream);
+    case 5: return launch_multi_n<kKind, 5>(ls, stream);
+    case 6: return launch_multi_n<kKind, 6>(ls, stream);
+    case 7: return launch_multi_n<kKind, 7>(ls, stream);
+    case 8: return launch_multi_n<kKind, 8>(ls, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int kKind>
+int occupancy_multi_kind(int n_ranks, int kernel, int threads) {
+  switch (n_ranks) {
+    case 1: return occupancy_multi_n<kKind, 1>(kernel, threads);
+    case 2: return occupancy_multi_n<kKind, 2>(kernel, threads);
+    case 3: return occupancy_multi_n<kKind, 3>(kernel, threads);
+    case 4: return occupancy_multi_n<kKind, 4>(kernel, threads);
+    case 5: return occupancy_multi_n<kKind, 5>(kernel, threads);
+    case 6: return occupancy_multi_n<kKind, 6>(kernel, threads);
+    case 7: return occupancy_multi_n<kKind, 7>(kernel, threads);
+    case 8: return occupancy_multi_n<kKind, 8>(kernel, threads);
+    default: return 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_multi(const LaunchSpec& ls, hipStream_t stream) {
+  switch (ls.kind) {
+    case kKindF32: return launch_multi_kind<kKindF32>(ls, stream);
+    case kKindF16: return launch_multi_kind<kKindF16>(ls, stream);
+    case kKindBF16: return launch_multi_kind<kKindBF16>(ls, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int occupancy_multi(int kind, int n_ranks, int kernel, int threads) {
+  switch (kind) {
+    case kKindF32: return occupancy_multi_kind<kKindF32>(n_ranks, kernel, threads);
+    case kKindF16: return occupancy_multi_kind<kKindF16>(n_ranks, kernel, threads);
+    case kKindBF16: return occupancy_multi_kind<kKindBF16>(n_ranks, kernel, threads);
+    default: return 0;
+  }
+}
+
+}  // namespace llar

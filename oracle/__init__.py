@@ -16,8 +16,11 @@ Contents
 * ``pyref.py``: a second, pure-Python implementation of the same definition
   that rounds by exact rational comparison (small cases only), used to pin the
   C code.
+* ``reduce_scatter``: segment j of the same sum for rank j (definition from
+  the yololab.net article's collective table).
 * ``models.py``: bit-level models of the LL line, the Sentinel buffer, the
-  LL128 atomic line and the double-buffer/credit schedule.
+  LL128 atomic line, the double-buffer/credit schedule, and what a receiver
+  gets over a wire (point-to-point and AllGather).
 
 dtype codes: ``F32 = 0``, ``F16 = 1``, ``BF16 = 2``.  Element arrays are
 passed as their bit patterns (``uint32`` for binary32, ``uint16`` otherwise).
@@ -106,6 +109,20 @@ def allreduce(partials: np.ndarray, dtype: int) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_allreduce rejected its arguments")
     return out
+
+
+def reduce_scatter(partials: np.ndarray, dtype: int) -> list:
+    """Rank j keeps segment j of the element-wise sum: the yololab.net article
+    on network architecture for LLM inference, table of its All-Reduce /
+    All-Gather / Reduce-Scatter section.  ``partials``: (N, N * c) bits;
+    returns N arrays of c output bits, segment j = elements [j c, (j+1) c)
+    summed like ``allreduce`` (binary64 in rank order, one rounding)."""
+    parts = np.ascontiguousarray(as_bits(np.asarray(partials), dtype))
+    n_ranks, n = parts.shape
+    if n % n_ranks:
+        raise ValueError("each partial must hold N equal segments")
+    c = n // n_ranks
+    return [allreduce(parts[:, j * c:(j + 1) * c], dtype) for j in range(n_ranks)]
 
 
 def sum_f64(partials: np.ndarray, dtype: int) -> np.ndarray:

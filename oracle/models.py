@@ -133,6 +133,15 @@ def p2p_transfer(send_bits: np.ndarray, dtype: int, wire: str, epoch: int = 1) -
     raise ValueError("unknown wire %r" % (wire,))
 
 
+def all_gather(fragments, dtype: int, wire: str) -> np.ndarray:
+    """What every receiving rank of an AllGather holds: all ranks' fragments
+    back to back in rank order (the yololab.net article's collective table:
+    every rank collects every rank's piece), each as it arrives over the wire
+    (``p2p_transfer``); the receiver treats its own fragment the same way so
+    that every copy agrees."""
+    return np.concatenate([p2p_transfer(f, dtype, wire) for f in fragments])
+
+
 # ----------------------------------------------------------------------------
 # LL128 atomic two-shot
 # ----------------------------------------------------------------------------

@@ -187,6 +187,56 @@ def test_p2p_equals_a_two_rank_sum_with_negative_zero(dt, wire):
     assert oracle.same_result(got, want, dt).all()
 
 
+# --------------------------------------------------------------------------- ReduceScatter / AllGather
+@pytest.mark.parametrize("dt", [F32, F16, BF16])
+def test_reduce_scatter_segments_tile_the_allreduce(dt):
+    # the N segments, back to back, are the AllReduce of the whole message
+    g = np.random.default_rng(60 + dt)
+    for n_ranks, c in [(1, 5), (3, 7), (8, 129)]:
+        bits = oracle.round_to(g.standard_normal((n_ranks, n_ranks * c)) * 8.0, dt)
+        segs = oracle.reduce_scatter(bits, dt)
+        assert len(segs) == n_ranks and all(s.size == c for s in segs)
+        assert oracle.same_result(np.concatenate(segs), oracle.allreduce(bits, dt), dt).all()
+
+
+def test_reduce_scatter_brute_force_against_pure_python():
+    # tiny case, element by element with the pure-Python rational rounding
+    from oracle import pyref
+    g = np.random.default_rng(61)
+    for dt in (F32, F16, BF16):
+        bits = oracle.round_to(g.standard_normal((3, 6)) * 1e3, dt)
+        segs = oracle.reduce_scatter(bits, dt)
+        for j in range(3):
+            cols = [[int(bits[r, 2 * j + i]) for i in range(2)] for r in range(3)]
+            assert [int(x) for x in segs[j]] == pyref.allreduce(cols, dt)
+
+
+def test_reduce_scatter_keeps_the_right_segment():
+    # rank r holds r+1 in segment j = r only: segment j sums to j+1
+    n_ranks, c = 4, 3
+    parts = np.zeros((n_ranks, n_ranks * c), np.float32)
+    for r in range(n_ranks):
+        parts[r, r * c:(r + 1) * c] = r + 1
+    segs = oracle.reduce_scatter(oracle.as_bits(parts, F32), F32)
+    for j in range(n_ranks):
+        assert (oracle.decode(segs[j], F32) == j + 1).all()
+    with pytest.raises(ValueError):
+        oracle.reduce_scatter(np.zeros((3, 7), np.uint32), F32)
+
+
+@pytest.mark.parametrize("dt", [F32, F16, BF16])
+def test_all_gather_rebuilds_the_sharded_tensor(dt):
+    g = np.random.default_rng(62 + dt)
+    nb = 32 if dt == F32 else 16
+    full = g.integers(0, 2**nb, size=8 * 37, dtype=np.uint64).astype(oracle.BITS_DTYPE[dt])
+    frags = np.split(full, 8)
+    assert np.array_equal(models.all_gather(frags, dt, "ll"), full)
+    got = models.all_gather(frags, dt, "sentinel")
+    s = models.SENTINEL_BITS[dt]
+    assert np.array_equal(got[full != s], full[full != s]) and not (got == s).any()
+    assert oracle.is_nan_bits(got[full == s], dt).all()
+
+
 # --------------------------------------------------------------------------- LL128
 def test_ll128_lane_grouping_matches_page(pages):
     p = pages["ll128"]
