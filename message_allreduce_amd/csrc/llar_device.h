@@ -22,79 +22,47 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "llar_wire.h"
+
 namespace llar {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x2 __attribute__((ext_vector_type(2)));
+// The staging primitives are those of the public device-side header: the
+// kernels below are written with the same building blocks that custom
+// kernels use.
+using llar_wire::s16x2;
+using llar_wire::u32x2;
+using llar_wire::u32x4;
+using llar_wire::kCpolNone;
+using llar_wire::kCpolNt;
+using llar_wire::kCpolSc0;
+using llar_wire::kCpolSc1;
+using llar_wire::ld16_coh;
+using llar_wire::ld4_coh;
+using llar_wire::ld8_coh;
+using llar_wire::make_rsrc;
+using llar_wire::sentinel_is_empty;
+using llar_wire::st16_coh;
+using llar_wire::st16_l2;
+using llar_wire::wall_ticks;
+template <int kSleep>
+using SpinT = llar_wire::PollT<kSleep>;
+using Spin = llar_wire::Poll;          // latency-critical polls
+using SpinBulk = llar_wire::PollBulk;  // polls of the bandwidth pipeline
 
-// gfx950 cache-policy bits of vector memory instructions
-constexpr int kCpolNone = 0;
-constexpr int kCpolSc0 = 1;
-constexpr int kCpolNt = 2;
-constexpr int kCpolSc1 = 16;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // The inputs are uniform, but after divergent code (a thread-0 branch) the
-  // compiler may no longer prove it; a descriptor it believes divergent is
-  // kept in VGPRs and every buffer access becomes a readfirstlane loop, which
-  // also hides the memory counters from its wait analysis.  readfirstlane
-  // states the uniformity outright.
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-  void* const ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  // word3 0x00020000: raw (untyped) 32-bit data format for gfx9-family buffers
-  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)n, 0x00020000);
-}
-
-// ---- coherent accesses to staging -------------------------------------------
-// The buffer-load intrinsics are "read-only memory" to the compiler: inside a
-// polling loop with no store it may hoist the load out of the loop, or delete
-// a loop it cannot prove to terminate.  The empty volatile asm with a memory
-// clobber in front of every coherent load is a side effect that forces a
-// fresh load on each iteration (loads issued back to back still overlap).
-__device__ __forceinline__ u32x4 ld16_coh(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  asm volatile("" ::: "memory");
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1);
-}
-__device__ __forceinline__ u32x2 ld8_coh(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  asm volatile("" ::: "memory");
-  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolSc1);
-}
-__device__ __forceinline__ uint32_t ld4_coh(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  asm volatile("" ::: "memory");
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCpolSc1);
-}
-__device__ __forceinline__ void st16_coh(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolSc1);
-}
-__device__ __forceinline__ void st16_l2(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolNone);
-}
+// Placement-scoped staging stores: plain stores when every reader shares the
+// writer's XCD (local placement), device-coherent ones otherwise.
+constexpr llar_wire::Scope scope_of(bool local) { return local ? llar_wire::kXcd : llar_wire::kDevice; }
 template <bool kLocal>
 __device__ __forceinline__ void st16_stage(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
-  if constexpr (kLocal) st16_l2(r, off, v);
-  else st16_coh(r, off, v);
+  llar_wire::store16<scope_of(kLocal)>(r, off, v);
 }
 template <bool kLocal>
 __device__ __forceinline__ void st8_stage(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
-  if constexpr (kLocal) __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpolNone);
-  else __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpolSc1);
+  llar_wire::store8<scope_of(kLocal)>(r, off, v);
 }
-
-// ---- ordering -----------------------------------------------------------------
-// Wait until every vector memory operation of this wave has completed; the
-// signal fences keep the compiler from moving memory operations across it.
-__device__ __forceinline__ void drain_vm() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
+__device__ __forceinline__ void drain_vm() { llar_wire::release(); }
 
 // ---- clocks and ids -------------------------------------------------------------
-__device__ __forceinline__ uint64_t wall_ticks() { return (uint64_t)wall_clock64(); }
 __device__ __forceinline__ uint32_t xcc_id() {
   // HW register XCC_ID (20), bits 3:0
   return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xFu;
@@ -178,51 +146,18 @@ __device__ __forceinline__ void vec_set(u32x4& v, int k, uint32_t bits) {
   }
 }
 
-// Sentinel: the all-ones pattern (a negative NaN in all three formats).  A
-// datum equal to it is replaced by the pattern one below (still a negative
-// NaN), so the staged data can never look like an empty slot.
+// Sentinel helpers keyed by element kind (the wire's own are keyed by width).
 template <int kKind>
 __device__ __forceinline__ u32x4 sentinel_canon(u32x4 v) {
-  if constexpr (Elem<kKind>::kBytes == 4) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (v[i] == 0xFFFFFFFFu) ? 0xFFFFFFFEu : v[i];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t w = v[i];
-      if ((w & 0xFFFFu) == 0xFFFFu) w -= 1u;
-      if ((w >> 16) == 0xFFFFu) w -= 0x10000u;
-      v[i] = w;
-    }
-  }
-  return v;
+  return llar_wire::sentinel_canon<Elem<kKind>::kBytes>(v);
 }
-// true when the whole 16-byte slot holds the sentinel (a consumer's reset
-// has fully landed); a slot that is partly reset is not empty yet
-__device__ __forceinline__ bool sentinel_is_empty(const u32x4& v) {
-  return (v[0] & v[1] & v[2] & v[3]) == 0xFFFFFFFFu;
-}
-// true when no element of the 8-byte unit still holds the sentinel
 template <int kKind>
 __device__ __forceinline__ bool sentinel_ready8(const u32x2& v) {
-  if constexpr (Elem<kKind>::kBytes == 4) {
-    return (v[0] != 0xFFFFFFFFu) & (v[1] != 0xFFFFFFFFu);
-  } else {
-    return ((v[0] & 0xFFFFu) != 0xFFFFu) & ((v[0] >> 16) != 0xFFFFu) & ((v[1] & 0xFFFFu) != 0xFFFFu) &
-           ((v[1] >> 16) != 0xFFFFu);
-  }
+  return llar_wire::sentinel_ready8<Elem<kKind>::kBytes>(v);
 }
-// true when no element of the vector still holds the sentinel
 template <int kKind>
 __device__ __forceinline__ bool sentinel_ready(const u32x4& v) {
-  if constexpr (Elem<kKind>::kBytes == 4) {
-    return (v[0] != 0xFFFFFFFFu) & (v[1] != 0xFFFFFFFFu) & (v[2] != 0xFFFFFFFFu) & (v[3] != 0xFFFFFFFFu);
-  } else {
-    bool ok = true;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ok &= ((v[i] & 0xFFFFu) != 0xFFFFu) & ((v[i] >> 16) != 0xFFFFu);
-    return ok;
-  }
+  return llar_wire::sentinel_ready<Elem<kKind>::kBytes>(v);
 }
 
 // ---- device control block --------------------------------------------------------------
@@ -259,24 +194,6 @@ __host__ __device__ __forceinline__ uint32_t next_host_epoch(uint32_t e) {
 __host__ __device__ __forceinline__ uint32_t next_device_epoch(uint32_t e) {
   return 0x80000000u | next_host_epoch(e & 0x7FFFFFFFu);
 }
-
-// Bounded poll helper.  expired() is called after every failed poll: it
-// backs off for kSleep x 64 cycles (s_sleep), so that waiting waves do not
-// flood the L2 with re-polls that the producers' traffic has to queue
-// behind, and every 16th call checks the wall-clock limit.
-template <int kSleep>
-struct SpinT {
-  uint64_t t0, limit;
-  uint32_t n;
-  __device__ __forceinline__ SpinT(uint64_t lim) : t0(wall_ticks()), limit(lim), n(0) {}
-  __device__ __forceinline__ bool expired() {
-    if constexpr (kSleep > 0) __builtin_amdgcn_s_sleep(kSleep);
-    if ((++n & 15u) != 0u) return false;
-    return wall_ticks() - t0 > limit;
-  }
-};
-using Spin = SpinT<1>;       // latency-critical polls (about 27 ns back-off)
-using SpinBulk = SpinT<8>;   // polls of the bandwidth pipeline (about 210 ns)
 
 __device__ __forceinline__ void raise_status(Ctrl* c, uint32_t bits) {
   __hip_atomic_fetch_or(&c->status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

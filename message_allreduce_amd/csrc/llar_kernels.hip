@@ -202,12 +202,8 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
       u32x4 x = (v == v0 + threadIdx.x) ? first_vec : load_vec<false>(src, v, nbytes);
       if (v == v0) trace_at(trace, 2, true);
       uint32_t off = base + v * kVecStage;
-      if constexpr (kWire == kWireLL) {
-        st16_stage<kLocal>(rs, off, u32x4{x[0], e, x[1], e});
-        st16_stage<kLocal>(rs, off + 16u, u32x4{x[2], e, x[3], e});
-      } else {
-        st16_stage<kLocal>(rs, off, sentinel_canon<kKind>(x));
-      }
+      if constexpr (kWire == kWireLL) llar_wire::ll_put16<scope_of(kLocal)>(rs, off, x, e);
+      else llar_wire::sentinel_put<Elem<kKind>::kBytes, scope_of(kLocal)>(rs, off, x);
       if (v == v0) trace_at(trace, 3, true);
     }
   } else if (consumer) {
@@ -229,14 +225,8 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
 #pragma unroll
         for (int k = 0; k < N - 1; ++k) {
           uint32_t off = par_off + (uint32_t)k * rank_stride + u * kUnitStage;
-          if constexpr (kWire == kWireLL) {
-            u32x4 line = ld16_coh(rs, off);
-            all &= (line[1] == e) & (line[3] == e);
-            d[k] = u32x2{line[0], line[2]};
-          } else {
-            d[k] = ld8_coh(rs, off);
-            all &= sentinel_ready8<kKind>(d[k]);
-          }
+          if constexpr (kWire == kWireLL) all &= llar_wire::ll_try(rs, off, e, d[k]);
+          else all &= llar_wire::sentinel_try8<Elem<kKind>::kBytes>(rs, off, d[k]);
         }
         if (all) break;
         if (spin.expired()) {
@@ -257,7 +247,7 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
         if (!keep) {
 #pragma unroll
           for (int k = 0; k < N - 1; ++k)
-            st8_stage<kLocal>(rs, par_off + (uint32_t)k * rank_stride + u * 8u, u32x2{0xFFFFFFFFu, 0xFFFFFFFFu});
+            llar_wire::sentinel_reset8<scope_of(kLocal)>(rs, par_off + (uint32_t)k * rank_stride + u * 8u);
         }
       }
     }
@@ -358,7 +348,7 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
             float val;
             if constexpr (E::kBytes == 4) val = __uint_as_float(reinterpret_cast<const uint32_t*>(src)[cbase + e_idx]);
             else val = E::to_f32(reinterpret_cast<const uint16_t*>(src)[cbase + e_idx]);
-            __hip_atomic_fetch_add(reinterpret_cast<float*>(a.stage + off), val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            llar_wire::ll128_add(reinterpret_cast<float*>(a.stage + off), val);
           } else {
             // two 16-bit slots per dword: slots 2q and 2q+1
             uint32_t lo = 0u, hi = 0u;
@@ -370,12 +360,7 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
             uint32_t e1 = line * K + s1 - 1u;
             if (e1 < len) hi = reinterpret_cast<const uint16_t*>(src)[cbase + e1];
             if ((lo | hi) == 0u) continue;  // nothing to add (both +0)
-            s16x2 v = {(short)lo, (short)hi};
-            if constexpr (kKind == kKindBF16)
-              __builtin_amdgcn_global_atomic_fadd_v2bf16(reinterpret_cast<s16x2*>(a.stage + off), v);
-            else
-              __builtin_amdgcn_global_atomic_fadd_v2f16(reinterpret_cast<_Float16 __attribute__((ext_vector_type(2)))*>(a.stage + off),
-                                                       __builtin_bit_cast(_Float16 __attribute__((ext_vector_type(2))), v));
+            llar_wire::ll128_add2<kKind == kKindBF16>(a.stage + off, s16x2{(short)lo, (short)hi});
           }
         }
       }
@@ -391,14 +376,9 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
         if (lane < 8u && line < l1) {
           uint32_t off = poff + line * 128u;
           if constexpr (!kAcc16) {
-            __hip_atomic_fetch_add(reinterpret_cast<float*>(a.stage + off), 1.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            llar_wire::ll128_flag(reinterpret_cast<float*>(a.stage + off));
           } else {
-            s16x2 v = {(short)E::from_f32(1.0f), (short)0};
-            if constexpr (kKind == kKindBF16)
-              __builtin_amdgcn_global_atomic_fadd_v2bf16(reinterpret_cast<s16x2*>(a.stage + off), v);
-            else
-              __builtin_amdgcn_global_atomic_fadd_v2f16(reinterpret_cast<_Float16 __attribute__((ext_vector_type(2)))*>(a.stage + off),
-                                                       __builtin_bit_cast(_Float16 __attribute__((ext_vector_type(2))), v));
+            llar_wire::ll128_flag2<kKind == kKindBF16>(a.stage + off, E::from_f32(1.0f));
           }
         }
       }
@@ -415,22 +395,12 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
         if (line >= l1) continue;
         uint32_t loff = poff + line * 128u;
         Spin spin(a.spin_limit);
-        bool ok = true;
-        while (true) {
-          uint32_t f = ld4_coh(rs, loff);
-          if constexpr (kAcc16) f &= 0xFFFFu;
-          if (f == flag_full) break;
-          if (spin.expired()) {
-            raise_status(a.ctrl, kStatusTimeout);
-            ok = false;
-            break;
-          }
-        }
-        if (!ok) {
+        if (!llar_wire::ll128_wait<kAcc16 != 0>(rs, loff, flag_full, spin)) {
+          raise_status(a.ctrl, kStatusTimeout);
           dead = true;
           break;
         }
-        u32x4 v = ld16_coh(rs, loff + j * 16u);
+        u32x4 v = llar_wire::ll128_read16(rs, loff + j * 16u);
         if constexpr (!kAcc16) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
@@ -451,7 +421,7 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
             reinterpret_cast<uint16_t*>(a.out)[cbase + e_idx] = (uint16_t)(v[t >> 1] >> ((t & 1) * 16));
           }
         }
-        if (!a.keep) st16_coh(rs, loff + j * 16u, u32x4{0u, 0u, 0u, 0u});
+        if (!a.keep) llar_wire::ll128_reset16(rs, loff + j * 16u);
       }
     }
     // every wave's zeroing stores are acknowledged before any wave of this

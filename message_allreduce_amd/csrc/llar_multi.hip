@@ -139,12 +139,8 @@ __global__ void __launch_bounds__(512) k_multi(MultiArgs a) {
         const u32x4 y = x[kGather ? 0 : j];
         const uint32_t slot = (uint32_t)j * (uint32_t)(N - 1) + (uint32_t)(r < j ? r : r - 1);
         const uint32_t off = par_off + slot * slot_stride + v * kVecStage;
-        if constexpr (kWire == kWireLL) {
-          st16_stage<kLocal>(rs, off, u32x4{y[0], e, y[1], e});
-          st16_stage<kLocal>(rs, off + 16u, u32x4{y[2], e, y[3], e});
-        } else {
-          st16_stage<kLocal>(rs, off, sentinel_canon<kKind>(y));
-        }
+        if constexpr (kWire == kWireLL) llar_wire::ll_put16<scope_of(kLocal)>(rs, off, y, e);
+        else llar_wire::sentinel_put<Elem<kKind>::kBytes, scope_of(kLocal)>(rs, off, y);
       }
     }
   }
@@ -165,14 +161,8 @@ __global__ void __launch_bounds__(512) k_multi(MultiArgs a) {
 #pragma unroll
         for (int k = 0; k < N - 1; ++k) {
           const uint32_t off = my_slots + (uint32_t)k * slot_stride + u * kUnitStage;
-          if constexpr (kWire == kWireLL) {
-            const u32x4 line = ld16_coh(rs, off);
-            all &= (line[1] == e) & (line[3] == e);
-            d[k] = u32x2{line[0], line[2]};
-          } else {
-            d[k] = ld8_coh(rs, off);
-            all &= sentinel_ready8<kKind>(d[k]);
-          }
+          if constexpr (kWire == kWireLL) all &= llar_wire::ll_try(rs, off, e, d[k]);
+          else all &= llar_wire::sentinel_try8<Elem<kKind>::kBytes>(rs, off, d[k]);
         }
         if (all) break;
         if (spin.expired()) {
@@ -203,7 +193,7 @@ __global__ void __launch_bounds__(512) k_multi(MultiArgs a) {
         if (!keep) {
 #pragma unroll
           for (int k = 0; k < N - 1; ++k)
-            st8_stage<kLocal>(rs, my_slots + (uint32_t)k * slot_stride + u * 8u, u32x2{0xFFFFFFFFu, 0xFFFFFFFFu});
+            llar_wire::sentinel_reset8<scope_of(kLocal)>(rs, my_slots + (uint32_t)k * slot_stride + u * 8u);
         }
       }
     }

@@ -89,3 +89,31 @@ def test_package_has_no_cpu_fallback():
                 src = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src, f
                 assert "oracle/" not in src, f
+
+
+def test_device_header_is_self_contained_and_demo_exports():
+    """include/llar_wire.h compiles on its own for gfx950, and the demo
+    library written against it exports its launchers."""
+    import shutil
+    import subprocess
+    import tempfile
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.hip")
+        with open(src, "w") as f:
+            f.write('#include "llar_wire.h"\n'
+                    '__global__ void k(uint8_t* s, uint32_t e) {\n'
+                    '  llar_wire::Wire w = llar_wire::make_wire(s, 4096);\n'
+                    '  llar_wire::ll_put<llar_wire::kDevice>(w, 0, llar_wire::u32x2{1u, 2u}, e);\n'
+                    '  llar_wire::sentinel_put<2, llar_wire::kXcd>(w, 16, llar_wire::u32x4{0u, 0u, 0u, 0u});\n'
+                    '}\n')
+        res = subprocess.run([hipcc, "--offload-arch=gfx950", "--cuda-device-only", "-fsyntax-only", "-std=c++17",
+                              "-I", os.path.join(root, "include"), src], capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr[-2000:]
+    lib = os.path.join(root, "tests", "device_api", "libwire_demo.so")
+    assert os.path.exists(lib), "run __graft_entry__.build()"
+    L = ctypes.CDLL(lib)
+    for name in ("demo_scaled_allreduce_ll", "demo_sentinel_chain", "demo_ll128_reduce"):
+        assert hasattr(L, name)
+
