@@ -13,6 +13,10 @@ Default run (one JSON line on stdout):
     algorithmic bytes (N + 1) x 64 MiB, and the HBM roofline of that kernel;
   * cpu_baseline: the CPU oracle on the same 16 KiB workload.
 
+  * rows: point-to-point send/recv (8 KB fp16) and ReduceScatter /
+    AllGather (N = 8, 16 KiB bf16) per call from graph replay, and
+    device-side.
+
 --sweep adds the 128 B .. 64 MiB size sweep for every protocol and the
 alpha + beta * size fit (written to --sweep-out).
 """
@@ -112,6 +116,101 @@ def time_graph(comm, parts, out, proto, steps, stream, per_graph=100):
         raise RuntimeError("device status %d (bits %#x) during graph replay of %s" % (st, bits, proto))
     del g
     return a.elapsed_time(b) * 1e3 / (reps * per_graph)
+
+
+def time_graph_fn(fn, steps, stream, per_graph=100):
+    """Per-call microseconds of `fn` (one library call on `stream`) from
+    replays of a HIP graph of `per_graph` captured calls: GPU time only, no
+    Python call overhead."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(per_graph):
+                fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // per_graph)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) * 1e3 / (reps * per_graph)
+
+
+def device_side_fn(comm, fn, calls, stream):
+    """Median and minimum device-side microseconds of `fn` (first workgroup
+    start to last workgroup end) over `calls` calls."""
+    import torch
+    import message_allreduce_amd as llar
+    calls = min(calls, 60)
+    comm.set_option("timing", 1)
+    try:
+        with torch.cuda.stream(stream):
+            for _ in range(calls):
+                fn()
+        torch.cuda.synchronize()
+        recs = comm.timing(calls)
+    finally:
+        comm.set_option("timing", 0)
+    hz = llar.llar_wallclock_hz()
+    d = sorted((t1 - t0) / hz * 1e6 for t0, t1 in recs if t1 > t0)
+    return statistics.median(d), d[0]
+
+
+def measure_rows(stream, steps):
+    """The other collectives at the shapes the pages give them: point-to-point
+    send/recv of one token's 4096 x fp16 hidden state (8 KB) between two
+    pipeline stages, and ReduceScatter / AllGather of the N = 8, 16 KiB bf16
+    tensor-parallel hidden state (2 KiB segments)."""
+    import torch
+    import message_allreduce_amd as llar
+    rows = {}
+    c2 = llar.Communicator(2, torch.float16, 8192)
+    try:
+        send = torch.randn(4096, dtype=torch.float16, device="cuda")
+        recv = torch.empty_like(send)
+        for wire in ("ll", "sentinel"):
+            fn = (lambda w=wire: c2.send_recv(send, recv, w, stream=stream))
+            us = time_graph_fn(fn, steps, stream)
+            dmed, dmin = device_side_fn(c2, fn, 60, stream)
+            rows["send_recv_8KB_fp16_" + wire] = {"us_per_call_graph": round(us, 3), "device_us_median": round(dmed, 3),
+                                                  "device_us_min": round(dmin, 3)}
+            log("send/recv 8 KB fp16 %s: %.3f us per call (graph), device %.3f us" % (wire, us, dmed))
+        st, bits = c2.device_status()
+        if st != 0:
+            raise RuntimeError("device status %d (bits %#x) in send/recv timing" % (st, bits))
+    finally:
+        c2.close()
+    c8 = llar.Communicator(N_RANKS, torch.bfloat16, SMALL_BYTES)
+    try:
+        n = SMALL_BYTES // 2
+        cnt = n // N_RANKS
+        _, parts = device_inputs(5, N_RANKS, n, "normal", 1.0)
+        segs = [torch.empty(cnt, dtype=torch.bfloat16, device="cuda") for _ in range(N_RANKS)]
+        full = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(N_RANKS)]
+        for wire in ("ll", "sentinel"):
+            for name, fn in (("reduce_scatter", lambda w=wire: c8.reduce_scatter(parts, segs, w, stream=stream)),
+                             ("all_gather", lambda w=wire: c8.all_gather(segs, full, w, stream=stream))):
+                us = time_graph_fn(fn, steps, stream)
+                dmed, dmin = device_side_fn(c8, fn, 60, stream)
+                rows["%s_16KiB_x8_bf16_%s" % (name, wire)] = {"us_per_call_graph": round(us, 3),
+                                                               "device_us_median": round(dmed, 3),
+                                                               "device_us_min": round(dmin, 3)}
+                log("%s 16 KiB x 8 bf16 %s: %.3f us per call (graph), device %.3f us" % (name, wire, us, dmed))
+        st, bits = c8.device_status()
+        if st != 0:
+            raise RuntimeError("device status %d (bits %#x) in collective timing" % (st, bits))
+    finally:
+        c8.close()
+    return rows
 
 
 def profiled_traffic(kernel_file, name):
@@ -239,6 +338,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="skip the send/recv, ReduceScatter, AllGather timings")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--sweep-out", default=os.path.join(ROOT, "gpurun_out", "sweep.json"))
     args = ap.parse_args()
@@ -327,6 +427,9 @@ def main():
                      "traffic": None if traffic is None else int(traffic),
                      "kernel": "%s, 64 MiB x 8 bf16" % PROTO_NAMES[proto_big]},
     }
+    if not args.no_rows:
+        log("other collectives")
+        result["rows"] = measure_rows(stream, min(args.steps, 1000))
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
