@@ -9,9 +9,9 @@
 // Microsecond Matters" (agihunt.info summary, two-shot LL128 paragraph).
 //
 // One launch, every rank both sends and receives.  Workgroup (rank r,
-// slice w) first puts slice w of each of its blocks into the staging slot
-// the receiving rank reads (no wait: producers never block), then polls its
-// own N-1 slots for slice w and writes its output.  The wires are those of
+// slice w) first puts slice w of its block for each receiving rank into the
+// staging slot that rank reads (no wait: producers never block), then polls
+// its own N-1 slots for slice w and writes its output.  The wires are those of
 // the one-shot AllReduce: LL lines {data0, epoch, data1, epoch} (LL
 // paragraph), or a Sentinel-prefilled slot that the receiver resets after
 // use (Sentinel paragraph).  Every workgroup of the grid is resident at once
@@ -123,25 +123,21 @@ __global__ void __launch_bounds__(512) k_multi(MultiArgs a) {
   constexpr uint32_t kUnitStage = (kWire == kWireLL) ? 16u : 8u;
 
   // ---- send: slice w of this rank's block for every receiver -----------------
+  // Work items are (receiver, vector) pairs, receiver-major, so that a small
+  // slice still spreads over the whole workgroup.  The p-th receiver other
+  // than this rank is p (p < r) or p + 1.
   if (!idle && (uint32_t)r != drop_rank) {
-    for (uint32_t v = v0 + threadIdx.x; v < v1; v += blockDim.x) {
-      // every load first, then every store
-      u32x4 x[kGather ? 1 : N];
-#pragma unroll
-      for (int j = 0; j < (kGather ? 1 : N); ++j) {
-        const uint64_t base = kGather ? 0u : (uint64_t)j * blk;
-        const bool wanted = kGather || (j != r && (uint32_t)j < n_recv);
-        x[j] = wanted ? load16_at(src, base + (uint64_t)v * 16u, base + blk, aligned) : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int j = 0; j < N; ++j) {
-        if (j == r || (uint32_t)j >= n_recv) continue;
-        const u32x4 y = x[kGather ? 0 : j];
-        const uint32_t slot = (uint32_t)j * (uint32_t)(N - 1) + (uint32_t)(r < j ? r : r - 1);
-        const uint32_t off = par_off + slot * slot_stride + v * kVecStage;
-        if constexpr (kWire == kWireLL) llar_wire::ll_put16<scope_of(kLocal)>(rs, off, y, e);
-        else llar_wire::sentinel_put<Elem<kKind>::kBytes, scope_of(kLocal)>(rs, off, y);
-      }
+    const uint32_t span = v1 - v0;
+    const uint32_t n_peers = (uint32_t)r < n_recv ? n_recv - 1u : n_recv;
+    for (uint32_t it = threadIdx.x; it < n_peers * span; it += blockDim.x) {
+      const uint32_t p = it / span, v = v0 + (it - p * span);
+      const uint32_t j = p < (uint32_t)r ? p : p + 1u;
+      const uint64_t base = kGather ? 0u : (uint64_t)j * blk;
+      const u32x4 y = load16_at(src, base + (uint64_t)v * 16u, base + blk, aligned);
+      const uint32_t slot = j * (uint32_t)(N - 1) + ((uint32_t)r < j ? (uint32_t)r : (uint32_t)r - 1u);
+      const uint32_t off = par_off + slot * slot_stride + v * kVecStage;
+      if constexpr (kWire == kWireLL) llar_wire::ll_put16<scope_of(kLocal)>(rs, off, y, e);
+      else llar_wire::sentinel_put<Elem<kKind>::kBytes, scope_of(kLocal)>(rs, off, y);
     }
   }
 
