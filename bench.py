@@ -13,9 +13,9 @@ Default run (one JSON line on stdout):
     algorithmic bytes (N + 1) x 64 MiB, and the HBM roofline of that kernel;
   * cpu_baseline: the CPU oracle on the same 16 KiB workload.
 
-  * rows: point-to-point send/recv (8 KB fp16) and ReduceScatter /
-    AllGather (N = 8, 16 KiB bf16) per call from graph replay, and
-    device-side.
+  * rows: point-to-point send/recv (8 KB fp16) and ReduceScatter (LL,
+    Sentinel, LL128 atomic) / AllGather (LL, Sentinel) at N = 8, 16 KiB
+    bf16, per call from graph replay, and device-side.
 
 --sweep adds the 128 B .. 64 MiB size sweep for every protocol and the
 alpha + beta * size fit (written to --sweep-out).
@@ -196,9 +196,11 @@ def measure_rows(stream, steps):
         _, parts = device_inputs(5, N_RANKS, n, "normal", 1.0)
         segs = [torch.empty(cnt, dtype=torch.bfloat16, device="cuda") for _ in range(N_RANKS)]
         full = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(N_RANKS)]
-        for wire in ("ll", "sentinel"):
-            for name, fn in (("reduce_scatter", lambda w=wire: c8.reduce_scatter(parts, segs, w, stream=stream)),
-                             ("all_gather", lambda w=wire: c8.all_gather(segs, full, w, stream=stream))):
+        for wire in ("ll", "sentinel", "ll128"):
+            calls = [("reduce_scatter", lambda w=wire: c8.reduce_scatter(parts, segs, w, stream=stream))]
+            if wire != "ll128":  # nothing to sum in an AllGather
+                calls.append(("all_gather", lambda w=wire: c8.all_gather(segs, full, w, stream=stream)))
+            for name, fn in calls:
                 us = time_graph_fn(fn, steps, stream)
                 dmed, dmin = device_side_fn(c8, fn, 60, stream)
                 rows["%s_16KiB_x8_bf16_%s" % (name, wire)] = {"us_per_call_graph": round(us, 3),

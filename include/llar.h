@@ -140,9 +140,15 @@ int llar_send_recv(llar_comm* h, const void* send_buf, void* recv_buf, size_t n_
  * binary64 in rank order with one rounding (deterministic, the same
  * arithmetic as the LL and Sentinel AllReduce).
  * protocol: LLAR_LL, LLAR_SENTINEL or LLAR_AUTO (LL while N * recv_count *
- *   sizeof(dtype) is within the "thr_sentinel" size); others: LLAR_ERR_ARG.
+ *   sizeof(dtype) is within the "thr_sentinel" size), or LLAR_LL128: the
+ *   reduce-scatter half of the two-shot LL128 AllReduce -- every rank
+ *   atomically adds its copy of segment j into rank j's 128-byte lines
+ *   (slot 0 counts contributions up to N) and rank j rounds what the lines
+ *   hold, in an unspecified order (non-deterministic; binary32 staging, or
+ *   16-bit with the "ll128_acc" option).  Others: LLAR_ERR_ARG.
  * Limits: N * recv_count * sizeof(dtype) <= max_bytes (else LLAR_ERR_ARG),
- *   and <= 8 MiB (LL) or 16 MiB (Sentinel) (else LLAR_ERR_UNSUPPORTED).
+ *   and <= 8 MiB (LL) or 16 MiB (Sentinel, LL128) (else
+ *   LLAR_ERR_UNSUPPORTED).
  *   recv_count need not be a multiple of 16 bytes.  recv_count == 0 is a
  *   no-op.  Pointers 16-byte aligned.  Errors, epochs and stream rules are
  *   those of llar_allreduce, whose staging and epoch this call shares. */
@@ -163,7 +169,8 @@ int llar_reduce_scatter(llar_comm* h, const void* const* partials, void* const* 
  *   carry its all-ones pattern, which arrives as the pattern one below (a
  *   negative NaN still); the receiver applies the same to its own fragment,
  *   so every copy is identical.
- * protocol, limits (N * send_count * sizeof(dtype)), errors and streams as
+ * protocol: LLAR_LL, LLAR_SENTINEL or LLAR_AUTO (no LLAR_LL128: nothing is
+ *   summed); limits (N * send_count * sizeof(dtype)), errors and streams as
  *   for llar_reduce_scatter. */
 int llar_all_gather(llar_comm* h, const void* const* inputs, void* const* outs, int n_outs, size_t send_count,
                     llar_dtype dtype, llar_protocol protocol, void* stream);

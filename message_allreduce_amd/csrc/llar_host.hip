@@ -356,7 +356,9 @@ llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes) {
   h->sent.rank_stride = s_vec * 16;
   h->sent.parity_stride = h->sent.rank_stride * (size_t)std::max(N - 1, 1);
   // LL128 one round: [parity][line] 128 B, binary32 staging needs the most lines
-  size_t l_one = ceil_div(std::min(mb, kCapLL128) / h->elem, 31) + 1;
+  // (N spare lines: the N segments of a ReduceScatter, each rounded up to
+  // whole lines, fit)
+  size_t l_one = ceil_div(std::min(mb, kCapLL128) / h->elem, 31) + 1 + (size_t)N;
   h->ll128.parity_stride = l_one * 128;
   // LL128 pipelined: [parity][line] for the largest chunk
   const size_t chunk_cap = std::max(std::min(ceil_div(mb, 16) * 16, kCapChunk), (size_t)1024);
@@ -603,7 +605,8 @@ int run_multi(llar_comm* h, const void* const* ins, void* const* outs, int n_rec
   if ((int)dtype != h->kind) return fail(LLAR_ERR_ARG);
   const int N = h->n_ranks;
   if (n_recv != N && !(gather && n_recv == 1)) return fail(LLAR_ERR_ARG);
-  if (protocol != LLAR_AUTO && protocol != LLAR_LL && protocol != LLAR_SENTINEL) return fail(LLAR_ERR_ARG);
+  const bool atomic = (protocol == LLAR_LL128 && !gather);  // the reduce-scatter half of the two-shot
+  if (protocol != LLAR_AUTO && protocol != LLAR_LL && protocol != LLAR_SENTINEL && !atomic) return fail(LLAR_ERR_ARG);
   if (count == 0) return LLAR_OK;
   if (count > h->max_bytes / h->elem / (size_t)N) return fail(LLAR_ERR_ARG);
   for (int r = 0; r < N; ++r)
@@ -614,12 +617,60 @@ int run_multi(llar_comm* h, const void* const* ins, void* const* outs, int n_rec
   const size_t total = blk * (size_t)N;
   int proto = (int)protocol;
   if (protocol == LLAR_AUTO) proto = ((long long)total <= h->thr_sentinel && total <= kCapLL) ? LLAR_LL : LLAR_SENTINEL;
-  if (total > (proto == LLAR_LL ? kCapLL : kCapSentinel)) return fail(LLAR_ERR_UNSUPPORTED);
+  if (total > (proto == LLAR_LL ? kCapLL : proto == LLAR_LL128 ? kCapLL128 : kCapSentinel))
+    return fail(LLAR_ERR_UNSUPPORTED);
   const Region* reg = region_of(h, proto);
   if (!reg->ptr) return fail(LLAR_ERR_UNSUPPORTED);
 
-  const int threads = h->threads ? (int)h->threads : 256;
+  // measured on MI355X: the atomic reduce-scatter issues best from 512-thread
+  // workgroups (1 MiB: 28 us against 32 us at 256; equal at 16 KiB)
+  const int threads = h->threads ? (int)h->threads : (atomic ? 512 : 256);
   if (threads != 64 && threads != 128 && threads != 256 && threads != 512) return fail(LLAR_ERR_ARG);
+  if (atomic) {
+    // owner o's segment in lines o*Lo .. o*Lo+Lo-1 of one parity; every
+    // owner's lines split into the same slices
+    const bool acc16 = (h->ll128_acc == 1) && h->kind != kKindF32;
+    const size_t K = acc16 ? 63 : 31;
+    const size_t lo_lines = ceil_div(count, K);
+    if ((size_t)N * lo_lines * 128 > reg->parity_stride) return fail(LLAR_ERR_UNSUPPORTED);
+    const int slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(lo_lines, (size_t)8), 1, 64);
+    LaunchSpec ls;
+    memset(&ls, 0, sizeof(ls));
+    ls.kind = h->kind;
+    ls.n_ranks = N;
+    ls.kernel = acc16 ? kKernRsLL128Acc16 : kKernRsLL128Acc32;
+    ls.threads = threads;
+    ls.grid = N * slices;
+    int occ = occupancy(h->kind, N, ls.kernel, threads);
+    if (occ <= 0) return fail(LLAR_ERR_HIP);
+    if (ls.grid > occ * h->cu_count) return fail(LLAR_ERR_UNSUPPORTED);
+    if (h->timing && ls.grid > kTimingMaxWgs) return fail(LLAR_ERR_UNSUPPORTED);
+    bool device_epoch = false;
+    uint32_t host_epoch = 0;
+    if (!call_epoch(h, stream, device_epoch, host_epoch)) return fail(LLAR_ERR_HIP);
+    MultiArgs& a = ls.multi;
+    for (int r = 0; r < N; ++r) {
+      a.in[r] = static_cast<const uint8_t*>(ins[r]);
+      a.out[r] = static_cast<uint8_t*>(outs[r]);
+    }
+    a.stage = reg->ptr;
+    a.ctrl = h->ctrl;
+    a.blk = blk;
+    a.spin_limit = spin_ticks(h);
+    a.stage_bytes = (uint32_t)reg->bytes;
+    a.parity_stride = (uint32_t)reg->parity_stride;
+    a.n_recv = (uint32_t)N;
+    a.grid = (uint32_t)ls.grid;
+    a.slices = (uint32_t)slices;
+    a.timing = h->timing ? 1u : 0u;
+    a.keep = h->keep_staging ? 1u : 0u;
+    a.drop_rank = h->debug_drop_rank < 0 ? 0xFFFFFFFFu : (uint32_t)h->debug_drop_rank;
+    a.host_epoch = host_epoch;
+    hipError_t e = launch(ls, stream);
+    if (e != hipSuccess) return fail(LLAR_ERR_HIP);
+    finish_call(h, device_epoch);
+    return LLAR_OK;
+  }
   const size_t nv = ceil_div(blk, 16);
   // measured on MI355X (N = 8, bf16, 16 KiB and 1 MiB in total): the best
   // slice count grows as the square root of a block's 8-byte units (4 at

@@ -47,7 +47,10 @@ enum KernelId : int {
   kKernRsSentinelLocal = 19,
   kKernAgLLLocal = 20,
   kKernAgSentinelLocal = 21,
-  kKernCount = 22
+  // ReduceScatter over the LL128 atomic wire (binary32 or 16-bit staging)
+  kKernRsLL128Acc32 = 22,
+  kKernRsLL128Acc16 = 23,
+  kKernCount = 24
 };
 constexpr int kKernFirstMulti = kKernRsLL;
 

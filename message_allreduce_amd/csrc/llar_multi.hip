@@ -197,6 +197,118 @@ __global__ void __launch_bounds__(512) k_multi(MultiArgs a) {
   wg_end(ctrl, st, host_epoch, grid, timing, idle);
 }
 
+// ---- ReduceScatter over the LL128 atomic wire ----------------------------------------
+// The reduce-scatter half of the two-shot LL128 AllReduce, with the owners'
+// shards equal to the ReduceScatter segments.  Owner o's segment (c
+// elements) occupies Lo = ceil(c / K) lines of its own, o*Lo .. o*Lo+Lo-1;
+// element i of it sits in line o*Lo + i/K, slot 1 + i%K (K = 31 binary32
+// slots, or 63 16-bit ones).  Every owner's lines are split the same way
+// into W slices.  Workgroup (rank r, slice w):
+//   produce: for every owner o, atomically add rank r's copy of segment o,
+//            slice w, into o's lines; once every wave's data atomics are
+//            acknowledged (drain + workgroup barrier), add 1.0 to slot 0 of
+//            each of those lines;
+//   consume: for each line of owner r's slice w, wait for the count N, read
+//            it (8 lanes x 16 bytes), round to the output type, zero it.
+// No line is shared between slices, so a workgroup only waits for the
+// slice-w workgroups of the other ranks, all resident.  The spread placement
+// is used: device-scope atomics resolve at the memory side wherever the
+// ranks run.
+template <int kKind, int kAcc16, int N>
+__global__ void __launch_bounds__(512) k_rs_ll128(MultiArgs a) {
+  int r;
+  uint32_t w;
+  decode_role_t<false, N>(blockIdx.x, r, w);
+  const uint8_t* const src = a.in[r];
+  uint8_t* const out = a.out[r];
+  uint8_t* const stage = a.stage;
+  Ctrl* const ctrl = a.ctrl;
+  const uint64_t blk = a.blk, spin_limit = a.spin_limit;
+  const uint32_t stage_bytes = a.stage_bytes, grid = a.grid, slices = a.slices;
+  const uint32_t timing = a.timing, keep = a.keep, drop_rank = a.drop_rank, host_epoch = a.host_epoch;
+  LLAR_UNIFORM_AT_ENTRY("s"(src), "s"(out), "s"(stage), "s"(ctrl), "s"(blk), "s"(spin_limit), "s"(stage_bytes),
+                        "s"(grid), "s"(slices), "s"(timing), "s"(keep), "s"(drop_rank), "s"(host_epoch));
+  using E = Elem<kKind>;
+  constexpr uint32_t K = kAcc16 ? 63u : 31u;
+  const bool idle = (w >= slices);
+  WgState st = wg_begin(ctrl, host_epoch, timing, idle);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(stage, stage_bytes);
+  const uint32_t c = (uint32_t)(blk / E::kBytes);  // elements per segment
+  const uint32_t Lo = (c + K - 1u) / K;               // lines per owner
+  const uint32_t l0 = (uint32_t)((uint64_t)w * Lo / slices), l1 = (uint32_t)((uint64_t)(w + 1u) * Lo / slices);
+  const uint32_t nl = idle ? 0u : l1 - l0;
+  uint32_t full;
+  if constexpr (!kAcc16) full = __float_as_uint((float)N);
+  else full = E::from_f32((float)N);
+
+  // ---- produce: data atomics into every owner's lines of slice w, then counts
+  if ((uint32_t)r != drop_rank) {
+    for (int o = 0; o < N; ++o) {
+      const uint8_t* const seg = src + (uint64_t)o * blk;
+      for (uint32_t it = threadIdx.x; it < nl * 32u; it += blockDim.x) {
+        const uint32_t line = l0 + it / 32u, q = it % 32u;  // dword q of the line
+        uint8_t* const dst = stage + ((uint64_t)o * Lo + line) * llar_wire::kLL128LineBytes + q * 4u;
+        if constexpr (!kAcc16) {
+          const uint32_t i = line * K + q - 1u;
+          if (q == 0u || i >= c) continue;
+          float val;
+          if constexpr (E::kBytes == 4) val = __uint_as_float(reinterpret_cast<const uint32_t*>(seg)[i]);
+          else val = E::to_f32(reinterpret_cast<const uint16_t*>(seg)[i]);
+          llar_wire::ll128_add(reinterpret_cast<float*>(dst), val);
+        } else {
+          // 16-bit slots 2q and 2q+1 hold elements line*K + 2q - 1 and line*K + 2q
+          const uint32_t i0 = line * K + 2u * q - 1u, i1 = line * K + 2u * q;
+          const uint32_t lo = (q != 0u && i0 < c) ? reinterpret_cast<const uint16_t*>(seg)[i0] : 0u;
+          const uint32_t hi = (i1 < c) ? reinterpret_cast<const uint16_t*>(seg)[i1] : 0u;
+          if ((lo | hi) == 0u) continue;  // nothing to add (both +0)
+          llar_wire::ll128_add2<kKind == kKindBF16>(dst, s16x2{(short)lo, (short)hi});
+        }
+      }
+    }
+  }
+  // every wave's data atomics acknowledged before any count of this workgroup
+  drain_vm();
+  __syncthreads();
+  if ((uint32_t)r != drop_rank) {
+    for (uint32_t it = threadIdx.x; it < (uint32_t)N * nl; it += blockDim.x) {
+      const uint32_t o = it / nl, line = l0 + it % nl;
+      uint8_t* const dst = stage + ((uint64_t)o * Lo + line) * llar_wire::kLL128LineBytes;
+      if constexpr (!kAcc16) llar_wire::ll128_flag(reinterpret_cast<float*>(dst));
+      else llar_wire::ll128_flag2<kKind == kKindBF16>(dst, E::from_f32(1.0f));
+    }
+  }
+
+  // ---- consume owner r's lines of slice w: 8 lanes per line
+  for (uint32_t it = threadIdx.x; it < nl * 8u; it += blockDim.x) {
+    const uint32_t line = l0 + it / 8u, j = it % 8u;
+    const uint32_t loff = ((uint32_t)r * Lo + line) * llar_wire::kLL128LineBytes;
+    Spin spin(spin_limit);
+    if (!llar_wire::ll128_wait<kAcc16 != 0>(rs, loff, full, spin)) {
+      raise_status(ctrl, kStatusTimeout);
+      break;
+    }
+    const u32x4 v = llar_wire::ll128_read16(rs, loff + j * 16u);
+    if constexpr (!kAcc16) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t s = j * 4u + (uint32_t)t, i = line * K + s - 1u;
+        if (s == 0u || i >= c) continue;
+        if constexpr (E::kBytes == 4) reinterpret_cast<uint32_t*>(out)[i] = v[t];
+        else reinterpret_cast<uint16_t*>(out)[i] = (uint16_t)E::from_f32(__uint_as_float(v[t]));
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t s = j * 8u + (uint32_t)t, i = line * K + s - 1u;
+        if (s == 0u || i >= c) continue;
+        reinterpret_cast<uint16_t*>(out)[i] = (uint16_t)(v[t >> 1] >> ((t & 1) * 16));
+      }
+    }
+    if (!keep) llar_wire::ll128_reset16(rs, loff + j * 16u);
+  }
+  wg_end(ctrl, st, host_epoch, grid, timing, idle);
+}
+
 template <int kKind, int N>
 hipError_t launch_multi_n(const LaunchSpec& ls, hipStream_t stream) {
   const dim3 grid(ls.grid), block(ls.threads);
@@ -209,6 +321,13 @@ hipError_t launch_multi_n(const LaunchSpec& ls, hipStream_t stream) {
     case kKernRsSentinelLocal: hipLaunchKernelGGL((k_multi<kWireSentinel, kKind, N, false, true>), grid, block, 0, stream, ls.multi); break;
     case kKernAgLLLocal: hipLaunchKernelGGL((k_multi<kWireLL, kKind, N, true, true>), grid, block, 0, stream, ls.multi); break;
     case kKernAgSentinelLocal: hipLaunchKernelGGL((k_multi<kWireSentinel, kKind, N, true, true>), grid, block, 0, stream, ls.multi); break;
+    case kKernRsLL128Acc32: hipLaunchKernelGGL((k_rs_ll128<kKind, 0, N>), grid, block, 0, stream, ls.multi); break;
+    case kKernRsLL128Acc16:
+      if constexpr (kKind != kKindF32) {
+        hipLaunchKernelGGL((k_rs_ll128<kKind, 1, N>), grid, block, 0, stream, ls.multi);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -227,6 +346,10 @@ int occupancy_multi_n(int kernel, int threads) {
     case kKernRsSentinelLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_multi<kWireSentinel, kKind, N, false, true>, threads, 0); break;
     case kKernAgLLLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_multi<kWireLL, kKind, N, true, true>, threads, 0); break;
     case kKernAgSentinelLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_multi<kWireSentinel, kKind, N, true, true>, threads, 0); break;
+    case kKernRsLL128Acc32: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_rs_ll128<kKind, 0, N>, threads, 0); break;
+    case kKernRsLL128Acc16:
+      if constexpr (kKind != kKindF32) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_rs_ll128<kKind, 1, N>, threads, 0);
+      break;
     default: break;
   }
   return err == hipSuccess ? blocks : 0;

@@ -16,7 +16,7 @@ import oracle
 from oracle import F32, F16, BF16, models
 from workloads import make_partials, random_bits
 
-from gpu_util import CODE, TORCH_DT, assert_exact, run, to_device, to_host
+from gpu_util import CODE, TORCH_DT, assert_exact, assert_tol, run, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -135,6 +135,71 @@ def test_reduce_scatter_maximum_size():
             want = oracle.reduce_scatter(bits, dt)
             for j in range(n_ranks):
                 assert_exact(got[j], want[j], dt, "%s rank %d" % (wire, j))
+
+
+@pytest.mark.parametrize("acc", [0, 1], ids=["fp32_staging", "16bit_staging"])
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_reduce_scatter_ll128_atomic_within_tolerance(dtype, acc):
+    """The reduce-scatter half of the two-shot LL128 AllReduce: within the
+    atomic protocol's tolerance, exact on small integers with binary32
+    staging, lines zero after."""
+    dt = CODE[dtype]
+    if acc == 1 and dt == F32:
+        pytest.skip("16-bit staging applies to 16-bit types only")
+    n_ranks = 8
+    with comm_for(n_ranks, dt, n_ranks * max(COUNTS) * 4, ll128_acc=acc) as c:
+        for i, cnt in enumerate(COUNTS):
+            bits = make_partials(4000 + dt, i, n_ranks, dtype, n_ranks * cnt, "normal", 0.02)
+            got = rs_run(c, bits, dt, "ll128")
+            want = oracle.reduce_scatter(bits, dt)
+            for j in range(n_ranks):
+                assert_tol(got[j], want[j], dt, "%s acc%d count=%d rank %d" % (dtype, acc, cnt, j))
+            if acc == 1:
+                continue  # 16-bit staging rounds partial sums of integers above 256 (bf16)
+            ints = make_partials(4100 + dt, i, n_ranks, dtype, n_ranks * cnt, "integer", 1.0)
+            got = rs_run(c, ints, dt, "ll128")
+            want = oracle.reduce_scatter(ints, dt)
+            for j in range(n_ranks):
+                assert_exact(got[j], want[j], dt, "integers %s acc%d count=%d rank %d" % (dtype, acc, cnt, j))
+        assert not c.staging(llar.LL128).any(), "every line is zeroed by its owner"
+
+
+@pytest.mark.parametrize("n_ranks", [1, 2, 3, 5, 8])
+def test_reduce_scatter_ll128_every_rank_count(n_ranks):
+    dt = BF16
+    cnt = 1000
+    with comm_for(n_ranks, dt, n_ranks * cnt * 2) as c:
+        for rep in range(3):
+            bits = make_partials(4200 + n_ranks, rep, n_ranks, "bf16", n_ranks * cnt, "normal", 1.0)
+            got = rs_run(c, bits, dt, "ll128")
+            want = oracle.reduce_scatter(bits, dt)
+            for j in range(n_ranks):
+                assert_tol(got[j], want[j], dt, "N=%d rep %d rank %d" % (n_ranks, rep, j))
+        assert not c.staging(llar.LL128).any()
+
+
+def test_reduce_scatter_ll128_maximum_size_and_allreduce_interleaving():
+    """16 MiB in total (the LL128 limit), then AllReduce and ReduceScatter
+    calls sharing the LL128 staging."""
+    dt = BF16
+    n_ranks = 8
+    total = 16 << 20
+    cnt = total // 2 // n_ranks
+    with comm_for(n_ranks, dt, total) as c:
+        bits = make_partials(4300, 0, n_ranks, "bf16", n_ranks * cnt, "normal", 0.02)
+        got = rs_run(c, bits, dt, "ll128")
+        want = oracle.reduce_scatter(bits, dt)
+        for j in range(n_ranks):
+            assert_tol(got[j], want[j], dt, "max size rank %d" % j)
+        for rep in range(6):
+            small = make_partials(4301, rep, n_ranks, "bf16", n_ranks * 1024, "normal", 0.02)
+            got = run(c, small, "ll128", dt)
+            assert_tol(got, oracle.allreduce(small, dt), dt, "allreduce rep %d" % rep)
+            got = rs_run(c, small, dt, "ll128")
+            want = oracle.reduce_scatter(small, dt)
+            for j in range(n_ranks):
+                assert_tol(got[j], want[j], dt, "rs rep %d rank %d" % (rep, j))
+        assert not c.staging(llar.LL128).any()
 
 
 # --------------------------------------------------------------------------- AllGather
@@ -263,8 +328,8 @@ def test_collectives_graph_capture_replays():
         c.close()
 
 
-@pytest.mark.parametrize("op", ["reduce_scatter", "all_gather"])
-@pytest.mark.parametrize("wire", WIRES)
+@pytest.mark.parametrize("op,wire", [("reduce_scatter", "ll"), ("reduce_scatter", "sentinel"),
+                                     ("reduce_scatter", "ll128"), ("all_gather", "ll"), ("all_gather", "sentinel")])
 def test_collectives_lost_contribution_times_out_and_recovers(op, wire):
     """A rank whose sends are dropped (forced from the host) makes the other
     receivers' bounded polls expire; after a reset the next call works."""
@@ -291,7 +356,7 @@ def test_collectives_lost_contribution_times_out_and_recovers(op, wire):
         got = rs_run(c, bits, dt, wire)
         want = oracle.reduce_scatter(bits, dt)
         for j in range(n_ranks):
-            assert_exact(got[j], want[j], dt, "after recovery rank %d" % j)
+            (assert_tol if wire == "ll128" else assert_exact)(got[j], want[j], dt, "after recovery rank %d" % j)
 
 
 def test_collectives_argument_errors():
@@ -302,8 +367,9 @@ def test_collectives_argument_errors():
         outs = [torch.zeros(cnt, dtype=torch.bfloat16, device="cuda") for _ in range(n_ranks)]
         p = [t.data_ptr() for t in parts]
         o = [t.data_ptr() for t in outs]
-        for proto in (llar.LL128, llar.LL128_PIPELINED, llar.SENTINEL_PIPELINED, 9):
+        for proto in (llar.LL128_PIPELINED, llar.SENTINEL_PIPELINED, 9):
             assert llar.llar_reduce_scatter(c.h, p, o, cnt, BF16, proto, 0) == -1
+        for proto in (llar.LL128, llar.LL128_PIPELINED, llar.SENTINEL_PIPELINED, 9):
             assert llar.llar_all_gather(c.h, o, p, cnt, BF16, proto, 0) == -1
         assert llar.llar_reduce_scatter(c.h, p, o, cnt + 1, BF16, llar.LL, 0) == -1      # beyond max_bytes
         assert llar.llar_reduce_scatter(c.h, p, o, cnt, F32, llar.LL, 0) == -1          # wrong dtype
