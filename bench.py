@@ -11,6 +11,9 @@ Default run (one JSON line on stdout):
     2 x (L2 round trip) + (cross-XCD store visibility), all measured here;
   * bandwidth_64MiB: the 64 MiB-per-rank reduce, effective GB/s over the
     algorithmic bytes (N + 1) x 64 MiB, and the HBM roofline of that kernel;
+  * barrier_ablation: the same 16 KiB one-shot reduce with a grid-wide
+    barrier in place of the LL flags, beside LL itself (what removing the
+    barrier buys);
   * cpu_baseline: the CPU oracle on the same 16 KiB workload.
 
   * rows: point-to-point send/recv (8 KB fp16) and ReduceScatter (LL,
@@ -375,6 +378,18 @@ def main():
     log("16 KiB: %.3f us per call (stream; min %.3f p90 %.3f), %s us per call in a graph, device-side median "
         "%.3f us (min %.3f)" % (us, us_min, us_p90, us_graph, dev_med, dev_min))
 
+    # ---- the same reduce behind a grid-wide barrier (what the flags replace)
+    comm.set_option("barrier_ablation", 1)
+    try:
+        _, ab_us, _ = time_batches(comm, parts, out, 1, args.steps, args.warmup, stream)
+        ab_dev_med, ab_dev_min = device_side_us(comm, parts, out, 1, 60, stream)
+    finally:
+        comm.set_option("barrier_ablation", 0)
+    _, ll_us, _ = time_batches(comm, parts, out, 1, args.steps, 0, stream)
+    ll_dev_med, _ = device_side_us(comm, parts, out, 1, 60, stream)
+    log("16 KiB barrier ablation: %.3f us per call, device %.3f us; LL %.3f us per call, device %.3f us"
+        % (ab_us, ab_dev_med, ll_us, ll_dev_med))
+
     # ---- 64 MiB bf16, N = 8, AUTO
     n_big = BIG_BYTES // 2
     _, parts_big = device_inputs(5, N_RANKS, n_big, "normal", 1.0)
@@ -418,6 +433,11 @@ def main():
                                   "per_call_stream_us": {"min": round(us_min, 3), "median": round(us, 3),
                                                          "p90": round(us_p90, 3)},
                                   "per_call_graph_us": None if us_graph is None else round(us_graph, 3)}),
+        "barrier_ablation": {"workload": "the same 16 KiB x 8 one-shot reduce, grid-wide barrier instead of LL flags",
+                             "per_call_us": round(ab_us, 3), "device_us_median": round(ab_dev_med, 3),
+                             "device_us_min": round(ab_dev_min, 3), "ll_per_call_us": round(ll_us, 3),
+                             "ll_device_us_median": round(ll_dev_med, 3),
+                             "barrier_cost_device_us": round(ab_dev_med - ll_dev_med, 3)},
         "bandwidth_64MiB": {"protocol": PROTO_NAMES[proto_big], "geometry": geo_big,
                             "us": {"min": round(us_big_min, 2), "median": round(us_big, 2), "p90": round(us_big_p90, 2)},
                             "GBps": round(gbps, 1), "algorithmic_bytes": alg_bytes,

@@ -211,6 +211,10 @@ int llar_clear_device_status(llar_comm* h);
  *   "debug_drop_rank"  tests: the producers of this rank write nothing, so consumers time out (-1 = none)
  *   "trace"            1 = one-shot kernels record per-workgroup phase stamps (see llar_get_trace),
  *                      the pipelined Sentinel per-chunk stamps (see llar_get_pipeline_trace)
+ *   "barrier_ablation" 1 = LL and Sentinel AllReduce calls run the same one-shot exchange behind a
+ *                      grid-wide memory barrier instead of per-line flags (raw stores, barrier, then
+ *                      reads): the synchronisation the pages say earlier implementations pay at every
+ *                      step, kept for measurement; same results, up to 8 MiB per rank
  *   "device_epoch"     1 = always read the device-resident epoch; otherwise the host numbers
  *                      stream-ordered calls and the device epoch is used only on a stream that is
  *                      being captured into a graph (replays then never reuse an epoch)

@@ -181,6 +181,10 @@ struct Ctrl {
   uint32_t pad1[31];
   uint32_t status;     // sticky error bits
   uint32_t pad2[31];
+  uint32_t bar_count;  // grid barrier of the barrier-based ablation kernel: arrivals of this call
+  uint32_t pad3[31];
+  uint32_t bar_gen;    // ... and its generation, advanced by the last arrival
+  uint32_t pad4[31];
   uint32_t timing_grid[kTimingRing];  // per epoch slot: workgroups that recorded a span
   uint64_t* timing_wg;  // [kTimingRing][kTimingMaxWgs][2]: each workgroup's start, end (wall ticks)
 };

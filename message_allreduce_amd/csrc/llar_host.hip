@@ -85,6 +85,7 @@ struct llar_comm {
   long long pipe_buffers = 4;  // staging buffers of the pipelined Sentinel (2, 4, 6 or 8)
   long long sentinel_credit = 0;  // pipelined Sentinel: 0 = workgroup credit, 1 = slot handshake
   long long cons_waves = 0;       // slot handshake: consumer waves per workgroup (0 = a quarter)
+  long long barrier_ablation = 0;  // 1: LL/Sentinel AllReduce behind a grid-wide barrier (measurement)
   long long thr_sentinel = 64ll << 10;    // AUTO: LL up to (<=) this many bytes
   long long thr_ll128 = 1ll << 62;        // AUTO: one-shot Sentinel up to here (LL128 one round above)
   long long thr_pipelined = 512ll << 10;  // AUTO: pipelined Sentinel above this
@@ -473,7 +474,10 @@ void finish_call(llar_comm* h, bool device_epoch) {
 int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_t n_elems, int proto,
           const Geometry& g, hipStream_t stream) {
   const size_t nbytes = n_elems * h->elem;
-  const Region* reg = region_of(h, proto);
+  // the barrier ablation stages raw vectors in the LL region and leaves what
+  // it used zero (invalid LL lines)
+  const bool barrier = g.kernel == kKernBarrier || g.kernel == kKernBarrierLocal;
+  const Region* reg = barrier ? &h->ll : region_of(h, proto);
 
   LaunchSpec ls;
   memset(&ls, 0, sizeof(ls));
@@ -496,7 +500,8 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
   const bool is_oneshot = g.kernel == kKernOneShotLL || g.kernel == kKernOneShotSentinel ||
                           g.kernel == kKernOneShotLLLocal || g.kernel == kKernOneShotSentinelLocal ||
                           g.kernel == kKernP2PLL || g.kernel == kKernP2PSentinel || g.kernel == kKernP2PLLLocal ||
-                          g.kernel == kKernP2PSentinelLocal;
+                          g.kernel == kKernP2PSentinelLocal || g.kernel == kKernBarrier ||
+                          g.kernel == kKernBarrierLocal;
   if (is_oneshot) {
     OneShotArgs& a = ls.oneshot;
     for (int r = 0; r < n_launch; ++r) a.part[r] = static_cast<const uint8_t*>(parts[r]);
@@ -749,6 +754,11 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
   Geometry g;
   int st = plan(h, n_elems, proto, g);
   if (st != LLAR_OK) return fail(st);
+  if (h->barrier_ablation && (proto == LLAR_LL || proto == LLAR_SENTINEL)) {
+    // the same one-shot geometry, synchronised by a grid-wide barrier
+    if (nbytes > kCapLL) return fail(LLAR_ERR_UNSUPPORTED);
+    g.kernel = g.placement == kPlaceLocal ? kKernBarrierLocal : kKernBarrier;
+  }
   return issue(h, partials, h->n_ranks, out, n_elems, proto, g, static_cast<hipStream_t>(stream));
 }
 
@@ -835,6 +845,7 @@ static long long* option_slot(llar_comm* h, const char* key) {
       {"pipeline_buffers", &llar_comm::pipe_buffers},
       {"sentinel_credit", &llar_comm::sentinel_credit},
       {"consumer_waves", &llar_comm::cons_waves},
+      {"barrier_ablation", &llar_comm::barrier_ablation},
       {"auto_threshold_sentinel", &llar_comm::thr_sentinel},
       {"auto_threshold_ll128", &llar_comm::thr_ll128},
       {"auto_threshold_pipelined", &llar_comm::thr_pipelined},
@@ -862,7 +873,7 @@ int llar_set_option(llar_comm* h, const char* key, long long value) {
   if (strcmp(key, "consumer_waves") == 0 && (value < 0 || value > 15)) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "placement") == 0 && value == 2 && !h->local_ok) return fail(LLAR_ERR_UNSUPPORTED);
   if ((strcmp(key, "timing") == 0 || strcmp(key, "keep_staging") == 0 || strcmp(key, "trace") == 0 ||
-       strcmp(key, "device_epoch") == 0) &&
+       strcmp(key, "device_epoch") == 0 || strcmp(key, "barrier_ablation") == 0) &&
       (value < 0 || value > 1))
     return fail(LLAR_ERR_ARG);
   if (strcmp(key, "timing") == 0 && value == 1 && h->timing == 0) {

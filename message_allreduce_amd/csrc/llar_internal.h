@@ -50,7 +50,10 @@ enum KernelId : int {
   // ReduceScatter over the LL128 atomic wire (binary32 or 16-bit staging)
   kKernRsLL128Acc32 = 22,
   kKernRsLL128Acc16 = 23,
-  kKernCount = 24
+  // ablation: the one-shot reduce with a grid-wide barrier instead of flags
+  kKernBarrier = 24,
+  kKernBarrierLocal = 25,
+  kKernCount = 26
 };
 constexpr int kKernFirstMulti = kKernRsLL;
 

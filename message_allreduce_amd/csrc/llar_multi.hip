@@ -21,6 +21,8 @@
 // Blocks need not be a multiple of 16 bytes: then the accesses to the
 // caller's buffers (which start at block multiples) move halfwords, and the
 // last vector of a block is zero-padded in staging.
+#include <stddef.h>
+
 #include "llar_device.h"
 #include "llar_internal.h"
 
@@ -309,6 +311,117 @@ __global__ void __launch_bounds__(512) k_rs_ll128(MultiArgs a) {
   wg_end(ctrl, st, host_epoch, grid, timing, idle);
 }
 
+// ---- ablation: the one-shot reduce behind a grid-wide barrier ----------------------------
+// What the barrier-free protocols replace: "Every Microsecond Matters"
+// (agihunt.info summary, the paragraph on where the time goes) locates the
+// gap to the speed of light in the global memory barrier that earlier
+// implementations place at every synchronisation step.  This kernel is the
+// one-shot reduce written that way, for measurement: ranks 1..N-1 store
+// their raw vectors into the LL staging region (no flag), every workgroup
+// arrives at a grid-wide barrier once its stores are acknowledged, and only
+// then do rank 0's workgroups read the staging, reduce (binary64, rank
+// order, one rounding: the same result as LL and Sentinel) and zero what
+// they read, which leaves those bytes invalid LL lines (epoch 0).  The
+// barrier is sense-reversing (arrival count plus generation), so it needs no
+// host state between calls and works under graph replay.
+template <int kKind, int N, bool kLocal>
+__global__ void __launch_bounds__(512) k_oneshot_barrier(OneShotArgs a) {
+  int r;
+  uint32_t w;
+  decode_role_t<kLocal, N>(blockIdx.x, r, w);
+  const uint8_t* const src = a.part[r];
+  uint8_t* const out = a.out;
+  uint8_t* const stage = a.stage;
+  Ctrl* const ctrl = a.ctrl;
+  const uint64_t nbytes = a.nbytes, spin_limit = a.spin_limit;
+  const uint32_t slices = a.slices, vq = a.vq, vr = a.vr, stage_bytes = a.stage_bytes;
+  const uint32_t parity_stride = a.parity_stride, rank_stride = a.rank_stride, grid = a.grid;
+  const uint32_t timing = a.timing, drop_rank = a.drop_rank, host_epoch = a.host_epoch;
+  LLAR_UNIFORM_AT_ENTRY("s"(src), "s"(out), "s"(stage), "s"(ctrl), "s"(nbytes), "s"(spin_limit), "s"(slices),
+                        "s"(vq), "s"(vr), "s"(stage_bytes), "s"(parity_stride), "s"(rank_stride), "s"(grid),
+                        "s"(timing), "s"(drop_rank), "s"(host_epoch));
+  const bool idle = (w >= slices);
+  const uint32_t v0 = idle ? 0u : w * vq + min(w, vr);
+  const uint32_t v1 = idle ? 0u : v0 + vq + (w < vr ? 1u : 0u);
+  WgState st = wg_begin(ctrl, host_epoch, timing, idle);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(stage, stage_bytes);
+  const uint32_t par_off = (st.epoch & 1u) * parity_stride;
+  // phase 1: ranks 1..N-1 store their raw vectors
+  if (!idle && r != 0 && (uint32_t)r != drop_rank) {
+    const uint32_t base = par_off + (uint32_t)(r - 1) * rank_stride;
+    for (uint32_t v = v0 + threadIdx.x; v < v1; v += blockDim.x) {
+      const uint64_t off = (uint64_t)v * 16u;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (off + 16u <= nbytes) {
+        x = *reinterpret_cast<const u32x4*>(src + off);
+      } else {
+#pragma unroll
+        for (uint32_t b = 0; b < 16u; b += 2u)
+          if (off + b < nbytes) x[b >> 2] |= (uint32_t)(*reinterpret_cast<const uint16_t*>(src + off + b)) << ((b & 2u) * 8u);
+      }
+      st16_stage<kLocal>(rs, base + v * 16u, x);
+    }
+  }
+  // the grid-wide barrier (sense-reversing): read the generation, arrive;
+  // the last arrival resets the count and advances the generation, which
+  // releases everybody
+  __shared__ uint32_t s_dead;
+  drain_vm();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const __amdgpu_buffer_rsrc_t cr = make_rsrc(ctrl, (uint32_t)sizeof(Ctrl));
+    const uint32_t gen_off = (uint32_t)offsetof(Ctrl, bar_gen);
+    const uint32_t gen = ld4_coh(cr, gen_off);
+    const uint32_t ticket = __hip_atomic_fetch_add(&ctrl->bar_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t dead = 0u;
+    if (ticket == grid - 1u) {
+      __hip_atomic_store(&ctrl->bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      drain_vm();  // the reset lands before anybody is released
+      __hip_atomic_fetch_add(&ctrl->bar_gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      Spin spin(spin_limit);
+      while (ld4_coh(cr, gen_off) == gen) {
+        if (spin.expired()) {
+          raise_status(ctrl, kStatusTimeout);
+          dead = 1u;
+          break;
+        }
+      }
+    }
+    s_dead = dead;
+  }
+  __syncthreads();
+  // phase 2: rank 0 reduces what the barrier guarantees is there
+  if (!idle && r == 0 && s_dead == 0u) {
+    for (uint32_t u = 2u * v0 + threadIdx.x; u < 2u * v1; u += blockDim.x) {
+      const uint64_t off = (uint64_t)u * 8u;
+      u32x2 own = {0u, 0u};
+      if (off + 8u <= nbytes) {
+        own = *reinterpret_cast<const u32x2*>(src + off);
+      } else {
+#pragma unroll
+        for (uint32_t b = 0; b < 8u; b += 2u)
+          if (off + b < nbytes) own[b >> 2] |= (uint32_t)(*reinterpret_cast<const uint16_t*>(src + off + b)) << ((b & 2u) * 8u);
+      }
+      u32x2 d[N > 1 ? N - 1 : 1];
+      d[0] = u32x2{0u, 0u};
+#pragma unroll
+      for (int k = 0; k < N - 1; ++k) d[k] = ld8_coh(rs, par_off + (uint32_t)k * rank_stride + u * 8u);
+      const u32x2 s = reduce_unit_at<kKind, N>(own, 0, d);
+      if (off + 8u <= nbytes) {
+        *reinterpret_cast<u32x2*>(out + off) = s;
+      } else {
+#pragma unroll
+        for (uint32_t b = 0; b < 8u; b += 2u)
+          if (off + b < nbytes) *reinterpret_cast<uint16_t*>(out + off + b) = (uint16_t)(s[b >> 2] >> ((b & 2u) * 8u));
+      }
+#pragma unroll
+      for (int k = 0; k < N - 1; ++k) st8_stage<kLocal>(rs, par_off + (uint32_t)k * rank_stride + u * 8u, u32x2{0u, 0u});
+    }
+  }
+  wg_end(ctrl, st, host_epoch, grid, timing, idle);
+}
+
 template <int kKind, int N>
 hipError_t launch_multi_n(const LaunchSpec& ls, hipStream_t stream) {
   const dim3 grid(ls.grid), block(ls.threads);
@@ -322,6 +435,8 @@ hipError_t launch_multi_n(const LaunchSpec& ls, hipStream_t stream) {
     case kKernAgLLLocal: hipLaunchKernelGGL((k_multi<kWireLL, kKind, N, true, true>), grid, block, 0, stream, ls.multi); break;
     case kKernAgSentinelLocal: hipLaunchKernelGGL((k_multi<kWireSentinel, kKind, N, true, true>), grid, block, 0, stream, ls.multi); break;
     case kKernRsLL128Acc32: hipLaunchKernelGGL((k_rs_ll128<kKind, 0, N>), grid, block, 0, stream, ls.multi); break;
+    case kKernBarrier: hipLaunchKernelGGL((k_oneshot_barrier<kKind, N, false>), grid, block, 0, stream, ls.oneshot); break;
+    case kKernBarrierLocal: hipLaunchKernelGGL((k_oneshot_barrier<kKind, N, true>), grid, block, 0, stream, ls.oneshot); break;
     case kKernRsLL128Acc16:
       if constexpr (kKind != kKindF32) {
         hipLaunchKernelGGL((k_rs_ll128<kKind, 1, N>), grid, block, 0, stream, ls.multi);
@@ -347,6 +462,8 @@ int occupancy_multi_n(int kernel, int threads) {
     case kKernAgLLLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_multi<kWireLL, kKind, N, true, true>, threads, 0); break;
     case kKernAgSentinelLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_multi<kWireSentinel, kKind, N, true, true>, threads, 0); break;
     case kKernRsLL128Acc32: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_rs_ll128<kKind, 0, N>, threads, 0); break;
+    case kKernBarrier: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_oneshot_barrier<kKind, N, false>, threads, 0); break;
+    case kKernBarrierLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_oneshot_barrier<kKind, N, true>, threads, 0); break;
     case kKernRsLL128Acc16:
       if constexpr (kKind != kKindF32) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_rs_ll128<kKind, 1, N>, threads, 0);
       break;

@@ -565,3 +565,57 @@ def test_pipelined_short_last_chunk_regression(proto):
                     bits = make_partials(1600 + i, rep, n_ranks, "bf16", n, "normal", 1.0)
                     got = run(c, bits, proto, dt)
                     check(got, oracle.allreduce(bits, dt), dt, proto, "N=%d n=%d rep %d" % (n_ranks, n, rep))
+
+
+# --------------------------------------------------------------------------- the barrier ablation
+@pytest.mark.parametrize("placement", [1, 2], ids=["spread", "local"])
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_barrier_ablation_is_exact_and_leaves_the_protocols_working(dtype, placement):
+    """The one-shot reduce behind a grid-wide barrier (measurement option)
+    computes the same bit-exact sum; LL and Sentinel calls before and after
+    it stay exact, so the staging it borrows is left valid."""
+    dt = CODE[dtype]
+    n_ranks = 8
+    sizes = [1, 7, 8192, 65537]
+    with comm_for(n_ranks, dt, max(sizes) * 4, placement=placement) as c:
+        for i, n in enumerate(sizes):
+            bits = make_partials(5000 + dt, i, n_ranks, dtype, n, "normal", 1.0)
+            want = oracle.allreduce(bits, dt)
+            c.set_option("barrier_ablation", 1)
+            for proto in ("ll", "sentinel", "auto"):
+                assert_exact(run(c, bits, proto, dt), want, dt, "ablation %s n=%d" % (proto, n))
+            c.set_option("barrier_ablation", 0)
+            for proto in ALL_PROTOCOLS:
+                check(run(c, bits, proto, dt), want, dt, proto, "after ablation %s n=%d" % (proto, n))
+
+
+@pytest.mark.parametrize("n_ranks", [1, 2, 3, 5, 8])
+def test_barrier_ablation_every_rank_count_and_graph_replays(n_ranks):
+    dt = BF16
+    n = 3000
+    c = comm_for(n_ranks, dt, n * 2, barrier_ablation=1)
+    try:
+        parts = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(n_ranks)]
+        out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        bits = make_partials(5100 + n_ranks, 0, n_ranks, "bf16", n)
+        for r in range(n_ranks):
+            parts[r].copy_(to_device(bits[r], dt))
+        c.allreduce(parts, out, "ll")
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            c.allreduce(parts, out, "ll")
+            c.allreduce(parts, out, "ll")
+        torch.cuda.synchronize()
+        for rep in range(1, 4):
+            bits = make_partials(5100 + n_ranks, rep, n_ranks, "bf16", n)
+            for r in range(n_ranks):
+                parts[r].copy_(to_device(bits[r], dt))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            st, sbits = c.device_status()
+            assert st == 0, (st, sbits)
+            assert_exact(to_host(out, dt), oracle.allreduce(bits, dt), dt, "N=%d replay %d" % (n_ranks, rep))
+    finally:
+        c.close()
