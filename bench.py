@@ -430,6 +430,8 @@ def main():
                               else "stream-ordered back-to-back calls, median of 5 batches")},
         "latency": dict(floor, **{"device_us_median": round(dev_med, 3), "device_us_min": round(dev_min, 3),
                                   "device_over_floor": round(dev_med / floor["floor_us"], 3),
+                                  "per_call_over_floor_plus_launch": round(
+                                      value / (floor["floor_us"] + floor["empty_launch_us"]), 3),
                                   "per_call_stream_us": {"min": round(us_min, 3), "median": round(us, 3),
                                                          "p90": round(us_p90, 3)},
                                   "per_call_graph_us": None if us_graph is None else round(us_graph, 3)}),

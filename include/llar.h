@@ -204,7 +204,9 @@ int llar_clear_device_status(llar_comm* h);
  *                      producer and consumer waves and needs at least 128
  *   "pipeline_buffers" staging buffers of the pipelined Sentinel: 2, 4 (default), 6 or 8; with B
  *                      buffers a producer runs up to B/2 - 1 chunks ahead of its consumer
- *   "placement"        0 = auto, 1 = spread (rank r on XCD r mod 8), 2 = local (one slice's ranks share an XCD)
+ *   "placement"        0 = auto, 1 = spread (rank r on XCD r mod 8), 2 = local (one slice's ranks share an XCD);
+ *                      auto: local for the LL and Sentinel AllReduce and send/recv, spread for LL128, and
+ *                      for ReduceScatter / AllGather local from 8 slices per rank up, spread below
  *   "timing"           1 = record device-side start/end wall-clock per call (see llar_get_timing);
  *                      a call whose grid exceeds 4096 workgroups then fails with LLAR_ERR_UNSUPPORTED
  *   "keep_staging"     1 = LL128/Sentinel consumers do not reset staging (tests only; the next call is invalid)
