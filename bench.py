@@ -218,6 +218,88 @@ def measure_rows(stream, steps):
     return rows
 
 
+def measure_device_api(stream, steps):
+    """The device-side API's use case: an epilogue fused with the exchange.
+    N = 8 fp32 partials of 16 KiB are scaled per rank and summed, either by
+    one custom kernel written against include/llar_wire.h (the LL demo of
+    tests/device_api) or by a scaling kernel followed by the library's LL
+    AllReduce.  Per call from graph replay; None if the demo is not built."""
+    import ctypes
+    import torch
+    import message_allreduce_amd as llar
+    lib = os.path.join(ROOT, "tests", "device_api", "libwire_demo.so")
+    if not os.path.exists(lib):
+        return None
+    L = ctypes.CDLL(lib)
+    vp, u32, u64, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int
+    L.demo_scaled_allreduce_ll.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_float), vp, u32, i32, vp, u32,
+                                           u32, u64, vp, vp]
+    L.demo_scaled_allreduce_ll.restype = i32
+    n = SMALL_BYTES // 4
+    stacked = torch.randn(N_RANKS, n, dtype=torch.float32, device="cuda")
+    scales = torch.linspace(0.5, 2.0, N_RANKS, dtype=torch.float32, device="cuda").view(N_RANKS, 1)
+    scaled = torch.empty_like(stacked)
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    stage = torch.zeros((N_RANKS - 1) * ((n + 1) // 2) * 16, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ptrs = (vp * N_RANKS)(*[stacked[r].data_ptr() for r in range(N_RANKS)])
+    host_scales = (ctypes.c_float * N_RANKS)(*scales.view(-1).tolist())
+    def fused(epoch):
+        rc = L.demo_scaled_allreduce_ll(ptrs, host_scales, out.data_ptr(), n, N_RANKS, stage.data_ptr(),
+                                        stage.numel(), epoch, 10_000_000, status.data_ptr(),
+                                        ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("demo_scaled_allreduce_ll returned %d" % rc)
+
+    # A captured launch repeats its arguments: the graph holds 100 launches
+    # with epochs 1..100, and the LL staging is cleared (one fill kernel)
+    # before each replay so that no line of the previous replay looks valid.
+    per_graph = 100
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        stage.zero_()
+        fused(1)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for ep in range(1, per_graph + 1):
+                fused(ep)
+        torch.cuda.synchronize()
+        stage.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // per_graph)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            stage.zero_()
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+    us_fused = a.elapsed_time(b) * 1e3 / (reps * per_graph)
+    del g
+
+    c = llar.Communicator(N_RANKS, torch.float32, SMALL_BYTES)
+    try:
+        parts = [scaled[r] for r in range(N_RANKS)]
+
+        def unfused():
+            torch.mul(stacked, scales, out=scaled)
+            c.allreduce(parts, out, "ll", stream=stream)
+
+        us_unfused = time_graph_fn(unfused, steps, stream, per_graph)
+        torch.cuda.synchronize()
+        if int(status.item()) != 0 or c.device_status()[0] != 0:
+            raise RuntimeError("a wait expired in the device-API timing")
+    finally:
+        c.close()
+    log("device API: fused scale+allreduce %.3f us per call, scale kernel + llar_allreduce %.3f us"
+        % (us_fused, us_unfused))
+    return {"workload": "8 x 16 KiB fp32 partials, per-rank scale then sum",
+            "fused_us_per_call_graph": round(us_fused, 3),
+            "unfused_us_per_call_graph": round(us_unfused, 3)}
+
+
 def profiled_traffic(kernel_file, name):
     """HBM bytes per launch of the 64 MiB reduce, from the committed counter
     summary -- only while the kernel source is the one that was profiled."""
@@ -454,6 +536,7 @@ def main():
     if not args.no_rows:
         log("other collectives")
         result["rows"] = measure_rows(stream, min(args.steps, 1000))
+        result["rows"]["device_api_fused_epilogue"] = measure_device_api(stream, min(args.steps, 1000))
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -27,6 +27,15 @@ namespace {
 
 using namespace llar_wire;
 
+// binary32 product, rounded before any later use: the empty asm makes the
+// value opaque, so the compiler cannot contract the multiply into a wider
+// fused multiply-add with the sum it feeds
+__device__ __forceinline__ float mul_f32(float a, float b) {
+  float p = a * b;
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
 struct Parts {
   const float* p[8];
   float scale[8];
@@ -43,22 +52,30 @@ __global__ void __launch_bounds__(256) k_scaled_allreduce_ll(Parts in, float* ou
   const Wire wire = make_wire(stage, stage_bytes);  // [rank 1..N-1][unit] 16-byte LL lines
   for (uint32_t u = w * blockDim.x + threadIdx.x; u < units; u += slices * blockDim.x) {
     const uint32_t i0 = 2u * u, i1 = 2u * u + 1u;
-    // the product rounds to binary32 before it is widened (no contraction)
-    auto scaled = [&](int k, uint32_t i) -> float { return i < n ? __fmul_rn(in.p[k][i], in.scale[k]) : 0.0f; };
+    auto scaled = [&](int k, uint32_t i) -> float { return i < n ? mul_f32(in.p[k][i], in.scale[k]) : 0.0f; };
     if (r != 0) {
       const u32x2 v = {__float_as_uint(scaled(r, i0)), __float_as_uint(scaled(r, i1))};
       ll_put<kDevice>(wire, ((uint32_t)(r - 1) * units + u) * 16u, v, epoch);
     } else {
-      double s0 = scaled(0, i0), s1 = scaled(0, i1);
-      for (int k = 1; k < N; ++k) {
-        u32x2 v;
-        Poll poll(spin);
-        if (!ll_wait(wire, ((uint32_t)(k - 1) * units + u) * 16u, epoch, poll, v)) {
+      // poll every sender's line in one pass (all loads in flight) until a
+      // pass finds them all ready; a ready line stays ready for this epoch
+      u32x2 v[N - 1];
+      Poll poll(spin);
+      while (true) {
+        bool all = true;
+#pragma unroll
+        for (int k = 1; k < N; ++k) all &= ll_try(wire, ((uint32_t)(k - 1) * units + u) * 16u, epoch, v[k - 1]);
+        if (all) break;
+        if (poll.expired()) {
           atomicOr(status, 1u);
           return;
         }
-        s0 += (double)__uint_as_float(v[0]);
-        s1 += (double)__uint_as_float(v[1]);
+      }
+      double s0 = scaled(0, i0), s1 = scaled(0, i1);
+#pragma unroll
+      for (int k = 1; k < N; ++k) {
+        s0 += (double)__uint_as_float(v[k - 1][0]);
+        s1 += (double)__uint_as_float(v[k - 1][1]);
       }
       out[i0] = (float)s0;
       if (i1 < n) out[i1] = (float)s1;
