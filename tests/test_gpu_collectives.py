@@ -237,6 +237,20 @@ def test_all_gather_every_rank_count(n_ranks, wire):
                 assert_bits_equal(got[j], want, "N=%d rep %d copy %d" % (n_ranks, rep, j))
 
 
+def test_all_gather_maximum_size_every_copy():
+    """N * count at the Sentinel's 16 MiB limit, every rank's copy."""
+    dt = BF16
+    n_ranks = 8
+    total = 16 << 20
+    cnt = total // 2 // n_ranks
+    with comm_for(n_ranks, dt, total) as c:
+        frags = np.stack([random_bits(3450, r, cnt, "bf16") for r in range(n_ranks)])
+        got = ag_run(c, frags, dt, "sentinel", n_ranks)
+        want = models.all_gather(list(frags), dt, "sentinel")
+        for j in range(n_ranks):
+            assert_bits_equal(got[j], want, "copy %d" % j)
+
+
 # --------------------------------------------------------------------------- composition, epochs, failures
 @pytest.mark.parametrize("wire", WIRES)
 def test_reduce_scatter_then_all_gather_is_the_allreduce(wire):

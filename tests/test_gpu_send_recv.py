@@ -202,3 +202,14 @@ def test_send_recv_argument_errors():
         c.send_recv(a, b, "auto")                        # AUTO picks the Sentinel wire
         torch.cuda.synchronize()
         assert c.device_status()[0] == 0
+
+
+def test_send_recv_maximum_sizes():
+    """The byte limits of both wires: 8 MiB over LL, 16 MiB over the Sentinel."""
+    dt = F32
+    for wire, nbytes in (("ll", 8 << 20), ("sentinel", 16 << 20)):
+        n = nbytes // 4
+        with comm_for(2, dt, nbytes) as c:
+            bits = random_bits(2600, nbytes, n, "fp32")
+            got = send_recv(c, bits, dt, wire)
+            assert_bits_equal(got, models.p2p_transfer(bits, dt, wire), "%s %d bytes" % (wire, nbytes))
