@@ -427,7 +427,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the send/recv, ReduceScatter, AllGather timings")
     ap.add_argument("--sweep", action="store_true")
-    ap.add_argument("--sweep-out", default=os.path.join(ROOT, "gpurun_out", "sweep.json"))
+    ap.add_argument("--sweep-out", default="sweep.json", help="where --sweep writes its rows and fits")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the N ranks are emulated inside a single MI355X "
@@ -543,7 +543,8 @@ def main():
     if args.sweep:
         log("sweep")
         sw = run_sweep(llar.Communicator, args, stream)
-        os.makedirs(os.path.dirname(args.sweep_out), exist_ok=True)
+        if os.path.dirname(args.sweep_out):
+            os.makedirs(os.path.dirname(args.sweep_out), exist_ok=True)
         with open(args.sweep_out, "w") as f:
             json.dump(sw, f, indent=1)
     print(json.dumps(result), flush=True)

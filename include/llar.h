@@ -133,8 +133,9 @@ int llar_send_recv(llar_comm* h, const void* send_buf, void* recv_buf, size_t n_
  *
  * partials: host array of N device pointers, each N * recv_count elements.
  * outs:     host array of N device pointers, each recv_count elements; outs[j]
- *           may be partials[j] + j*recv_count (in place) but must not
- *           overlap any other block that is read.
+ *           may be partials[j] + j*recv_count (in place, when that address is
+ *           16-byte aligned like every pointer here) but must not overlap any
+ *           other block that is read.
  * One launch in which every rank sends its copy of segment j to rank j over
  * the LL or Sentinel wire and rank j sums what arrived with its own copy, in
  * binary64 in rank order with one rounding (deterministic, the same
@@ -234,9 +235,12 @@ int llar_get_option(llar_comm* h, const char* key, long long* value);
 /* Protocol AUTO would run for a message of `bytes` per rank. */
 int llar_select_protocol(llar_comm* h, size_t bytes);
 
-/* Copy `bytes` of the staging region of `protocol` (both parities, layout as
- * documented in the design notes) to host memory; synchronises first.  For
- * tests of flags and packing. */
+/* Copy `bytes` of the staging region of `protocol` to host memory, both
+ * parities, in the kernels' layout: LL [parity][sender 1..N-1][vector][two
+ * 16-byte lines {d0, epoch, d1, epoch}]; Sentinel [parity][sender][16-byte
+ * slot], all-ones when empty; LL128 [parity][128-byte line], slot 0 the
+ * count; pipelined Sentinel [buffer][owner][sender][16-byte slot].
+ * Synchronises first.  For tests of flags and packing. */
 int llar_debug_copy_staging(llar_comm* h, llar_protocol protocol, void* host_dst, size_t bytes);
 /* Size in bytes of that staging region (0 if none). */
 size_t llar_staging_bytes(llar_comm* h, llar_protocol protocol);

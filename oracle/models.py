@@ -18,8 +18,7 @@ in GPU Collectives" (agihunt.info summary), the four protocol paragraphs:
   flag; all 8 atomically add into staging; the line is complete when the flag
   sums to N; about D/N staging; waste about 1.5 % (FP16) and 3 % (FP32).
 
-Readings where the page is silent (each is listed with its reason in the
-design notes): LL words are laid out [data0, epoch, data1, epoch] with a
+Readings where the page is silent: LL words are laid out [data0, epoch, data1, epoch] with a
 monotone non-zero epoch; the sentinel is the all-ones pattern (a negative NaN
 in all three formats) and producers replace a datum equal to it by the
 all-ones-minus-one pattern (still a negative NaN); the LL128 flag is 1.0 in
