@@ -313,15 +313,24 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
   if constexpr (!kAcc16) flag_full = __float_as_uint((float)N);
   else flag_full = E::from_f32((float)N);
   bool dead = idle;  // idle padding workgroup, or a poll timed out
+  // Lines are partitioned by the nominal chunk (not a chunk's length): a
+  // line must belong to the same (owner, slice) in every chunk, or the
+  // implicit credit of one slice would release a line another slice has not
+  // consumed yet.  Elements past the message end are masked.  Owner s holds
+  // lines [s L / N, (s+1) L / N), split evenly into the slices; computed once
+  // (32-bit: L < 2^19 lines and w < 64).
+  const uint32_t L = (a.chunk_elems + K - 1) / K;
+  uint32_t sl0[N], sl1[N];
+#pragma unroll
+  for (int s = 0; s < N; ++s) {
+    const uint32_t o0 = (uint32_t)s * L / (uint32_t)N, o1 = ((uint32_t)s + 1u) * L / (uint32_t)N;
+    sl0[s] = o0 + w * (o1 - o0) / a.slices;
+    sl1[s] = o0 + (w + 1u) * (o1 - o0) / a.slices;
+  }
 
   for (uint32_t c = 0; c < a.n_chunks && !dead; ++c) {
     const uint64_t cbase = (uint64_t)c * a.chunk_elems;
     const uint32_t len = (uint32_t)min((uint64_t)a.chunk_elems, a.n - cbase);
-    // Lines are partitioned by the nominal chunk (not this chunk's length):
-    // a line must belong to the same (owner, slice) in every chunk, or the
-    // implicit credit of one slice would release a line another slice has
-    // not consumed yet.  Elements past the message end are masked.
-    const uint32_t L = (a.chunk_elems + K - 1) / K;
     // lines that hold data of this chunk: producers flag and consumers poll
     // only these (both sides agree, and a line past them stays zero)
     const uint32_t Lr = (len + K - 1) / K;
@@ -330,9 +339,7 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
     // ---- produce: data atomics for every owner's slice w
     const bool silent = ((uint32_t)r == a.drop_rank);
     for (int s = 0; s < N && !silent; ++s) {
-      uint32_t o0 = (uint32_t)((uint64_t)s * L / N), o1 = (uint32_t)((uint64_t)(s + 1) * L / N);
-      uint32_t l0 = o0 + (uint32_t)((uint64_t)w * (o1 - o0) / a.slices);
-      uint32_t l1 = min(o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices), Lr);
+      const uint32_t l0 = sl0[s], l1 = min(sl1[s], Lr);
       for (uint32_t lb = l0 + wave * 8u; lb < l1; lb += n_waves * 8u) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -368,9 +375,7 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
     // data of this wave acknowledged before any of its flags
     drain_vm();
     for (int s = 0; s < N && !silent; ++s) {
-      uint32_t o0 = (uint32_t)((uint64_t)s * L / N), o1 = (uint32_t)((uint64_t)(s + 1) * L / N);
-      uint32_t l0 = o0 + (uint32_t)((uint64_t)w * (o1 - o0) / a.slices);
-      uint32_t l1 = min(o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices), Lr);
+      const uint32_t l0 = sl0[s], l1 = min(sl1[s], Lr);
       for (uint32_t lb = l0 + wave * 8u; lb < l1; lb += n_waves * 8u) {
         uint32_t line = lb + lane;
         if (lane < 8u && line < l1) {
@@ -386,9 +391,15 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
 
     // ---- consume owner r's slice w: 8 lanes per line
     {
-      uint32_t o0 = (uint32_t)((uint64_t)r * L / N), o1 = (uint32_t)((uint64_t)(r + 1) * L / N);
-      uint32_t l0 = o0 + (uint32_t)((uint64_t)w * (o1 - o0) / a.slices);
-      uint32_t l1 = min(o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices), Lr);
+      // owner r's slice w (a runtime index into the bounds: selected, not
+      // indexed, so that the arrays stay in registers)
+      uint32_t l0 = sl0[0], l1 = sl1[0];
+#pragma unroll
+      for (int s = 1; s < N; ++s) {
+        l0 = (s == r) ? sl0[s] : l0;
+        l1 = (s == r) ? sl1[s] : l1;
+      }
+      l1 = min(l1, Lr);
       const uint32_t grp = lane >> 3, j = lane & 7u;
       for (uint32_t lb = l0 + wave * 8u; lb < l1; lb += n_waves * 8u) {
         uint32_t line = lb + grp;
@@ -497,6 +508,18 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
     // ---------------- producer waves
     const uint32_t pl = wave * 64u + lane, PL = n_prod * 64u;
     const bool silent = ((uint32_t)r == a.drop_rank);
+    // slice w of every other owner's shard, the same in every chunk: owner s
+    // holds vectors [s nv / N, (s+1) nv / N) of a chunk, split evenly into
+    // the slices (32-bit: nv < 2^18 vectors and w < 64)
+    uint32_t own0[N > 1 ? N - 1 : 1], sl0[N > 1 ? N - 1 : 1], sl1[N > 1 ? N - 1 : 1];
+#pragma unroll
+    for (int k = 0; k < N - 1; ++k) {
+      const uint32_t s = (uint32_t)(k < r ? k : k + 1);
+      const uint32_t o0 = s * nv / (uint32_t)N, o1 = (s + 1u) * nv / (uint32_t)N;
+      own0[k] = o0;
+      sl0[k] = o0 + w * (o1 - o0) / a.slices;
+      sl1[k] = o0 + (w + 1u) * (o1 - o0) / a.slices;
+    }
     for (uint32_t c = 0; c < a.n_chunks && !dead; ++c) {
       const uint64_t vbase = (uint64_t)c * chunk_vecs;
       // vectors of this chunk that exist; the partition below uses the
@@ -510,15 +533,11 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
         uint32_t vo[N > 1 ? N - 1 : 1][kU];  // vector offset inside the owner's shard, or ~0
 #pragma unroll
         for (int k = 0; k < N - 1; ++k) {
-          const int s = k < r ? k : k + 1;
-          const uint32_t o0 = (uint32_t)((uint64_t)s * nv / N), o1 = (uint32_t)((uint64_t)(s + 1) * nv / N);
-          const uint32_t s0 = o0 + (uint32_t)((uint64_t)w * (o1 - o0) / a.slices);
-          const uint32_t s1 = o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices);
 #pragma unroll
           for (int u = 0; u < kU; ++u) {
-            const uint32_t v = s0 + b0 + pl + (uint32_t)u * PL;
-            const bool ok = (v < s1) && (v < nv_real);
-            vo[k][u] = ok ? v - o0 : ~0u;
+            const uint32_t v = sl0[k] + b0 + pl + (uint32_t)u * PL;
+            const bool ok = (v < sl1[k]) && (v < nv_real);
+            vo[k][u] = ok ? v - own0[k] : ~0u;
             x[k][u] = ok ? load_vec(src, vbase + v, nbytes) : u32x4{0u, 0u, 0u, 0u};
           }
         }
@@ -556,9 +575,9 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
     const uint32_t cw = wave - n_prod;
     const uint32_t cl = cw * 64u + lane, CL = n_cons * 64u;
     const uint32_t nv = chunk_vecs;
-    const uint32_t o0 = (uint32_t)((uint64_t)r * nv / N), o1 = (uint32_t)((uint64_t)(r + 1) * nv / N);
-    const uint32_t s0 = o0 + (uint32_t)((uint64_t)w * (o1 - o0) / a.slices);
-    const uint32_t s1n = o0 + (uint32_t)((uint64_t)(w + 1) * (o1 - o0) / a.slices);
+    const uint32_t o0 = (uint32_t)r * nv / (uint32_t)N, o1 = ((uint32_t)r + 1u) * nv / (uint32_t)N;
+    const uint32_t s0 = o0 + w * (o1 - o0) / a.slices;
+    const uint32_t s1n = o0 + (w + 1u) * (o1 - o0) / a.slices;
     // own vectors of the first batch of the next chunk, requested early
     u32x4 own_next[kUc];
 #pragma unroll
