@@ -33,6 +33,12 @@
  *   - Device pointers are HIP device allocations on the device that was
  *     current when the communicator was created.
  *   - Streams are hipStream_t passed as void* (0 = the null stream).
+ *   - Workgroups of one call wait on each other, so a call needs all of its
+ *     workgroups resident at once: the library checks that its grid fits the
+ *     device's occupancy, but kernels from other streams that fill the GPU
+ *     at the same time can keep some of them out.  The waits are bounded
+ *     ("spin_timeout_us"), so such a call ends with LLAR_ERR_TIMEOUT in the
+ *     status word instead of hanging.
  */
 #ifndef LLAR_H
 #define LLAR_H
