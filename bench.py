@@ -176,6 +176,22 @@ def measure_rows(stream, steps):
     import torch
     import message_allreduce_amd as llar
     rows = {}
+    # the pages' smallest case: two ranks, 128 bytes of fp32, LL one-shot
+    c1 = llar.Communicator(2, torch.float32, 128)
+    try:
+        p1 = [torch.randn(32, dtype=torch.float32, device="cuda") for _ in range(2)]
+        o1 = torch.empty(32, dtype=torch.float32, device="cuda")
+        fn = (lambda: c1.allreduce(p1, o1, "ll", stream=stream))
+        us = time_graph_fn(fn, steps, stream)
+        dmed, dmin = device_side_fn(c1, fn, 60, stream)
+        rows["allreduce_128B_x2_fp32_ll"] = {"us_per_call_graph": round(us, 3), "device_us_median": round(dmed, 3),
+                                             "device_us_min": round(dmin, 3)}
+        log("allreduce 128 B x 2 fp32 ll: %.3f us per call (graph), device %.3f us" % (us, dmed))
+        st, bits = c1.device_status()
+        if st != 0:
+            raise RuntimeError("device status %d (bits %#x) in the 128 B timing" % (st, bits))
+    finally:
+        c1.close()
     c2 = llar.Communicator(2, torch.float16, 8192)
     try:
         send = torch.randn(4096, dtype=torch.float16, device="cuda")
