@@ -209,8 +209,10 @@ int llar_clear_device_status(llar_comm* h);
  *   "threads"          threads per workgroup: 64, 128, 256 or 512, or 1024 for the slot-handshake
  *                      Sentinel (0 = tuned default); the pipelined Sentinel splits a workgroup into
  *                      producer and consumer waves and needs at least 128
- *   "pipeline_buffers" staging buffers of the pipelined Sentinel: 2, 4 (default), 6 or 8; with B
- *                      buffers a producer runs up to B/2 - 1 chunks ahead of its consumer
+ *   "pipeline_buffers" staging buffers of the pipelined Sentinel: even, 2 to 64 (default 4), as many
+ *                      as fit the staging allocated for the largest chunk (a call that needs more
+ *                      returns LLAR_ERR_UNSUPPORTED); with B buffers a producer runs up to B/2 - 1
+ *                      chunks ahead of its consumer
  *   "placement"        0 = auto, 1 = spread (rank r on XCD r mod 8), 2 = local (one slice's ranks share an XCD);
  *                      auto: local for the LL and Sentinel AllReduce and send/recv, spread for LL128, and
  *                      for ReduceScatter / AllGather local from 8 slices per rank up, spread below

@@ -82,7 +82,7 @@ struct llar_comm {
   long long debug_drop_rank = -1;
   long long trace_on = 0;
   long long device_epoch = 0;  // 1: always read the device-resident epoch
-  long long pipe_buffers = 4;  // staging buffers of the pipelined Sentinel (2, 4, 6 or 8)
+  long long pipe_buffers = 4;  // staging buffers of the pipelined Sentinel (even, 2..64; they must fit the region)
   long long sentinel_credit = 0;  // pipelined Sentinel: 0 = workgroup credit, 1 = slot handshake
   long long cons_waves = 0;       // slot handshake: consumer waves per workgroup (0 = a quarter)
   long long barrier_ablation = 0;  // 1: LL/Sentinel AllReduce behind a grid-wide barrier (measurement)
@@ -541,6 +541,14 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
     a.shard_cap = (proto == LLAR_SENTINEL_PIPELINED)
                       ? (uint32_t)(reg->parity_stride / ((size_t)h->n_ranks * h->n_ranks * 16))
                       : 0u;
+    if (g.kernel == kKernSentinelPipe || g.kernel == kKernSentinelPipeLocal) {
+      // buffers spaced by this chunk's own stride, so that small chunks can
+      // use more of them in the same region
+      a.shard_cap = sentinel_shard_cap((size_t)g.chunk_elems * h->elem, h->n_ranks);
+      const size_t stride = (size_t)h->n_ranks * h->n_ranks * a.shard_cap * 16;
+      if (stride * a.n_buffers > reg->bytes) return fail(LLAR_ERR_UNSUPPORTED);
+      a.parity_stride = (uint32_t)stride;
+    }
     if (g.kernel == kKernSentinelHs || g.kernel == kKernSentinelHsLocal) {
       // Slot handshake: the chunk-c and chunk-(c - B) uses of a slot are
       // consumer items c*n_bat + b and (c - B)*n_bat + b, taken by consumer
@@ -867,8 +875,7 @@ int llar_set_option(llar_comm* h, const char* key, long long value) {
                                         value == 1024))
     return fail(LLAR_ERR_ARG);
   if (strcmp(key, "placement") == 0 && (value < 0 || value > 2)) return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "pipeline_buffers") == 0 && !(value == 2 || value == 4 || value == 6 || value == 8))
-    return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "pipeline_buffers") == 0 && !(value >= 2 && value <= 64 && value % 2 == 0)) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "sentinel_credit") == 0 && (value < 0 || value > 1)) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "consumer_waves") == 0 && (value < 0 || value > 15)) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "placement") == 0 && value == 2 && !h->local_ok) return fail(LLAR_ERR_UNSUPPORTED);

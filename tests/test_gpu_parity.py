@@ -319,7 +319,7 @@ def test_sentinel_pipelined_chunks_and_placements(placement, chunk):
         assert (c.staging(llar.SENTINEL_PIPELINED) == 0xFF).all()
 
 
-@pytest.mark.parametrize("buffers", [2, 4, 6, 8])
+@pytest.mark.parametrize("buffers", [2, 4, 6, 8, 16, 32])
 def test_sentinel_pipelined_buffers_and_credit_order(buffers):
     """Every staging-buffer count gives the exact sum, and the per-chunk
     stamps of each workgroup follow the credit rule: with B buffers the
