@@ -14,10 +14,15 @@
 //
 // Sources (prose of "Every Microsecond Matters", agihunt.info summary):
 //   LL paragraph        -> k_oneshot<kWireLL>
-//   Sentinel paragraph  -> k_oneshot<kWireSentinel>, k_twoshot_sentinel
-//   bidirectional + double buffering paragraph -> the chunk loop of the
-//                          two-shot kernels (parity = chunk & 1, implicit credit)
+//   Sentinel paragraph  -> k_oneshot<kWireSentinel>, k_twoshot_sentinel,
+//                          k_twoshot_sentinel_hs
+//   bidirectional + double buffering paragraph -> the chunk loops of the
+//                          two-shot kernels (LL128: parity = chunk & 1 with an
+//                          implicit credit; Sentinel: B rotating buffers)
 //   Two-shot LL128 paragraph -> k_twoshot_ll128
+// The staging accesses use the primitives of include/llar_wire.h.  The
+// ReduceScatter / AllGather kernels and the barrier ablation live in
+// llar_multi.hip.
 #include "llar_device.h"
 #include "llar_internal.h"
 
