@@ -202,6 +202,25 @@ def test_reduce_scatter_ll128_maximum_size_and_allreduce_interleaving():
         assert not c.staging(llar.LL128).any()
 
 
+def test_reduce_scatter_ll128_keep_staging_matches_segment_line_model():
+    """Owner o's lines hold exactly segment o: with integer data every atomic
+    order stages the same sums, so the kept staging must equal, bit for bit,
+    the page's line model applied to each segment, owners back to back, with
+    every count at N."""
+    dt = BF16
+    n_ranks, cnt = 4, 100  # 100 = 3 full lines of 31 and a ragged fourth
+    bits = make_partials(4400, 0, n_ranks, "bf16", n_ranks * cnt, "integer", 1.0)
+    with comm_for(n_ranks, dt, n_ranks * cnt * 2, keep_staging=1) as c:
+        rs_run(c, bits, dt, "ll128")
+        model = np.concatenate([models.ll128_staging_image(bits[:, o * cnt:(o + 1) * cnt], dt, F32)
+                                for o in range(n_ranks)])
+        lines = model.shape[0]
+        stage = c.staging(llar.LL128)[: lines * 128].view(np.float32).reshape(lines, 32)
+        assert np.array_equal(stage.astype(np.float64), model)
+        assert (stage[:, 0] == n_ranks).all()
+        c.set_option("keep_staging", 0)
+
+
 # --------------------------------------------------------------------------- AllGather
 @pytest.mark.parametrize("replicated", [False, True], ids=["rank0", "every_rank"])
 @pytest.mark.parametrize("placement", [1, 2], ids=["spread", "local"])
