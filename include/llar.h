@@ -207,12 +207,23 @@ int llar_clear_device_status(llar_comm* h);
  *                      upper bound: every owner slice of a full chunk keeps at least one line
  *                      (LL128) or vector (Sentinel), because the credit is earned by consuming
  *   "threads"          threads per workgroup: 64, 128, 256 or 512, or 1024 for the slot-handshake
- *                      Sentinel (0 = tuned default); the pipelined Sentinel splits a workgroup into
- *                      producer and consumer waves and needs at least 128
- *   "pipeline_buffers" staging buffers of the pipelined Sentinel: even, 2 to 64 (default 4), as many
- *                      as fit the staging allocated for the largest chunk (a call that needs more
- *                      returns LLAR_ERR_UNSUPPORTED); with B buffers a producer runs up to B/2 - 1
- *                      chunks ahead of its consumer
+ *                      and owner-credit Sentinel pipelines (0 = tuned default); the pipelined
+ *                      Sentinel splits a workgroup into producer and consumer waves and needs at
+ *                      least 128
+ *   "pipeline_buffers" staging buffers of the pipelined Sentinel: 2 to 64 (default 4), as many as
+ *                      fit the staging allocated for the largest chunk (a call that needs more
+ *                      returns LLAR_ERR_UNSUPPORTED).  Workgroup credit: an even count, and a
+ *                      producer runs up to B/2 - 1 chunks ahead of its consumer; owner credit: any
+ *                      count, B - 1 chunks ahead; slot handshake: rounded up to a multiple of its
+ *                      wave period
+ *   "sentinel_credit"  credit of the pipelined Sentinel: 0 = workgroup credit (default: a producer
+ *                      stores chunk c once its own workgroup's consumers finished chunk c - B/2);
+ *                      1 = slot handshake (a producer stores into a slot once it reads the owner's
+ *                      reset there); 2 = owner credit (every owner's consumer waves publish a
+ *                      progress word; a producer stores chunk c once every owner finished c - B)
+ *   "consumer_waves"   slot handshake and owner credit: consumer waves per workgroup (0 = default:
+ *                      a quarter of the waves for the handshake, (waves - 1) / 2 for the owner
+ *                      credit, which keeps one wave to read the progress words; at most 8 there)
  *   "placement"        0 = auto, 1 = spread (rank r on XCD r mod 8), 2 = local (one slice's ranks share an XCD);
  *                      auto: local for the LL and Sentinel AllReduce and send/recv, spread for LL128, and
  *                      for ReduceScatter / AllGather local from 8 slices per rank up, spread below

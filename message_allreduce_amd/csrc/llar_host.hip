@@ -67,6 +67,7 @@ struct llar_comm {
   uint64_t* trace = nullptr;  // kTraceMaxWgs x kTraceWords stamps of the last traced one-shot call
   int trace_grid = 0;
   uint64_t* pipe_trace = nullptr;  // kPipeTraceMaxWgs x kPipeTraceWords stamps of the last traced pipeline call
+  uint64_t* credit = nullptr;      // kCreditWords progress words of the pipelined Sentinel's owner credit
   int pipe_trace_grid = 0;
   uint32_t host_epoch = 1;         // epoch of the next host-numbered call
   bool last_call_device = false;   // the last call read the device-resident epoch
@@ -82,8 +83,8 @@ struct llar_comm {
   long long debug_drop_rank = -1;
   long long trace_on = 0;
   long long device_epoch = 0;  // 1: always read the device-resident epoch
-  long long pipe_buffers = 4;  // staging buffers of the pipelined Sentinel (even, 2..64; they must fit the region)
-  long long sentinel_credit = 0;  // pipelined Sentinel: 0 = workgroup credit, 1 = slot handshake
+  long long pipe_buffers = 4;  // staging buffers of the pipelined Sentinel (2..64, even for the workgroup credit; they must fit the region)
+  long long sentinel_credit = 0;  // pipelined Sentinel: 0 = workgroup credit, 1 = slot handshake, 2 = owner credit
   long long cons_waves = 0;       // slot handshake: consumer waves per workgroup (0 = a quarter)
   long long barrier_ablation = 0;  // 1: LL/Sentinel AllReduce behind a grid-wide barrier (measurement)
   long long thr_sentinel = 64ll << 10;    // AUTO: LL up to (<=) this many bytes
@@ -126,6 +127,9 @@ hipError_t reset_staging(llar_comm* h) {
   if (h->ll128.ptr && (e = hipMemset(h->ll128.ptr, 0, h->ll128.bytes)) != hipSuccess) return e;
   if (h->ll128_pipe.ptr && (e = hipMemset(h->ll128_pipe.ptr, 0, h->ll128_pipe.bytes)) != hipSuccess) return e;
   if (h->sent_pipe.ptr && (e = hipMemset(h->sent_pipe.ptr, 0xFF, h->sent_pipe.bytes)) != hipSuccess) return e;
+  // progress words carry the epoch of the call that wrote them, and the
+  // device-resident epoch restarts with the control block
+  if (h->credit && (e = hipMemset(h->credit, 0, kCreditWords * sizeof(uint64_t))) != hipSuccess) return e;
   return hipDeviceSynchronize();
 }
 
@@ -146,6 +150,8 @@ void destroy_all(llar_comm* h) {
   h->timing_wg = nullptr;
   if (h->pipe_trace) (void)hipFree(h->pipe_trace);
   h->pipe_trace = nullptr;
+  if (h->credit) (void)hipFree(h->credit);
+  h->credit = nullptr;
   delete h;
 }
 
@@ -223,18 +229,20 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
     }
     case LLAR_SENTINEL_PIPELINED: {
       size_t cb = effective_chunk(h, proto);
-      g.kernel = h->sentinel_credit ? kKernSentinelHs : kKernSentinelPipe;
+      g.kernel = h->sentinel_credit == 1 ? kKernSentinelHs : h->sentinel_credit == 2 ? kKernSentinelOc : kKernSentinelPipe;
       g.chunk_elems = (uint32_t)(cb / h->elem);
       g.chunks = (int)ceil_div(n_elems, (size_t)g.chunk_elems);
       size_t vecs = ceil_div(std::min(cb, nbytes), 16);
       size_t per_owner = ceil_div(vecs, (size_t)N);
       // half the waves produce, half consume: one owner-slice vector per
       // consumer lane per chunk
-      g.threads = h->threads ? (int)h->threads : (h->sentinel_credit ? 1024 : 512);
+      g.threads = h->threads ? (int)h->threads : (h->sentinel_credit != 0 ? 1024 : 512);
       if (g.threads < 128) return LLAR_ERR_ARG;
       // measured on MI355X (64 MiB x 8 bf16): 1 MiB chunks, 512 threads and
       // 32 slices per rank (one workgroup per CU) stream best
       g.slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(per_owner, (size_t)g.threads / 2), 1, 32);
+      // owner credit: one 64-vector batch per slice of an owner's shard
+      if (g.kernel == kKernSentinelOc && !h->slices) g.slices = clampi((long long)ceil_div(per_owner, 64), 1, 32);
       if (g.chunks > 1) {
         // the credit is earned by consuming: every owner slice of a full
         // chunk must hold at least one vector
@@ -258,13 +266,16 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
     g.grid_slices = (int)ceil_div((size_t)g.slices, 8) * 8;
     if (g.kernel == kKernSentinelPipe) g.kernel = kKernSentinelPipeLocal;
     if (g.kernel == kKernSentinelHs) g.kernel = kKernSentinelHsLocal;
+    if (g.kernel == kKernSentinelOc) g.kernel = kKernSentinelOcLocal;
     if (g.kernel == kKernOneShotLL) g.kernel = kKernOneShotLLLocal;
     if (g.kernel == kKernOneShotSentinel) g.kernel = kKernOneShotSentinelLocal;
   }
   g.placement = place;
   if (g.threads != 64 && g.threads != 128 && g.threads != 256 && g.threads != 512 && g.threads != 1024)
     return LLAR_ERR_ARG;
-  if (g.threads == 1024 && g.kernel != kKernSentinelHs && g.kernel != kKernSentinelHsLocal) return LLAR_ERR_ARG;
+  if (g.threads == 1024 && g.kernel != kKernSentinelHs && g.kernel != kKernSentinelHsLocal &&
+      g.kernel != kKernSentinelOc && g.kernel != kKernSentinelOcLocal)
+    return LLAR_ERR_ARG;
   return LLAR_OK;
 }
 
@@ -376,6 +387,8 @@ llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes) {
   if (e == hipSuccess) e = hipMemset(h->trace, 0, (size_t)kTraceMaxWgs * kTraceWords * sizeof(uint64_t));
   if (e == hipSuccess) e = hipMalloc(&h->pipe_trace, (size_t)kPipeTraceMaxWgs * kPipeTraceWords * sizeof(uint64_t));
   if (e == hipSuccess) e = hipMemset(h->pipe_trace, 0, (size_t)kPipeTraceMaxWgs * kPipeTraceWords * sizeof(uint64_t));
+  if (e == hipSuccess) e = hipMalloc(&h->credit, kCreditWords * sizeof(uint64_t));
+  if (e == hipSuccess) e = hipMemset(h->credit, 0, kCreditWords * sizeof(uint64_t));
   if (e == hipSuccess) e = alloc_region(h->ll, 2 * h->ll.parity_stride, 0);
   if (e == hipSuccess) e = alloc_region(h->sent, 2 * h->sent.parity_stride, 0xFF);
   if (e == hipSuccess) e = alloc_region(h->ll128, 2 * h->ll128.parity_stride, 0);
@@ -541,7 +554,10 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
     a.shard_cap = (proto == LLAR_SENTINEL_PIPELINED)
                       ? (uint32_t)(reg->parity_stride / ((size_t)h->n_ranks * h->n_ranks * 16))
                       : 0u;
+    a.credit = nullptr;
     if (g.kernel == kKernSentinelPipe || g.kernel == kKernSentinelPipeLocal) {
+      // the workgroup credit needs an even buffer count (B >= 2 lag + 2)
+      if (a.n_buffers % 2u != 0u) return fail(LLAR_ERR_ARG);
       // buffers spaced by this chunk's own stride, so that small chunks can
       // use more of them in the same region
       a.shard_cap = sentinel_shard_cap((size_t)g.chunk_elems * h->elem, h->n_ranks);
@@ -577,6 +593,22 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
       if (stride * a.n_buffers > reg->bytes) return fail(LLAR_ERR_UNSUPPORTED);
       a.parity_stride = (uint32_t)stride;
     }
+    if (g.kernel == kKernSentinelOc || g.kernel == kKernSentinelOcLocal) {
+      // owner credit: one progress word per (rank, slice, consumer wave);
+      // one wave of each workgroup reads them, the rest produce
+      const uint32_t n_waves = (uint32_t)g.threads / 64u;
+      const uint32_t n_cons = h->cons_waves > 0 ? (uint32_t)h->cons_waves : (n_waves - 1u) / 2u;
+      if (n_cons < 1u || n_cons > (uint32_t)kCreditWaves || n_cons + 2u > n_waves) return fail(LLAR_ERR_ARG);
+      if (g.slices > kCreditSlices) return fail(LLAR_ERR_UNSUPPORTED);
+      // kept staging is never reset, so no buffer may be used twice
+      if (h->keep_staging && g.chunks > (int)a.n_buffers) return fail(LLAR_ERR_UNSUPPORTED);
+      a.cons_waves = n_cons;
+      a.credit = h->credit;
+      a.shard_cap = sentinel_shard_cap((size_t)g.chunk_elems * h->elem, h->n_ranks);
+      const size_t stride = (size_t)h->n_ranks * h->n_ranks * a.shard_cap * 16;
+      if (stride * a.n_buffers > reg->bytes) return fail(LLAR_ERR_UNSUPPORTED);
+      a.parity_stride = (uint32_t)stride;
+    }
     a.grid = (uint32_t)ls.grid;
     a.slices = (uint32_t)g.slices;
     a.placement = g.placement;
@@ -586,7 +618,8 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
     a.host_epoch = host_epoch;
     a.trace = nullptr;
     const bool pipe_kernel = g.kernel == kKernSentinelPipe || g.kernel == kKernSentinelPipeLocal ||
-                             g.kernel == kKernSentinelHs || g.kernel == kKernSentinelHsLocal;
+                             g.kernel == kKernSentinelHs || g.kernel == kKernSentinelHsLocal ||
+                             g.kernel == kKernSentinelOc || g.kernel == kKernSentinelOcLocal;
     if (h->trace_on && pipe_kernel && ls.grid <= kPipeTraceMaxWgs) {
       a.trace = h->pipe_trace;
       h->pipe_trace_grid = ls.grid;
@@ -875,8 +908,8 @@ int llar_set_option(llar_comm* h, const char* key, long long value) {
                                         value == 1024))
     return fail(LLAR_ERR_ARG);
   if (strcmp(key, "placement") == 0 && (value < 0 || value > 2)) return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "pipeline_buffers") == 0 && !(value >= 2 && value <= 64 && value % 2 == 0)) return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "sentinel_credit") == 0 && (value < 0 || value > 1)) return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "pipeline_buffers") == 0 && !(value >= 2 && value <= 64)) return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "sentinel_credit") == 0 && (value < 0 || value > 2)) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "consumer_waves") == 0 && (value < 0 || value > 15)) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "placement") == 0 && value == 2 && !h->local_ok) return fail(LLAR_ERR_UNSUPPORTED);
   if ((strcmp(key, "timing") == 0 || strcmp(key, "keep_staging") == 0 || strcmp(key, "trace") == 0 ||

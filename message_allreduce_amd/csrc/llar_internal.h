@@ -53,9 +53,14 @@ enum KernelId : int {
   // ablation: the one-shot reduce with a grid-wide barrier instead of flags
   kKernBarrier = 24,
   kKernBarrierLocal = 25,
-  kKernCount = 26
+  // pipelined Sentinel with the owner credit (llar_kernels.hip)
+  kKernSentinelOc = 26,
+  kKernSentinelOcLocal = 27,
+  kKernCount = 28
 };
 constexpr int kKernFirstMulti = kKernRsLL;
+// kernels that live in llar_multi.hip
+constexpr bool is_multi_kernel(int k) { return k >= kKernFirstMulti && k <= kKernBarrierLocal; }
 
 struct OneShotArgs {
   const uint8_t* part[8];
@@ -101,6 +106,7 @@ struct TwoShotArgs {
   uint32_t drop_rank;
   uint32_t host_epoch;
   uint64_t* trace;       // per-workgroup, per-chunk stamps (kPipeTraceWords each), or null
+  uint64_t* credit;      // Sentinel pipeline, owner credit: [rank][slice][consumer wave] progress, or null
 };
 
 // ReduceScatter / AllGather over the LL or Sentinel wire.  A block is what
@@ -134,6 +140,10 @@ struct MultiArgs {
 // ready, consumer done) of the first kPipeTraceChunks chunks
 constexpr int kPipeTraceChunks = 128;
 constexpr int kPipeTraceWords = 4 * kPipeTraceChunks;
+// owner credit of the pipelined Sentinel: one progress word per (rank, slice,
+// consumer wave)
+constexpr int kCreditSlices = 64, kCreditWaves = 8;
+constexpr size_t kCreditWords = (size_t)8 * kCreditSlices * kCreditWaves;
 
 // phase trace of the one-shot kernel: per workgroup, thread 0 records
 constexpr int kTraceWords = 8;  // start, epoch, input, ready, out-acked, end, id, spare

@@ -15,10 +15,11 @@
 // Sources (prose of "Every Microsecond Matters", agihunt.info summary):
 //   LL paragraph        -> k_oneshot<kWireLL>
 //   Sentinel paragraph  -> k_oneshot<kWireSentinel>, k_twoshot_sentinel,
-//                          k_twoshot_sentinel_hs
+//                          k_twoshot_sentinel_hs, k_twoshot_sentinel_oc
 //   bidirectional + double buffering paragraph -> the chunk loops of the
 //                          two-shot kernels (LL128: parity = chunk & 1 with an
-//                          implicit credit; Sentinel: B rotating buffers)
+//                          implicit credit; Sentinel: B rotating buffers with
+//                          a workgroup, slot or owner credit)
 //   Two-shot LL128 paragraph -> k_twoshot_ll128
 // The staging accesses use the primitives of include/llar_wire.h.  The
 // ReduceScatter / AllGather kernels and the barrier ablation live in
@@ -925,6 +926,296 @@ __global__ void __launch_bounds__(1024) k_twoshot_sentinel_hs(TwoShotArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// two-shot Sentinel, chunked, owner credit (progress words in memory)
+// ---------------------------------------------------------------------------
+// Staging: [buffer][owner s][sender k][vector of s's shard] 16 B, all-ones
+// when empty; chunk c uses buffer c % B.  Every rank stages its whole slice,
+// its own shard included, so no wave that polls ever has an HBM load queued
+// in front of its polls (a wave's vector memory operations complete in
+// order: one HBM load ahead of a poll delays the poll's answer by an HBM
+// latency).  Owner shards and slices split the nominal chunk evenly, so a
+// slot keeps its (owner, slice) in every chunk.
+// A 1024-thread workgroup (r, w) has three roles:
+//   producer waves: (chunk, batch) pairs dealt round-robin; a pair loads
+//            rank r's vectors of slice w of every owner's shard (one per
+//            owner per lane), and stores them into [c % B][s][r] once the
+//            chunk is free (below); two pairs in flight per wave;
+//   credit wave: reads the progress word of every (owner s, consumer wave)
+//            of slice w and publishes in LDS the first chunk that some owner
+//            has not consumed yet; chunk c is free once that is > c - B;
+//   consumer waves: whole chunks dealt round-robin; for each vector of
+//            owner r's slice w, poll the N slots, add them in binary64 in
+//            rank order, round, write `out` and reset the slots; after the
+//            chunk, drain (the resets are performed) and advance the wave's
+//            progress word (tagged with the call's epoch).
+// Chunk c reuses the buffer of chunk c - B only after every owner has
+// consumed chunk c - B and its resets were performed, so B buffers give a
+// run-ahead of B - 1 chunks (a credit read from the owners themselves, not
+// inferred from this workgroup's own consumers).
+template <int kKind, int N, bool kLocal>
+__global__ void __launch_bounds__(1024) k_twoshot_sentinel_oc(TwoShotArgs a) {
+  constexpr uint32_t kOff = 0x80000000u;  // an offset past every buffer
+  int r;
+  uint32_t w;
+  decode_role_t<kLocal, N>(blockIdx.x, r, w);
+  // every kernel argument, requested at entry as one batch
+  const uint8_t* src = a.part[r];
+  LLAR_UNIFORM_AT_ENTRY("s"(src), "s"(a.out), "s"(a.stage), "s"(a.ctrl), "s"(a.n), "s"(a.spin_limit),
+                        "s"(a.chunk_elems), "s"(a.n_chunks), "s"(a.stage_bytes), "s"(a.parity_stride),
+                        "s"(a.shard_cap), "s"(a.n_buffers), "s"(a.grid), "s"(a.slices), "s"(a.timing), "s"(a.keep),
+                        "s"(a.drop_rank), "s"(a.host_epoch), "s"(a.cons_waves), "s"(a.credit));
+  const bool idle = (w >= a.slices);
+  WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
+  using E = Elem<kKind>;
+  __shared__ uint32_t s_free;     // every owner has consumed all chunks below this
+  __shared__ uint32_t s_cons[8];  // chunks each consumer wave of this workgroup has finished
+  if (threadIdx.x == 0) s_free = 0u;
+  if (threadIdx.x < 8) s_cons[threadIdx.x] = 0u;
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.stage, a.stage_bytes);
+  const uint64_t nbytes = a.n * (uint64_t)E::kBytes;
+  const uint32_t nv = (uint32_t)(((uint64_t)a.chunk_elems * E::kBytes) / 16u);  // chunks are whole vectors
+  const uint64_t full_vecs = nbytes / 16u;
+  const bool has_tail = (nbytes % 16u) != 0u;  // vector full_vecs is partial
+  const uint32_t slot_bytes = a.shard_cap * 16u;
+  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
+  const uint32_t n_cons = a.cons_waves, n_prod = n_waves - n_cons - 1u;
+  const uint32_t n_buf = a.n_buffers, n_chunks = a.n_chunks;
+  const uint32_t reset_off = a.keep ? kOff : 0u;  // tests: keep the staged data
+  const u32x4 kEmpty = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  // owner s's shard of a chunk is [o0, o1) = [s nv / N, (s+1) nv / N); slice
+  // w of it is [o0 + w len / W, o0 + (w+1) len / W), len = o1 - o0 (32-bit:
+  // nv < 2^18 vectors, W <= 64)
+  const uint32_t span = ((nv + N - 1u) / N + a.slices - 1u) / a.slices;  // longest slice
+  auto slice_of = [&](uint32_t s, uint32_t& o0, uint32_t& s0, uint32_t& s1) {
+    o0 = s * nv / (uint32_t)N;
+    const uint32_t len = (s + 1u) * nv / (uint32_t)N - o0;
+    s0 = o0 + w * len / a.slices;
+    s1 = o0 + (w + 1u) * len / a.slices;
+  };
+  // chunk c's whole vectors (the partial last vector is moved on its own)
+  auto whole_in = [&](uint32_t c) -> uint32_t {
+    const uint64_t vb = (uint64_t)c * nv;
+    return (uint32_t)min((uint64_t)nv, full_vecs > vb ? full_vecs - vb : 0u);
+  };
+  const uint32_t tail_c = (uint32_t)(full_vecs / nv), tail_v = (uint32_t)(full_vecs % nv);
+  bool dead = idle;
+  uint64_t* tr = (a.trace && !idle) ? a.trace + (uint64_t)blockIdx.x * kPipeTraceWords : nullptr;
+  auto stamp = [&](int kind, uint32_t c) {
+    if (tr && lane == 0 && c < (uint32_t)kPipeTraceChunks) tr[kind * kPipeTraceChunks + c] = wall_ticks();
+  };
+
+  if (wave < n_prod) {
+    // ---------------- producer waves
+    const bool silent = ((uint32_t)r == a.drop_rank);
+    const uint32_t n_bat = (span + 63u) / 64u;  // 64-vector batches of a slice
+    const uint32_t n_pairs = (dead || silent) ? 0u : n_chunks * n_bat;
+    uint32_t o0s[N], sl0[N], sl1[N];
+#pragma unroll
+    for (int s = 0; s < N; ++s) slice_of((uint32_t)s, o0s[s], sl0[s], sl1[s]);
+    struct Set {
+      u32x4 x[N];
+      uint32_t off[N];  // slot offsets, or kOff
+      uint32_t c, b0;
+    };
+    auto issue = [&](uint32_t pair, Set& S) {
+      const uint32_t c = pair / n_bat, b0 = (pair % n_bat) * 64u;
+      S.c = c;
+      S.b0 = b0;
+      const uint64_t cb = (uint64_t)c * nv * 16u;
+      const uint32_t nfull = whole_in(c);
+      const __amdgpu_buffer_rsrc_t rin = make_rsrc(src + cb, nfull * 16u);
+      const uint32_t boff = (c % n_buf) * a.parity_stride + (uint32_t)r * slot_bytes;
+      uint32_t vin[N];
+#pragma unroll
+      for (int s = 0; s < N; ++s) {
+        const uint32_t v = sl0[s] + b0 + lane;
+        const bool ok = (v < sl1[s]) && (v < nfull);
+        S.off[s] = ok ? boff + (uint32_t)(s * N) * slot_bytes + (v - o0s[s]) * 16u : kOff;
+        vin[s] = ok ? v * 16u : kOff;
+      }
+#pragma unroll
+      for (int s = 0; s < N; ++s) S.x[s] = __builtin_amdgcn_raw_buffer_load_b128(rin, vin[s], 0, kCpolNt);
+      // keep these loads here: the compiler would otherwise sink them to
+      // their first use and only one pair would be in flight
+      asm volatile("" ::: "memory");
+    };
+    // chunk c may be staged once every owner has consumed chunk c - B
+    auto wait_free = [&](uint32_t c) -> bool {
+      if (c < n_buf) return true;
+      SpinBulk spin(a.spin_limit);
+      while (__hip_atomic_load(&s_free, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + n_buf <= c) {
+        if (spin.expired()) {
+          raise_status(a.ctrl, kStatusTimeout);
+          return false;
+        }
+      }
+      return true;
+    };
+    auto commit = [&](const Set& S) -> bool {
+      if (!wait_free(S.c)) return false;
+      if (S.b0 == 0u) stamp(0, S.c);
+#pragma unroll
+      for (int s = 0; s < N; ++s) st16_stage<kLocal>(rs, S.off[s], sentinel_canon<kKind>(S.x[s]));
+      if (S.b0 == 0u) stamp(1, S.c);
+      return true;
+    };
+    Set A, B;
+    uint32_t pair = wave;
+    if (pair < n_pairs) issue(pair, A);
+    for (; pair < n_pairs; pair += 2u * n_prod) {
+      if (pair + n_prod < n_pairs) issue(pair + n_prod, B);
+      if (!commit(A)) {
+        dead = true;
+        break;
+      }
+      if (pair + n_prod >= n_pairs) break;
+      if (pair + 2u * n_prod < n_pairs) issue(pair + 2u * n_prod, A);
+      if (!commit(B)) {
+        dead = true;
+        break;
+      }
+    }
+    // the partial last vector, by the lane whose pair covers its position
+    if (has_tail && !dead && !silent) {
+#pragma unroll
+      for (int s = 0; s < N; ++s) {
+        if (tail_v < sl0[s] || tail_v >= sl1[s]) continue;
+        const uint32_t i = tail_v - sl0[s];
+        if ((tail_c * n_bat + i / 64u) % n_prod != wave || i % 64u != lane) continue;
+        const u32x4 x = load_vec<false>(src, full_vecs, nbytes);
+        if (!wait_free(tail_c)) break;
+        const uint32_t off =
+            (tail_c % n_buf) * a.parity_stride + (uint32_t)(s * N + r) * slot_bytes + (tail_v - o0s[s]) * 16u;
+        st16_stage<kLocal>(rs, off, sentinel_canon<kKind>(x));
+      }
+    }
+  } else if (wave == n_prod) {
+    // ---------------- credit wave
+    // lane l reads owner l / n_cons's consumer wave l % n_cons; that wave
+    // has consumed chunks q, q + n_cons, ..., so every chunk below
+    // q + count * n_cons that it owns is consumed
+    const uint32_t target = n_chunks > n_buf ? n_chunks - n_buf : 0u;  // producers never need more
+    const uint32_t q = lane % n_cons;
+    uint64_t* const cp =
+        lane < (uint32_t)N * n_cons ? a.credit + ((size_t)(lane / n_cons) * kCreditSlices + w) * kCreditWaves + q : nullptr;
+    uint32_t have = 0u;
+    SpinBulk spin(a.spin_limit);
+    while (!dead && have < target) {
+      uint32_t f = ~0u;
+      if (cp != nullptr) {
+        const uint64_t v = __hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t cnt = ((uint32_t)(v >> 32) == st.epoch) ? (uint32_t)v : 0u;
+        f = q + cnt * n_cons;
+      }
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) f = min(f, (uint32_t)__shfl_xor((int)f, d));
+      if (f > have) {
+        have = f;
+        if (lane == 0) __hip_atomic_store(&s_free, have, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        spin = SpinBulk(a.spin_limit);
+      } else if (spin.expired()) {
+        raise_status(a.ctrl, kStatusTimeout);
+        dead = true;
+      }
+    }
+  } else {
+    // ---------------- consumer waves: owner r's slice w, staging only
+    const uint32_t cw = wave - n_prod - 1u;
+    uint32_t o0, s0, s1n;
+    slice_of((uint32_t)r, o0, s0, s1n);
+    uint64_t* const my_word = a.credit + ((size_t)r * kCreditSlices + w) * kCreditWaves + cw;
+    uint32_t done = 0u;
+    for (uint32_t c = cw; c < n_chunks && !dead; c += n_cons) {
+      // chunk c - B, the previous user of these slots, may belong to another
+      // consumer wave: its resets must be performed before this wave polls,
+      // or it would take chunk c - B's data for chunk c's
+      if (c >= n_buf) {
+        const uint32_t p = c - n_buf, pq = p % n_cons, need = p / n_cons + 1u;
+        SpinBulk spin(a.spin_limit);
+        while (__hip_atomic_load(&s_cons[pq], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < need) {
+          if (spin.expired()) {
+            raise_status(a.ctrl, kStatusTimeout);
+            dead = true;
+            break;
+          }
+        }
+        if (dead) break;
+      }
+      const uint64_t vbase = (uint64_t)c * nv;
+      const uint32_t fr = whole_in(c);
+      const uint32_t s1 = min(s1n, max(fr, s0));
+      const uint32_t my = (c % n_buf) * a.parity_stride + (uint32_t)(r * N) * slot_bytes;
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out + vbase * 16u, fr * 16u);
+      for (uint32_t b0 = 0; s0 + b0 < s1 && !dead; b0 += 64u) {
+        const uint32_t v = s0 + b0 + lane;
+        const uint32_t so = v < s1 ? my + (v - o0) * 16u : kOff;  // sender 0's slot, or kOff
+        const uint32_t oo = v < s1 ? v * 16u : kOff;
+        u32x4 d[N];
+        SpinBulk spin(a.spin_limit);
+        while (true) {
+          bool all = true;
+#pragma unroll
+          for (int k = 0; k < N; ++k) {
+            d[k] = ld16_coh(rs, so == kOff ? kOff : so + (uint32_t)k * slot_bytes);
+            all &= (so == kOff) | sentinel_ready<kKind>(d[k]);
+          }
+          if (__all((int)all)) break;
+          if (spin.expired()) {
+            raise_status(a.ctrl, kStatusTimeout);
+            dead = true;
+            break;
+          }
+        }
+        if (dead) break;
+        if (b0 == 0u) stamp(2, c);
+        __builtin_amdgcn_raw_buffer_store_b128(reduce_all<kKind, N>(d), ro, oo, 0, kCpolNt);
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+          st16_stage<kLocal>(rs, so == kOff ? kOff : so + (uint32_t)k * slot_bytes + reset_off, kEmpty);
+      }
+      // the partial last vector, by the lane that owns its position
+      if (has_tail && c == tail_c && !dead && tail_v >= s0 && tail_v < s1n && (tail_v - s0) % 64u == lane) {
+        const uint32_t base = my + (tail_v - o0) * 16u;
+        u32x4 d[N];
+        SpinBulk spin(a.spin_limit);
+        while (true) {
+          bool all = true;
+#pragma unroll
+          for (int k = 0; k < N; ++k) {
+            d[k] = ld16_coh(rs, base + (uint32_t)k * slot_bytes);
+            all &= sentinel_ready<kKind>(d[k]);
+          }
+          if (all) break;
+          if (spin.expired()) {
+            raise_status(a.ctrl, kStatusTimeout);
+            dead = true;
+            break;
+          }
+        }
+        if (!dead) {
+          store_vec(a.out, full_vecs, nbytes, reduce_all<kKind, N>(d));
+#pragma unroll
+          for (int k = 0; k < N; ++k) st16_stage<kLocal>(rs, base + (uint32_t)k * slot_bytes + reset_off, kEmpty);
+        }
+      }
+      dead = __any((int)dead) != 0;
+      if (dead) break;
+      // the resets are performed before the owner's progress advances
+      drain_vm();
+      ++done;
+      if (lane == 0) {
+        __hip_atomic_store(my_word, ((uint64_t)st.epoch << 32) | (uint64_t)done, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&s_cons[cw], done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      stamp(3, c);
+    }
+  }
+  wg_end(a.ctrl, st, a.host_epoch, a.grid, a.timing, idle);
+}
+
+// ---------------------------------------------------------------------------
 // launchers (host side, one instantiation per (dtype, N))
 // ---------------------------------------------------------------------------
 template <int kKind, int N>
@@ -982,6 +1273,12 @@ static hipError_t launch_n(const LaunchSpec& ls, hipStream_t stream) {
     case kKernSentinelHsLocal:
       hipLaunchKernelGGL((k_twoshot_sentinel_hs<kKind, N, true>), grid, block, 0, stream, ls.twoshot);
       break;
+    case kKernSentinelOc:
+      hipLaunchKernelGGL((k_twoshot_sentinel_oc<kKind, N, false>), grid, block, 0, stream, ls.twoshot);
+      break;
+    case kKernSentinelOcLocal:
+      hipLaunchKernelGGL((k_twoshot_sentinel_oc<kKind, N, true>), grid, block, 0, stream, ls.twoshot);
+      break;
     default:
       return hipErrorInvalidValue;
   }
@@ -1004,7 +1301,7 @@ static hipError_t launch_kind(const LaunchSpec& ls, hipStream_t stream) {
 }
 
 hipError_t launch(const LaunchSpec& ls, hipStream_t stream) {
-  if (ls.kernel >= kKernFirstMulti) return launch_multi(ls, stream);
+  if (is_multi_kernel(ls.kernel)) return launch_multi(ls, stream);
   switch (ls.kind) {
     case kKindF32: return launch_kind<kKindF32>(ls, stream);
     case kKindF16: return launch_kind<kKindF16>(ls, stream);
@@ -1038,6 +1335,8 @@ static int occupancy_n(int kernel, int threads) {
       if constexpr (N == 2) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_oneshot<kWireSentinel, kKind, 2, false, true>, threads, 0);
       break;
     case kKernSentinelHsLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_sentinel_hs<kKind, N, true>, threads, 0); break;
+    case kKernSentinelOc: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_sentinel_oc<kKind, N, false>, threads, 0); break;
+    case kKernSentinelOcLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_sentinel_oc<kKind, N, true>, threads, 0); break;
     default: break;
   }
   return err == hipSuccess ? blocks : 0;
@@ -1059,7 +1358,7 @@ static int occupancy_kind(int n_ranks, int kernel, int threads) {
 }
 
 int occupancy(int kind, int n_ranks, int kernel, int threads) {
-  if (kernel >= kKernFirstMulti) return occupancy_multi(kind, n_ranks, kernel, threads);
+  if (is_multi_kernel(kernel)) return occupancy_multi(kind, n_ranks, kernel, threads);
   switch (kind) {
     case kKindF32: return occupancy_kind<kKindF32>(n_ranks, kernel, threads);
     case kKindF16: return occupancy_kind<kKindF16>(n_ranks, kernel, threads);

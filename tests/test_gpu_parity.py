@@ -451,6 +451,117 @@ def test_sentinel_handshake_lost_contribution_times_out_and_recovers():
         assert_exact(got, oracle.allreduce(bits, dt), dt, "after recovery")
 
 
+# --------------------------------------------------------------------------- owner credit (sentinel_credit = 2)
+@pytest.mark.parametrize("placement", [1, 2])
+@pytest.mark.parametrize("chunk,threads,cons,buffers", [(1024, 0, 0, 2), (4096, 512, 2, 3), (65536, 0, 0, 5),
+                                                        (1 << 20, 256, 1, 2), (262144, 1024, 8, 4),
+                                                        (16384, 1024, 3, 7)])
+def test_sentinel_owner_credit_exact(placement, chunk, threads, cons, buffers):
+    """The pipelined Sentinel whose credit is every owner's published
+    progress: exact for every chunk size, wave split, buffer count (odd ones
+    too) and placement, with a ragged tail vector, fresh inputs on every
+    call, and every slot empty again afterwards."""
+    dt = BF16
+    n = (3 << 20) // 2 + 37  # 3 MiB + 74 bytes: the last vector is partial
+    with comm_for(8, dt, n * 2, sentinel_credit=2, chunk_bytes=chunk, threads=threads, consumer_waves=cons,
+                  pipeline_buffers=buffers, placement=placement) as c:
+        for rep in range(2):
+            bits = make_partials(2200 + placement, chunk + rep, 8, "bf16", n, "normal", 1.0)
+            got = run(c, bits, "sentinel_pipelined", dt)
+            assert_exact(got, oracle.allreduce(bits, dt), dt, "chunk %d rep %d" % (chunk, rep))
+        assert (c.staging(llar.SENTINEL_PIPELINED) == 0xFF).all()
+
+
+@pytest.mark.parametrize("n_ranks", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_sentinel_owner_credit_every_rank_count(n_ranks):
+    dt = BF16
+    n = 5001
+    with comm_for(n_ranks, dt, n * 2, sentinel_credit=2, chunk_bytes=2048, pipeline_buffers=3) as c:
+        for rep in range(3):
+            bits = make_partials(2300 + n_ranks, rep, n_ranks, "bf16", n, "normal", 0.5)
+            got = run(c, bits, "sentinel_pipelined", dt)
+            assert_exact(got, oracle.allreduce(bits, dt), dt, "N=%d rep %d" % (n_ranks, rep))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_sentinel_owner_credit_ragged_sizes_and_slices(dtype):
+    """Sizes around every vector and chunk boundary, and slice counts that
+    leave some slices of an owner's shard empty in a chunk (their consumer
+    waves still publish progress)."""
+    dt = CODE[dtype]
+    n_ranks = 8 if dtype != "fp32" else 5
+    sizes = [1, 7, 9, 63, 65, 1000, 4097, 20001, 70001]
+    with comm_for(n_ranks, dt, 70001 * 4, sentinel_credit=2, chunk_bytes=8192, pipeline_buffers=2) as c:
+        for slices in (1, 3, 7, 24, 32):
+            c.set_option("slices", slices)
+            for i, n in enumerate(sizes):
+                bits = make_partials(2400 + dt, slices * 100 + i, n_ranks, dtype, n, "normal", 1.0)
+                got = run(c, bits, "sentinel_pipelined", dt)
+                assert_exact(got, oracle.allreduce(bits, dt), dt, "slices %d n=%d" % (slices, n))
+
+
+def test_sentinel_owner_credit_many_chunks_device_epoch_and_other_credits():
+    """16 MiB per rank in 512 chunks through two buffers, with the device-
+    resident epoch (the progress words are tagged with it) and calls of the
+    other two credit schemes on the same staging in between."""
+    dt = BF16
+    n = 8 << 20
+    with comm_for(8, dt, n * 2, chunk_bytes=32768) as c:
+        for rep, (credit, dev) in enumerate([(2, 1), (0, 0), (2, 0), (1, 1), (2, 1)]):
+            c.set_option("sentinel_credit", credit)
+            c.set_option("device_epoch", dev)
+            c.set_option("pipeline_buffers", 2 if credit == 2 else 4)
+            bits = make_partials(2500, rep, 8, "bf16", n, "normal", 1.0)
+            got = run(c, bits, "sentinel_pipelined", dt)
+            assert_exact(got, oracle.allreduce(bits, dt), dt, "rep %d credit %d" % (rep, credit))
+        assert (c.staging(llar.SENTINEL_PIPELINED) == 0xFF).all()
+
+
+def test_sentinel_owner_credit_limits():
+    dt = BF16
+    n = 40000
+    bits = make_partials(2600, 0, 4, "bf16", n, "normal", 1.0)
+    with comm_for(4, dt, n * 2, sentinel_credit=2, chunk_bytes=4096) as c:
+        # more consumer waves than progress words per slice, or than the
+        # workgroup has room for next to a producer and the credit wave
+        for threads, cons in ((1024, 9), (256, 3)):
+            c.set_option("threads", threads)
+            c.set_option("consumer_waves", cons)
+            with pytest.raises(llar.LlarError) as ei:
+                run(c, bits, "sentinel_pipelined", dt)
+            assert ei.value.status == -1
+        c.set_option("threads", 0)
+        c.set_option("consumer_waves", 0)
+        # kept staging is never reset: a buffer used twice is refused
+        c.set_option("keep_staging", 1)
+        with pytest.raises(llar.LlarError) as ei:
+            run(c, bits, "sentinel_pipelined", dt)
+        assert ei.value.status == -2
+        c.set_option("keep_staging", 0)
+        got = run(c, bits, "sentinel_pipelined", dt)
+        assert_exact(got, oracle.allreduce(bits, dt), dt, "after refusals")
+
+
+def test_sentinel_owner_credit_lost_contribution_times_out_and_recovers():
+    dt = BF16
+    n = 40000
+    bits = make_partials(2700, 0, 4, "bf16", n, "normal", 1.0)
+    with comm_for(4, dt, n * 2, sentinel_credit=2, chunk_bytes=4096, pipeline_buffers=3) as c:
+        c.set_option("spin_timeout_us", 2000)
+        c.set_option("debug_drop_rank", 1)
+        parts = [to_device(bits[r], dt) for r in range(4)]
+        out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        c.allreduce(parts, out, "sentinel_pipelined")
+        torch.cuda.synchronize()
+        st, status_bits = c.device_status()
+        assert st == -5 and (status_bits & 1), (st, status_bits)
+        c.clear_device_status()
+        c.set_option("debug_drop_rank", -1)
+        c.set_option("spin_timeout_us", 100_000)
+        got = run(c, bits, "sentinel_pipelined", dt)
+        assert_exact(got, oracle.allreduce(bits, dt), dt, "after recovery")
+
+
 @pytest.mark.parametrize("threads", [64, 128, 256, 512])
 @pytest.mark.parametrize("proto", ALL_PROTOCOLS)
 def test_workgroup_sizes(proto, threads):
