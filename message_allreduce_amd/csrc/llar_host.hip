@@ -207,6 +207,10 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
         chunk_elems = std::max<size_t>(n_elems, 1);
       } else {
         chunk_elems = effective_chunk(h, proto) / h->elem;
+        // a message that fits one chunk is its own chunk: the lines are
+        // split among the owners by the chunk, so a larger nominal chunk
+        // would hand every line to the first owners
+        chunk_elems = std::min(chunk_elems, std::max<size_t>(n_elems, 1));
       }
       g.kernel = acc16 ? kKernLL128Acc16 : kKernLL128Acc32;
       g.chunk_elems = (uint32_t)chunk_elems;
@@ -231,6 +235,10 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
       size_t cb = effective_chunk(h, proto);
       g.kernel = h->sentinel_credit == 1 ? kKernSentinelHs : h->sentinel_credit == 2 ? kKernSentinelOc : kKernSentinelPipe;
       g.chunk_elems = (uint32_t)(cb / h->elem);
+      // a message that fits one chunk is its own chunk (in whole 16-byte
+      // vectors): owner shards split the chunk, so a larger nominal chunk
+      // would leave the whole message to the first owners' consumers
+      if (nbytes <= cb) g.chunk_elems = (uint32_t)(std::max<size_t>(ceil_div(nbytes, 16), 1) * 16 / h->elem);
       g.chunks = (int)ceil_div(n_elems, (size_t)g.chunk_elems);
       size_t vecs = ceil_div(std::min(cb, nbytes), 16);
       size_t per_owner = ceil_div(vecs, (size_t)N);
