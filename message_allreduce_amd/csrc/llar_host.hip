@@ -206,11 +206,13 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
         if (nbytes > kCapLL128) return LLAR_ERR_UNSUPPORTED;
         chunk_elems = std::max<size_t>(n_elems, 1);
       } else {
-        chunk_elems = effective_chunk(h, proto) / h->elem;
-        // a message that fits one chunk is its own chunk: the lines are
-        // split among the owners by the chunk, so a larger nominal chunk
-        // would hand every line to the first owners
-        chunk_elems = std::min(chunk_elems, std::max<size_t>(n_elems, 1));
+        // Lines are split among the owners by the chunk, so a message (or
+        // last chunk) shorter than the chunk would hand its lines to the
+        // first owners alone: the message is cut into equal chunks of at
+        // most the configured size.
+        const size_t n = std::max<size_t>(n_elems, 1);
+        const size_t nch = ceil_div(n, effective_chunk(h, proto) / h->elem);
+        chunk_elems = ceil_div(n, nch);
       }
       g.kernel = acc16 ? kKernLL128Acc16 : kKernLL128Acc32;
       g.chunk_elems = (uint32_t)chunk_elems;
@@ -232,13 +234,15 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
       break;
     }
     case LLAR_SENTINEL_PIPELINED: {
-      size_t cb = effective_chunk(h, proto);
       g.kernel = h->sentinel_credit == 1 ? kKernSentinelHs : h->sentinel_credit == 2 ? kKernSentinelOc : kKernSentinelPipe;
+      // Owner shards split the chunk, so the part of a chunk that lies past
+      // the message end would be missing from the last owners' shards, and
+      // a message shorter than the chunk would go to the first owners'
+      // consumers alone.  The message is therefore cut into equal chunks
+      // (whole 16-byte vectors) of at most the configured size.
+      const size_t nch = std::max<size_t>(ceil_div(nbytes, effective_chunk(h, proto)), 1);
+      const size_t cb = std::max<size_t>(ceil_div(ceil_div(nbytes, nch), 16), 1) * 16;
       g.chunk_elems = (uint32_t)(cb / h->elem);
-      // a message that fits one chunk is its own chunk (in whole 16-byte
-      // vectors): owner shards split the chunk, so a larger nominal chunk
-      // would leave the whole message to the first owners' consumers
-      if (nbytes <= cb) g.chunk_elems = (uint32_t)(std::max<size_t>(ceil_div(nbytes, 16), 1) * 16 / h->elem);
       g.chunks = (int)ceil_div(n_elems, (size_t)g.chunk_elems);
       size_t vecs = ceil_div(std::min(cb, nbytes), 16);
       size_t per_owner = ceil_div(vecs, (size_t)N);

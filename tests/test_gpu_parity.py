@@ -370,14 +370,24 @@ def test_ll128_pipelined_multiwave_credit_regression(threads):
 @pytest.mark.parametrize("proto", ["ll128_pipelined", "sentinel_pipelined"])
 def test_pipelined_slices_are_clamped_to_non_empty_owner_slices(proto):
     """Asking for more slices than the smallest owner shard of a chunk has
-    lines / vectors gives the largest safe count, and stays exact."""
+    lines / vectors gives the largest safe count, and stays exact.  The
+    message is cut into equal chunks of at most chunk_bytes (whole 16-byte
+    vectors for the Sentinel): 41 chunks of 1001 elements (33 LL128 lines,
+    4 per owner) or of 2016 bytes (126 vectors, 15 per owner)."""
     dt = BF16
-    n_ranks, chunk = 8, 2048  # 1024 elements: 34 LL128 lines (>= 4 per owner) / 128 vectors (16 per owner)
+    n_ranks, chunk = 8, 2048
     n = 40 * 1024 + 77
+    n_chunks = -(-(n * 2) // chunk)
     bits = make_partials(1710, 0, n_ranks, "bf16", n, "normal", 1.0)
     with comm_for(n_ranks, dt, n * 2, chunk_bytes=chunk, slices=64) as c:
         geo = c.geometry(n, llar.PROTOCOLS[proto])
-        per_owner = (chunk // 2 + 30) // 31 // n_ranks if proto == "ll128_pipelined" else chunk // 16 // n_ranks
+        assert geo["chunks"] == n_chunks == 41
+        if proto == "ll128_pipelined":
+            chunk_elems = -(-n // n_chunks)
+            per_owner = (chunk_elems + 30) // 31 // n_ranks
+        else:
+            chunk_vecs = -(-(-(-(n * 2) // n_chunks)) // 16)
+            per_owner = chunk_vecs // n_ranks
         assert geo["slices"] == per_owner
         for rep in range(3):
             got = run(c, bits, proto, dt)
