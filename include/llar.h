@@ -201,8 +201,11 @@ int llar_clear_device_status(llar_comm* h);
 /* Options (key, value).  Keys:
  *   "spin_timeout_us"  device poll limit in microseconds (default 200000)
  *   "ll128_acc"        LL128 staging type: 0 = binary32 (default), 1 = the I/O type (16-bit packed)
- *   "chunk_bytes"      per-rank chunk of the pipelined protocols (0 = tuned default: 128 KiB for
- *                      LL128, 1 MiB for the Sentinel; clamped to [1 KiB, 4 MiB] and to the message)
+ *   "chunk_bytes"      largest per-rank chunk of the pipelined protocols (0 = tuned default:
+ *                      128 KiB for LL128, 1 MiB for the Sentinel; clamped to [1 KiB, 4 MiB]); a
+ *                      message is cut into the fewest equal chunks of at most this size (whole
+ *                      16-byte vectors for the Sentinel), so that every owner gets an even share
+ *                      of every chunk
  *   "slices"           workgroups per rank (0 = tuned default); for the pipelined protocols an
  *                      upper bound: every owner slice of a full chunk keeps at least one line
  *                      (LL128) or vector (Sentinel), because the credit is earned by consuming
