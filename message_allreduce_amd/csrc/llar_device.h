@@ -177,7 +177,7 @@ constexpr uint32_t kStatusPlacement = 2u;
 struct Ctrl {
   uint32_t epoch;      // current call's epoch, 1..2^32-1 (0 = never written)
   uint32_t pad0[31];
-  uint32_t arrivals;   // workgroups of the running call that have read the epoch
+  uint32_t unused1;
   uint32_t pad1[31];
   uint32_t status;     // sticky error bits
   uint32_t pad2[31];
@@ -187,6 +187,7 @@ struct Ctrl {
   uint32_t pad4[31];
   uint32_t timing_grid[kTimingRing];  // per epoch slot: workgroups that recorded a span
   uint64_t* timing_wg;  // [kTimingRing][kTimingMaxWgs][2]: each workgroup's start, end (wall ticks)
+  uint32_t read_epoch[kTimingMaxWgs];  // device-numbered calls: the epoch workgroup b has read
 };
 
 // Epochs: host-numbered calls use 1 .. 2^31-1, device-numbered (graph
@@ -211,32 +212,34 @@ __device__ __forceinline__ void raise_status(Ctrl* c, uint32_t bits) {
 // clear): nothing to read on the device.  Under graph capture the arguments
 // would repeat on every replay, so the kernel reads the device-resident epoch
 // (bit 31 set; the two ranges never meet): thread 0 reads it, publishes it
-// through LDS and takes an arrival ticket; the workgroup that arrives last
-// (ticket == G-1) advances it when it finishes -- by then every workgroup of
-// the call has read the old value, and the next call starts after this one.
+// through LDS and records it in its workgroup's own word of read_epoch.  The
+// grid's last workgroup, when it finishes, waits until every word holds this
+// epoch -- every workgroup of the call has read it -- and advances it; the
+// next call starts after this one.  (One shared arrival counter instead
+// serialised an atomic per workgroup on a single address: about 6 us per
+// call for a 512-workgroup grid.)
 // Timing mode has each workgroup store its own start and end stamps in the
 // epoch's ring slot (plain stores, no shared counter); workgroup 0 also
 // records the grid so that the reader knows how many entries belong to it.
 struct WgState {
   uint32_t epoch;
-  uint32_t ticket;
-  bool counted;
+  bool counted;  // the epoch came from the device (recorded in read_epoch)
   uint64_t t0;
 };
 
 __device__ __forceinline__ WgState wg_begin(Ctrl* ctrl, uint32_t host_epoch, bool timing, bool idle) {
   __shared__ uint32_t s_epoch;
-  WgState st{host_epoch, 0u, false, 0ull};
+  WgState st{host_epoch, false, 0ull};
   if (timing && threadIdx.x == 0) st.t0 = wall_ticks();
   if (host_epoch != 0u) return st;
   if (threadIdx.x == 0) {
     const uint32_t e = __hip_atomic_load(&ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_epoch = e;
-    st.ticket = __hip_atomic_fetch_add(&ctrl->arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    st.counted = true;
+    __hip_atomic_store(&ctrl->read_epoch[blockIdx.x], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   st.epoch = s_epoch;
+  st.counted = true;
   return st;
 }
 
@@ -246,6 +249,34 @@ __device__ __forceinline__ void wg_end(Ctrl* ctrl, const WgState& st, uint32_t h
     drain_vm();
     __syncthreads();
   }
+  if (st.counted && blockIdx.x == grid - 1u && threadIdx.x < 64u) {
+    // every workgroup of the grid has read this call's epoch (all of them
+    // are resident, so the wait ends; the wall-clock bound is a safeguard)
+    // (each pass reads every word with 16-byte loads, four per lane in
+    // flight, so a pass costs one memory round trip per 1024 workgroups)
+    const uint32_t lane = threadIdx.x;
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(ctrl->read_epoch, grid * 4u);
+    llar_wire::Poll poll(100000000ull);  // 1 s
+    while (true) {
+      bool all = true;
+      for (uint32_t w0 = 0; w0 < grid; w0 += 1024u) {
+        u32x4 v[4];
+#pragma unroll
+        for (uint32_t k = 0; k < 4u; ++k) v[k] = ld16_coh(rr, (w0 + (k * 64u + lane) * 4u) * 4u);
+#pragma unroll
+        for (uint32_t k = 0; k < 4u; ++k)
+#pragma unroll
+          for (uint32_t t = 0; t < 4u; ++t) all &= (w0 + (k * 64u + lane) * 4u + t >= grid) | (v[k][t] == st.epoch);
+      }
+      if (__all((int)all)) break;
+      if (poll.expired()) {
+        raise_status(ctrl, kStatusTimeout);
+        break;
+      }
+    }
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&ctrl->epoch, next_device_epoch(st.epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (threadIdx.x != 0) return;
   if (timing) {
     const uint64_t t1 = wall_ticks();
@@ -254,10 +285,6 @@ __device__ __forceinline__ void wg_end(Ctrl* ctrl, const WgState& st, uint32_t h
     p[0] = idle ? ~0ull : st.t0;
     p[1] = idle ? 0ull : t1;
     if (blockIdx.x == 0) ctrl->timing_grid[slot] = grid;
-  }
-  if (st.counted && st.ticket == grid - 1u) {
-    __hip_atomic_store(&ctrl->arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&ctrl->epoch, next_device_epoch(st.epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -522,6 +522,8 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
   bool device_epoch = false;
   uint32_t host_epoch = 0;
   if (!call_epoch(h, stream, device_epoch, host_epoch)) return fail(LLAR_ERR_HIP);
+  // a device-numbered call records the epoch per workgroup
+  if (device_epoch && ls.grid > kTimingMaxWgs) return fail(LLAR_ERR_UNSUPPORTED);
   const bool is_oneshot = g.kernel == kKernOneShotLL || g.kernel == kKernOneShotSentinel ||
                           g.kernel == kKernOneShotLLLocal || g.kernel == kKernOneShotSentinelLocal ||
                           g.kernel == kKernP2PLL || g.kernel == kKernP2PSentinel || g.kernel == kKernP2PLLLocal ||
@@ -706,6 +708,7 @@ int run_multi(llar_comm* h, const void* const* ins, void* const* outs, int n_rec
     bool device_epoch = false;
     uint32_t host_epoch = 0;
     if (!call_epoch(h, stream, device_epoch, host_epoch)) return fail(LLAR_ERR_HIP);
+    if (device_epoch && ls.grid > kTimingMaxWgs) return fail(LLAR_ERR_UNSUPPORTED);
     MultiArgs& a = ls.multi;
     for (int r = 0; r < N; ++r) {
       a.in[r] = static_cast<const uint8_t*>(ins[r]);
@@ -763,6 +766,8 @@ int run_multi(llar_comm* h, const void* const* ins, void* const* outs, int n_rec
   bool device_epoch = false;
   uint32_t host_epoch = 0;
   if (!call_epoch(h, stream, device_epoch, host_epoch)) return fail(LLAR_ERR_HIP);
+  // a device-numbered call records the epoch per workgroup
+  if (device_epoch && ls.grid > kTimingMaxWgs) return fail(LLAR_ERR_UNSUPPORTED);
   MultiArgs& a = ls.multi;
   for (int r = 0; r < N; ++r) a.in[r] = static_cast<const uint8_t*>(ins[r]);
   for (int r = 0; r < n_recv; ++r) a.out[r] = static_cast<uint8_t*>(outs[r]);
