@@ -234,6 +234,46 @@ def measure_rows(stream, steps):
     return rows
 
 
+def measure_workloads(stream, steps, floor_us):
+    """The four fixed workloads of the parity suite, each with its own
+    protocol, rank count and dtype (the fifth is the size sweep): per call
+    from graph replay, the device-side span, the span over the latency floor,
+    and the algorithmic (N + 1) x S bytes over the span against the HBM peak."""
+    import torch
+    import message_allreduce_amd as llar
+    from workloads import WORKLOADS, workload_partials
+    tdt = {"fp32": (torch.float32, np.int32), "fp16": (torch.float16, np.int16), "bf16": (torch.bfloat16, np.int16)}
+    rows = {}
+    for k in (1, 2, 3, 4):
+        w = WORKLOADS[k]
+        dt, it = tdt[w.dtype]
+        nbytes = w.n_elems * torch.tensor([], dtype=dt).element_size()
+        c = llar.Communicator(w.n_ranks, dt, nbytes)
+        try:
+            if w.chunk_bytes:
+                c.set_option("chunk_bytes", w.chunk_bytes)
+            bits = workload_partials(w, 0)
+            parts = [torch.from_numpy(bits[r].view(it).copy()).view(dt).cuda() for r in range(w.n_ranks)]
+            out = torch.empty(w.n_elems, dtype=dt, device="cuda")
+            fn = (lambda: c.allreduce(parts, out, w.protocol, stream=stream))
+            # the 4 MiB pipelined workload takes ~0.4 ms per call: 500 calls
+            us = time_graph_fn(fn, 500 if w.chunk_bytes else steps, stream)
+            dmed, dmin = device_side_fn(c, fn, 60, stream)
+            alg = (w.n_ranks + 1) * nbytes
+            gbps = alg / dmed / 1e3
+            rows[w.name] = {"protocol": w.protocol, "n_ranks": w.n_ranks, "dtype": w.dtype, "bytes_per_rank": nbytes,
+                            "us_per_call_graph": round(us, 3), "device_us_median": round(dmed, 3),
+                            "device_us_min": round(dmin, 3), "device_over_floor": round(dmed / floor_us, 3),
+                            "GBps_device": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 5)}
+            log("workload %d %s: %.3f us per call (graph), device %.3f us, %.1f GB/s" % (k, w.name, us, dmed, gbps))
+            st, sbits = c.device_status()
+            if st != 0:
+                raise RuntimeError("device status %d (bits %#x) in workload %d" % (st, sbits, k))
+        finally:
+            c.close()
+    return rows
+
+
 def measure_device_api(stream, steps):
     """The device-side API's use case: an epilogue fused with the exchange.
     N = 8 fp32 partials of 16 KiB are scaled per rank and summed, either by
@@ -553,6 +593,8 @@ def main():
         log("other collectives")
         result["rows"] = measure_rows(stream, min(args.steps, 1000))
         result["rows"]["device_api_fused_epilogue"] = measure_device_api(stream, min(args.steps, 1000))
+        log("fixed workloads")
+        result["workloads"] = measure_workloads(stream, min(args.steps, 1000), floor["floor_us"])
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
