@@ -688,6 +688,32 @@ def test_pipelined_short_last_chunk_regression(proto):
                     check(got, oracle.allreduce(bits, dt), dt, proto, "N=%d n=%d rep %d" % (n_ranks, n, rep))
 
 
+def test_default_geometry_rules():
+    """The host's default geometry: one-shot workgroups of 256 threads up to
+    64 slices' worth of 8-byte units, 512 beyond; pipelined messages cut into
+    the fewest chunks of at most the configured size, and a message shorter
+    than the chunk as one chunk."""
+    with comm_for(8, BF16, 8 << 20) as c:
+        for nbytes, threads in ((16384, 256), (131072, 256), (131072 + 16, 512), (524288, 512)):
+            geo = c.geometry(nbytes // 2, llar.SENTINEL)
+            assert geo["threads"] == threads, (nbytes, geo)
+            units = 2 * (-(-nbytes // 16))
+            assert geo["slices"] == min(64, -(-units // threads)), (nbytes, geo)
+        for nbytes in (128, 65536, (1 << 20) - 16, 1 << 20, (1 << 20) + 16, (3 << 19), 8 << 20):
+            geo = c.geometry(nbytes // 2, llar.SENTINEL_PIPELINED)
+            assert geo["chunks"] == max(1, -(-nbytes // (1 << 20))), (nbytes, geo)
+        c.set_option("chunk_bytes", 65536)
+        geo = c.geometry((1 << 20) // 2 + 8, llar.LL128_PIPELINED)
+        assert geo["chunks"] == 17
+    # equal chunks of a ragged message stay exact
+    dt = BF16
+    n = (3 << 19) // 2 + 77
+    bits = make_partials(2800, 0, 8, "bf16", n, "normal", 1.0)
+    with comm_for(8, dt, n * 2) as c:
+        got = run(c, bits, "sentinel_pipelined", dt)
+        assert_exact(got, oracle.allreduce(bits, dt), dt, "1.5 MiB + 154 B")
+
+
 # --------------------------------------------------------------------------- the barrier ablation
 @pytest.mark.parametrize("placement", [1, 2], ids=["spread", "local"])
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
