@@ -429,6 +429,106 @@ def _check_split(n_ranks, slices, chunks, parities, max_states, credit_lag=0):
     return res
 
 
+def check_owner_credit(n_ranks: int, slices: int, chunks: int, buffers: int, cons_waves: int = 1,
+                       wave_order: bool = True, credit: str = "owner",
+                       max_states: int = 2_000_000) -> PipelineResult:
+    """Model of the owner-credit schedule over B rotating Sentinel buffers.
+
+    Per (rank r, slice w) a producer P and cons_waves consumer waves.  Chunk
+    c lives in buffer c % B; line (buffer, owner s, slice w) collects one
+    contribution per rank (the rank's own shard included).
+      P emits chunk c (one contribution per owner, separate steps) once the
+        credit allows it: credit "owner" -- every owner s has consumed every
+        chunk <= c - B; credit "own" -- only P's own consumer has (a weaker
+        credit, which the checker must catch);
+      consumer wave q consumes chunks q, q + Q, ... in order; with
+        ``wave_order`` chunk c also waits until chunk c - B (another wave's,
+        the previous user of the line) is consumed.  Like the Sentinel, a
+        wave sees only that the line is full, not which chunk filled it, so
+        reading a full line that holds another chunk is a stale read.
+    Checked: no overwrite, no stale read, progress.
+    """
+    Q = cons_waves
+    pairs = [(r, w) for r in range(n_ranks) for w in range(slices)]
+    idx = {p: i for i, p in enumerate(pairs)}
+    n_lines = buffers * n_ranks * slices
+
+    def line_id(b, owner, w):
+        return (b * n_ranks + owner) * slices + w
+
+    def consumed(cnts, c):  # chunk c consumed by the pair whose wave counts are cnts
+        return cnts[c % Q] > c // Q
+
+    def all_below(cnts, x):  # every chunk < x consumed
+        return all(consumed(cnts, c) for c in range(min(x, chunks)))
+
+    init = (tuple([(0, 0)] * len(pairs)), tuple([tuple([0] * Q)] * len(pairs)), tuple([(-1, 0)] * n_lines))
+    res = PipelineResult(states=0, terminal_ok=0)
+    seen, stack = set(), [init]
+    while stack:
+        st = stack.pop()
+        if st in seen:
+            continue
+        seen.add(st)
+        res.states += 1
+        if res.states > max_states:
+            raise RuntimeError("state space too large")
+        prod, cons, lines = st
+        if all(p[0] == chunks for p in prod) and all(q + cnt * Q >= chunks for cc in cons
+                                                     for q, cnt in enumerate(cc)):
+            res.terminal_ok += 1
+            continue
+        moved = False
+        for ai, (r, w) in enumerate(pairs):
+            c, s = prod[ai]
+            if c < chunks:
+                need = c - buffers + 1  # chunks below this must be consumed
+                if credit == "owner":
+                    ok = all(all_below(cons[idx[(o, w)]], need) for o in range(n_ranks))
+                else:
+                    ok = all_below(cons[ai], need)
+                if ok:
+                    lid = line_id(c % buffers, s, w)
+                    held, cnt = lines[lid]
+                    if held not in (-1, c):
+                        res.violations.append(("overwrite", (r, w), c, s, held))
+                        break
+                    nl = list(lines)
+                    nl[lid] = (c, cnt + 1)
+                    npr = list(prod)
+                    npr[ai] = (c, s + 1) if s + 1 < n_ranks else (c + 1, 0)
+                    stack.append((tuple(npr), cons, tuple(nl)))
+                    moved = True
+            for q in range(Q):
+                cc = q + cons[ai][q] * Q
+                if cc >= chunks:
+                    continue
+                if wave_order and cc >= buffers and not consumed(cons[ai], cc - buffers):
+                    continue
+                lid = line_id(cc % buffers, r, w)
+                held, cnt = lines[lid]
+                if cnt < n_ranks:
+                    continue  # not full yet: the wave keeps polling
+                if held != cc:
+                    res.violations.append(("stale read", (r, w), cc, held))
+                    break
+                nl = list(lines)
+                nl[lid] = (-1, 0)
+                nco = list(cons)
+                nq = list(cons[ai])
+                nq[q] += 1
+                nco[ai] = tuple(nq)
+                stack.append((prod, tuple(nco), tuple(nl)))
+                moved = True
+            if res.violations:
+                break
+        if res.violations:
+            break
+        if not moved:
+            res.deadlocks += 1
+    return res
+
+
 # ----------------------------------------------------------------------------
 # Speed-of-light arithmetic and the alpha + beta * size model
 # ----------------------------------------------------------------------------

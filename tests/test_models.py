@@ -390,3 +390,31 @@ def test_pipeline_credit_lag_needs_two_lag_plus_two_buffers():
         assert not ok.violations and ok.deadlocks == 0 and ok.terminal_ok == 1
         bad = models.check_pipeline(*shape, split=True, parities=3, credit_lag=1)
         assert any(v[0] == "overwrite" for v in bad.violations)
+
+
+def test_owner_credit_is_safe_exhaustively():
+    # every owner publishes its progress; a producer stores chunk c once every
+    # owner consumed every chunk <= c - B: safe for any B >= 1 and any number
+    # of consumer waves taking whole chunks round-robin
+    for shape in [dict(n_ranks=2, slices=1, chunks=4, buffers=1), dict(n_ranks=2, slices=1, chunks=4, buffers=2, cons_waves=2),
+                  dict(n_ranks=2, slices=1, chunks=5, buffers=3, cons_waves=2), dict(n_ranks=3, slices=1, chunks=3, buffers=2, cons_waves=2),
+                  dict(n_ranks=2, slices=2, chunks=3, buffers=2, cons_waves=2), dict(n_ranks=2, slices=1, chunks=4, buffers=2, cons_waves=3)]:
+        r = models.check_owner_credit(**shape)
+        assert not r.violations and r.deadlocks == 0 and r.terminal_ok == 1 and r.states > 10, (shape, r)
+
+
+def test_owner_credit_needs_the_wave_order_check():
+    # a consumer wave that polls chunk c before another wave consumed chunk
+    # c - B finds the old chunk's full line and takes it for its own
+    for shape in [dict(n_ranks=2, slices=1, chunks=3, buffers=1, cons_waves=2),
+                  dict(n_ranks=2, slices=1, chunks=3, buffers=2, cons_waves=3)]:
+        r = models.check_owner_credit(**shape, wave_order=False)
+        assert any(v[0] == "stale read" for v in r.violations), shape
+
+
+def test_owner_credit_from_the_own_consumer_alone_overwrites():
+    # the same buffer count with only the producer's own consumer as credit
+    # lets a fast rank overwrite a slower owner's unconsumed chunk
+    for n_ranks in (2, 3):
+        r = models.check_owner_credit(n_ranks=n_ranks, slices=1, chunks=4, buffers=2, credit="own")
+        assert any(v[0] == "overwrite" for v in r.violations), n_ranks
