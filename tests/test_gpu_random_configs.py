@@ -1,7 +1,8 @@
 """Randomised parity: seeded draws over operation (AllReduce, ReduceScatter,
-AllGather, send/recv), protocol, rank count, dtype, size, placement and
-workgroup size, each checked against the oracle (bit-exact for LL and
-Sentinel, within the atomic protocol's tolerance for LL128)."""
+AllGather, send/recv), protocol, rank count, dtype, size, placement,
+workgroup size, the pipelined Sentinel's credit and the epoch source, each
+checked against the oracle (bit-exact for LL and Sentinel, within the atomic
+protocol's tolerance for LL128)."""
 import numpy as np
 import pytest
 import torch
@@ -39,16 +40,19 @@ def draw(rng):
         n = max(1, n // n_ranks)
     else:
         proto = str(rng.choice(["ll", "sentinel", "auto"]))
-    return op, dtype, n_ranks, n, proto, placement, threads
+    # drawn last, so the fields above keep their values for a given seed
+    credit = int(rng.integers(0, 3))      # pipelined Sentinel: workgroup, slot or owner credit
+    dev_epoch = int(rng.integers(0, 2))   # 1: the device-resident epoch (per-workgroup epoch words)
+    return op, dtype, n_ranks, n, proto, placement, threads, credit, dev_epoch
 
 
 CASES = [draw(np.random.default_rng([7000, i])) for i in range(200)]
 
 
-@pytest.mark.parametrize("index", range(len(CASES)), ids=["%s-%s-N%d-n%d-%s-p%d-t%d" % c for c in CASES])
+@pytest.mark.parametrize("index", range(len(CASES)), ids=["%s-%s-N%d-n%d-%s-p%d-t%d-c%d-e%d" % c for c in CASES])
 def test_random_configuration(index):
     case = CASES[index]
-    op, dtype, n_ranks, n, proto, placement, threads = case
+    op, dtype, n_ranks, n, proto, placement, threads, credit, dev_epoch = case
     dt = CODE[dtype]
     esize = 4 if dtype == "fp32" else 2
     max_bytes = n * esize * (n_ranks if op in ("reduce_scatter", "all_gather") else 1)
@@ -56,8 +60,12 @@ def test_random_configuration(index):
     try:
         c.set_option("spin_timeout_us", 100_000)
         c.set_option("placement", placement)
+        c.set_option("device_epoch", dev_epoch)
         if not (threads == 64 and proto in ("sentinel_pipelined", "auto") and op == "allreduce"):
             c.set_option("threads", threads)
+        if proto == "sentinel_pipelined" and threads == 0:
+            # the slot and owner credits run 1024-thread workgroups by default
+            c.set_option("sentinel_credit", credit)
         seed = index
         if op == "allreduce":
             bits = make_partials(7100, seed, n_ranks, dtype, n, "normal", 0.5)
