@@ -193,10 +193,11 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
       g.kernel = proto == LLAR_LL ? kKernOneShotLL : kKernOneShotSentinel;
       // the consumer works in 8-byte units: 2 per 16-byte vector
       size_t units = 2 * ceil_div(nbytes, 16);
-      // measured on MI355X (graph replay, N = 8): 256 threads up to 64
-      // slices' worth of units, 512 beyond (512 KiB fp16 Sentinel: 8.13 ->
-      // 7.22 us per call, 256 KiB: 5.49 -> 5.19)
-      g.threads = h->threads ? (int)h->threads : (units > (size_t)256 * 64 ? 512 : 256);
+      // measured on MI355X (graph replay, N = 8): 256 threads below 64
+      // slices' worth of units, 512 from there (fp16 Sentinel per call:
+      // 128 KiB 4.13 -> 4.01 us, 256 KiB 5.49 -> 5.19, 512 KiB 8.13 -> 7.22;
+      // 64 KiB keeps 256: 3.70 against 3.96)
+      g.threads = h->threads ? (int)h->threads : (units >= (size_t)256 * 64 ? 512 : 256);
       g.slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(units, (size_t)g.threads), 1, 64);
       break;
     }
