@@ -177,8 +177,6 @@ constexpr uint32_t kStatusPlacement = 2u;
 struct Ctrl {
   uint32_t epoch;      // current call's epoch, 1..2^32-1 (0 = never written)
   uint32_t pad0[31];
-  uint32_t unused1;
-  uint32_t pad1[31];
   uint32_t status;     // sticky error bits
   uint32_t pad2[31];
   uint32_t bar_count;  // grid barrier of the barrier-based ablation kernel: arrivals of this call

@@ -36,9 +36,11 @@ constexpr size_t kCapLL128 = 16ull << 20;
 constexpr size_t kCapChunk = 4ull << 20;  // largest chunk of the pipelined protocols
 constexpr int kTraceMaxWgs = 4096;
 constexpr int kPipeTraceMaxWgs = 1024;
-// The pipelined Sentinel has up to 8 staging buffers: with B buffers a
-// producer may run B/2 - 1 chunks further ahead of its consumer (safe with
-// B >= 2 * lag + 2).  Default 4.
+// The pipelined Sentinel's region holds 8 staging buffers of the largest
+// chunk (a call spaces its buffers by its own chunk, so more of a smaller
+// chunk fit, up to 64).  With B buffers a producer runs B/2 - 1 chunks ahead
+// of its consumer under the workgroup credit (safe with B >= 2 lag + 2), B - 1
+// under the owner credit.  Default 4.
 constexpr uint32_t kSentinelPipeMaxBuffers = 8;
 
 size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
