@@ -412,6 +412,8 @@ def measure_floor():
         "t_store_same_xcd_ns": round(same_xcd, 1),
         "floor_us": round(floor_ns / 1e3, 4),
         "floor_same_xcd_us": round((2 * rt + same_xcd) / 1e3, 4),
+        # the shorter reading of the same bound: one L2 round trip plus one store
+        "floor_rt_plus_store_us": round((rt + t_store) / 1e3, 4),
         "empty_launch_us": round(launch / 1e3, 3),
         "atomic_latency_ns": round(atomic, 1),
     }
@@ -568,6 +570,7 @@ def main():
                               else "stream-ordered back-to-back calls, median of 5 batches")},
         "latency": dict(floor, **{"device_us_median": round(dev_med, 3), "device_us_min": round(dev_min, 3),
                                   "device_over_floor": round(dev_med / floor["floor_us"], 3),
+                                  "device_over_rt_plus_store": round(dev_med / floor["floor_rt_plus_store_us"], 3),
                                   "per_call_over_floor_plus_launch": round(
                                       value / (floor["floor_us"] + floor["empty_launch_us"]), 3),
                                   "per_call_stream_us": {"min": round(us_min, 3), "median": round(us, 3),
