@@ -60,6 +60,17 @@ template <bool kLocal>
 __device__ __forceinline__ void st8_stage(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
   llar_wire::store8<scope_of(kLocal)>(r, off, v);
 }
+// Reset of a consumed Sentinel slot in a pipeline that does not read the
+// slot again before its producer's next store: under the local placement a
+// non-temporal store (sc0 | nt), so that L2 evicts emptied slots before
+// staged data (measured on the 64 MiB x 8 reduce: 794 -> 646 MiB written per
+// launch, 3 % faster); device-coherent otherwise.
+template <bool kLocal>
+__device__ __forceinline__ void st16_reset(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 empty = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  if constexpr (kLocal) __builtin_amdgcn_raw_buffer_store_b128(empty, r, off, 0, kCpolSc0 | kCpolNt);
+  else st16_stage<false>(r, off, empty);
+}
 __device__ __forceinline__ void drain_vm() { llar_wire::release(); }
 
 // ---- clocks and ids -------------------------------------------------------------

@@ -642,14 +642,7 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
 #pragma unroll
             for (int k = 0; k < N - 1; ++k) {
               const int sender = k < r ? k : k + 1;
-              const uint32_t off = my + (uint32_t)sender * slot_bytes + (v - o0) * 16u;
-              const u32x4 empty = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-              // under the local placement the reset is a non-temporal store:
-              // the emptied slot is not read again before its next use, and
-              // evicting it first keeps more staged data in L2 (measured on
-              // the 64 MiB x 8 reduce: 794 -> 646 MiB written, 3 % faster)
-              if constexpr (kLocal) __builtin_amdgcn_raw_buffer_store_b128(empty, rs, off, 0, kCpolSc0 | kCpolNt);
-              else st16_stage<kLocal>(rs, off, empty);
+              st16_reset<kLocal>(rs, my + (uint32_t)sender * slot_bytes + (v - o0) * 16u);
             }
           }
         }
@@ -988,7 +981,6 @@ __global__ void __launch_bounds__(1024) k_twoshot_sentinel_oc(TwoShotArgs a) {
   const uint32_t n_cons = a.cons_waves, n_prod = n_waves - n_cons - 1u;
   const uint32_t n_buf = a.n_buffers, n_chunks = a.n_chunks;
   const uint32_t reset_off = a.keep ? kOff : 0u;  // tests: keep the staged data
-  const u32x4 kEmpty = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
   // owner s's shard of a chunk is [o0, o1) = [s nv / N, (s+1) nv / N); slice
   // w of it is [o0 + w len / W, o0 + (w+1) len / W), len = o1 - o0 (32-bit:
   // nv < 2^18 vectors, W <= 64)
@@ -1178,7 +1170,7 @@ __global__ void __launch_bounds__(1024) k_twoshot_sentinel_oc(TwoShotArgs a) {
         __builtin_amdgcn_raw_buffer_store_b128(reduce_all<kKind, N>(d), ro, oo, 0, kCpolNt);
 #pragma unroll
         for (int k = 0; k < N; ++k)
-          st16_stage<kLocal>(rs, so == kOff ? kOff : so + (uint32_t)k * slot_bytes + reset_off, kEmpty);
+          st16_reset<kLocal>(rs, so == kOff ? kOff : so + (uint32_t)k * slot_bytes + reset_off);
       }
       // the partial last vector, by the lane that owns its position
       if (has_tail && c == tail_c && !dead && tail_v >= s0 && tail_v < s1n && (tail_v - s0) % 64u == lane) {
@@ -1202,7 +1194,7 @@ __global__ void __launch_bounds__(1024) k_twoshot_sentinel_oc(TwoShotArgs a) {
         if (!dead) {
           store_vec(a.out, full_vecs, nbytes, reduce_all<kKind, N>(d));
 #pragma unroll
-          for (int k = 0; k < N; ++k) st16_stage<kLocal>(rs, base + (uint32_t)k * slot_bytes + reset_off, kEmpty);
+          for (int k = 0; k < N; ++k) st16_reset<kLocal>(rs, base + (uint32_t)k * slot_bytes + reset_off);
         }
       }
       dead = __any((int)dead) != 0;
