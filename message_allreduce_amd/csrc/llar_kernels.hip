@@ -496,6 +496,8 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   const uint64_t nbytes = a.n * (uint64_t)E::kBytes;
   const uint32_t chunk_vecs = (uint32_t)(((uint64_t)a.chunk_elems * E::kBytes + 15u) / 16u);
   const uint64_t total_vecs = (nbytes + 15u) / 16u;
+  const uint64_t full_vecs = nbytes / 16u;          // whole vectors of the message
+  const bool has_tail = (nbytes % 16u) != 0u;       // vector full_vecs is partial
   const uint32_t slot_bytes = a.shard_cap * 16u;
   const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
   const uint32_t n_prod = n_waves / 2, n_cons = n_waves - n_prod;
@@ -531,6 +533,11 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
       // vectors of this chunk that exist; the partition below uses the
       // nominal chunk so that a slot keeps its (owner, slice) in every chunk
       const uint32_t nv_real = (uint32_t)min((uint64_t)chunk_vecs, total_vecs - vbase);
+      // whole vectors of this chunk: the loads below read them through a
+      // buffer descriptor; the partial last vector of a message, if any, is
+      // staged after the chunk loop
+      const uint32_t nv_whole = (uint32_t)min((uint64_t)chunk_vecs, full_vecs > vbase ? full_vecs - vbase : 0u);
+      const __amdgpu_buffer_rsrc_t rin = make_rsrc(src + vbase * 16u, nv_whole * 16u);
       const uint32_t nv = chunk_vecs;
       const uint32_t poff = (c % n_buf) * a.parity_stride;
       const uint32_t span = (nv / N + 1u) / a.slices + 2u;  // longest (owner, slice) range
@@ -542,9 +549,12 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
 #pragma unroll
           for (int u = 0; u < kU; ++u) {
             const uint32_t v = sl0[k] + b0 + pl + (uint32_t)u * PL;
-            const bool ok = (v < sl1[k]) && (v < nv_real);
+            const bool ok = (v < sl1[k]) && (v < nv_whole);
             vo[k][u] = ok ? v - own0[k] : ~0u;
-            x[k][u] = ok ? load_vec(src, vbase + v, nbytes) : u32x4{0u, 0u, 0u, 0u};
+            // non-temporal (sc0 | nt): every input is read once; measured
+            // 3 % faster than non-temporal global loads on 64 MiB x 8.  A lane
+            // without a vector reads past the descriptor and gets zero.
+            x[k][u] = __builtin_amdgcn_raw_buffer_load_b128(rin, ok ? v * 16u : 0x80000000u, 0, kCpolSc0 | kCpolNt);
           }
         }
         if (b0 == 0 && c > lag) {
@@ -575,6 +585,19 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
         }
       }
       if (wave == 0) stamp(1, c);
+    }
+    // the partial last vector of the message (its chunk's credit was taken
+    // when that chunk was staged), by one lane, for the owner whose slice w
+    // holds it; the owner's own vector is read by its consumer directly
+    if (has_tail && !dead && !silent && wave == 0 && lane == 0) {
+      const uint32_t tc = (uint32_t)(full_vecs / chunk_vecs), tv = (uint32_t)(full_vecs % chunk_vecs);
+#pragma unroll
+      for (int k = 0; k < N - 1; ++k) {
+        if (tv < sl0[k] || tv >= sl1[k]) continue;
+        const int s = k < r ? k : k + 1;
+        const uint32_t slot = (tc % n_buf) * a.parity_stride + (uint32_t)(s * N + r) * slot_bytes;
+        st16_stage<kLocal>(rs, slot + (tv - own0[k]) * 16u, sentinel_canon<kKind>(load_vec<false>(src, full_vecs, nbytes)));
+      }
     }
   } else {
     // ---------------- consumer waves
