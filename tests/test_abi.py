@@ -122,3 +122,15 @@ def test_device_header_is_self_contained_and_demo_exports():
     for name in ("demo_scaled_allreduce_ll", "demo_sentinel_chain", "demo_ll128_reduce"):
         assert hasattr(L, name)
 
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py emulates the ranks on one GPU: --gpus N > 1 exits with a
+    message before touching any device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and not r.stdout
