@@ -198,8 +198,12 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
       // measured on MI355X (graph replay, N = 8): 256 threads below 64
       // slices' worth of units, 512 from there (fp16 Sentinel per call:
       // 128 KiB 4.13 -> 4.01 us, 256 KiB 5.49 -> 5.19, 512 KiB 8.13 -> 7.22;
-      // 64 KiB keeps 256: 3.70 against 3.96)
+      // 64 KiB keeps 256: 3.70 against 3.96).  Up to 4 x 512 units the
+      // exchange stays on at most four XCDs (slices): each slice runs on its
+      // own XCD, and the call waits for the slowest one (16 KiB x 8 bf16 LL:
+      // device span 2.0 -> 1.73 us, graph replay 3.40 -> 3.17 us per call)
       g.threads = h->threads ? (int)h->threads : (units >= (size_t)256 * 64 ? 512 : 256);
+      if (!h->threads && units > (size_t)4 * 256 && units <= (size_t)4 * 512) g.threads = 512;
       g.slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(units, (size_t)g.threads), 1, 64);
       break;
     }

@@ -690,11 +690,13 @@ def test_pipelined_short_last_chunk_regression(proto):
 
 def test_default_geometry_rules():
     """The host's default geometry: one-shot workgroups of 256 threads below
-    64 slices' worth of 8-byte units, 512 from there; pipelined messages cut into
-    the fewest chunks of at most the configured size, and a message shorter
-    than the chunk as one chunk."""
+    64 slices' worth of 8-byte units, 512 from there, and 512 as well while
+    that keeps a small message on at most four slices (XCDs) where 256 would
+    need more; pipelined messages cut into the fewest chunks of at most the
+    configured size, and a message shorter than the chunk as one chunk."""
     with comm_for(8, BF16, 8 << 20) as c:
-        for nbytes, threads in ((16384, 256), (131072 - 16, 256), (131072, 512), (524288, 512)):
+        for nbytes, threads in ((8192, 256), (8192 + 16, 512), (16384, 512), (16384 + 16, 256),
+                                (131072 - 16, 256), (131072, 512), (524288, 512)):
             geo = c.geometry(nbytes // 2, llar.SENTINEL)
             assert geo["threads"] == threads, (nbytes, geo)
             units = 2 * (-(-nbytes // 16))
