@@ -58,10 +58,21 @@ def device_inputs(cfg_id, n_ranks, n, dist, scale, rep=0):
     return bits, parts
 
 
+def order_after_current(stream):
+    """Make `stream` wait for the work already queued on the caller's current
+    stream.  Inputs and outputs are made there, and the caching allocator may
+    hand an output a block whose previous user (say, a dtype conversion's
+    temporary) is still being read there: without this order a call on
+    `stream` could write that block under the pending reader."""
+    import torch
+    stream.wait_stream(torch.cuda.current_stream())
+
+
 def time_calls(comm, parts, out, proto, steps, warmup, stream):
     """Per-call microseconds of `steps` back-to-back calls (HIP events on the
     launch stream), after `warmup` untimed calls."""
     import torch
+    order_after_current(stream)
     call = comm.prepare(parts, out, proto, stream=stream)
     with torch.cuda.stream(stream):
         for _ in range(warmup):
@@ -94,6 +105,7 @@ def time_graph(comm, parts, out, proto, steps, stream, per_graph=100):
     pays.  Captured calls read the device-resident epoch, so every replay is
     a fresh call."""
     import torch
+    order_after_current(stream)
     call = comm.prepare(parts, out, proto, stream=stream)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
@@ -126,6 +138,7 @@ def time_graph_fn(fn, steps, stream, per_graph=100):
     replays of a HIP graph of `per_graph` captured calls: GPU time only, no
     Python call overhead."""
     import torch
+    order_after_current(stream)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         fn()
@@ -152,6 +165,7 @@ def device_side_fn(comm, fn, calls, stream):
     """Median and minimum device-side microseconds of `fn` (first workgroup
     start to last workgroup end) over `calls` calls."""
     import torch
+    order_after_current(stream)
     import message_allreduce_amd as llar
     calls = min(calls, 60)
     comm.set_option("timing", 1)
@@ -310,6 +324,7 @@ def measure_device_api(stream, steps):
     # A captured launch repeats its arguments: the graph holds 100 launches
     # with epochs 1..100, and the LL staging is cleared (one fill kernel)
     # before each replay so that no line of the previous replay looks valid.
+    order_after_current(stream)
     per_graph = 100
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
@@ -378,6 +393,7 @@ def device_side_us(comm, parts, out, proto, calls, stream):
     """Median device-side microseconds (first workgroup start to last
     workgroup end, wall clock) over `calls` timed calls."""
     import torch
+    order_after_current(stream)
     import message_allreduce_amd as llar
     calls = min(calls, 60)
     comm.set_option("timing", 1)

@@ -342,11 +342,14 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
     const uint32_t Lr = (len + K - 1) / K;
     const uint32_t poff = (c & 1u) * a.parity_stride;
 
-    // ---- produce: data atomics for every owner's slice w
+    // ---- produce: data atomics for every owner's slice w.  An owner's
+    // slice is often a single block of 8 lines, so owner s's blocks start at
+    // wave (waves - s) mod waves: the waves of the workgroup add into
+    // different owners' lines at once instead of all owners falling to wave 0
     const bool silent = ((uint32_t)r == a.drop_rank);
     for (int s = 0; s < N && !silent; ++s) {
       const uint32_t l0 = sl0[s], l1 = min(sl1[s], Lr);
-      for (uint32_t lb = l0 + wave * 8u; lb < l1; lb += n_waves * 8u) {
+      for (uint32_t lb = l0 + ((wave + (uint32_t)s) % n_waves) * 8u; lb < l1; lb += n_waves * 8u) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           uint32_t d = (uint32_t)k * 64u + lane;  // dword of the 8-line block
@@ -378,11 +381,12 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
         }
       }
     }
-    // data of this wave acknowledged before any of its flags
+    // data of this wave acknowledged before any of its flags; a line is
+    // flagged by the wave that added its data (the same block assignment)
     drain_vm();
     for (int s = 0; s < N && !silent; ++s) {
       const uint32_t l0 = sl0[s], l1 = min(sl1[s], Lr);
-      for (uint32_t lb = l0 + wave * 8u; lb < l1; lb += n_waves * 8u) {
+      for (uint32_t lb = l0 + ((wave + (uint32_t)s) % n_waves) * 8u; lb < l1; lb += n_waves * 8u) {
         uint32_t line = lb + lane;
         if (lane < 8u && line < l1) {
           uint32_t off = poff + line * 128u;

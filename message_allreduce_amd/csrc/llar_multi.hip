@@ -243,28 +243,31 @@ __global__ void __launch_bounds__(512) k_rs_ll128(MultiArgs a) {
   if constexpr (!kAcc16) full = __float_as_uint((float)N);
   else full = E::from_f32((float)N);
 
-  // ---- produce: data atomics into every owner's lines of slice w, then counts
+  // ---- produce: data atomics into every owner's lines of slice w, then
+  // counts.  The (owner, line, dword) items are spread over all threads at
+  // once: a slice holds only a few lines per owner, and walking the owners
+  // in turn would leave most waves idle
   if ((uint32_t)r != drop_rank) {
-    for (int o = 0; o < N; ++o) {
+    const uint32_t per_owner = nl * 32u;
+    for (uint32_t it = threadIdx.x; it < (uint32_t)N * per_owner; it += blockDim.x) {
+      const uint32_t o = it / per_owner, rem = it % per_owner;
       const uint8_t* const seg = src + (uint64_t)o * blk;
-      for (uint32_t it = threadIdx.x; it < nl * 32u; it += blockDim.x) {
-        const uint32_t line = l0 + it / 32u, q = it % 32u;  // dword q of the line
-        uint8_t* const dst = stage + ((uint64_t)o * Lo + line) * llar_wire::kLL128LineBytes + q * 4u;
-        if constexpr (!kAcc16) {
-          const uint32_t i = line * K + q - 1u;
-          if (q == 0u || i >= c) continue;
-          float val;
-          if constexpr (E::kBytes == 4) val = __uint_as_float(reinterpret_cast<const uint32_t*>(seg)[i]);
-          else val = E::to_f32(reinterpret_cast<const uint16_t*>(seg)[i]);
-          llar_wire::ll128_add(reinterpret_cast<float*>(dst), val);
-        } else {
-          // 16-bit slots 2q and 2q+1 hold elements line*K + 2q - 1 and line*K + 2q
-          const uint32_t i0 = line * K + 2u * q - 1u, i1 = line * K + 2u * q;
-          const uint32_t lo = (q != 0u && i0 < c) ? reinterpret_cast<const uint16_t*>(seg)[i0] : 0u;
-          const uint32_t hi = (i1 < c) ? reinterpret_cast<const uint16_t*>(seg)[i1] : 0u;
-          if ((lo | hi) == 0u) continue;  // nothing to add (both +0)
-          llar_wire::ll128_add2<kKind == kKindBF16>(dst, s16x2{(short)lo, (short)hi});
-        }
+      const uint32_t line = l0 + rem / 32u, q = rem % 32u;  // dword q of the line
+      uint8_t* const dst = stage + ((uint64_t)o * Lo + line) * llar_wire::kLL128LineBytes + q * 4u;
+      if constexpr (!kAcc16) {
+        const uint32_t i = line * K + q - 1u;
+        if (q == 0u || i >= c) continue;
+        float val;
+        if constexpr (E::kBytes == 4) val = __uint_as_float(reinterpret_cast<const uint32_t*>(seg)[i]);
+        else val = E::to_f32(reinterpret_cast<const uint16_t*>(seg)[i]);
+        llar_wire::ll128_add(reinterpret_cast<float*>(dst), val);
+      } else {
+        // 16-bit slots 2q and 2q+1 hold elements line*K + 2q - 1 and line*K + 2q
+        const uint32_t i0 = line * K + 2u * q - 1u, i1 = line * K + 2u * q;
+        const uint32_t lo = (q != 0u && i0 < c) ? reinterpret_cast<const uint16_t*>(seg)[i0] : 0u;
+        const uint32_t hi = (i1 < c) ? reinterpret_cast<const uint16_t*>(seg)[i1] : 0u;
+        if ((lo | hi) == 0u) continue;  // nothing to add (both +0)
+        llar_wire::ll128_add2<kKind == kKindBF16>(dst, s16x2{(short)lo, (short)hi});
       }
     }
   }

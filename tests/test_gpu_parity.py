@@ -716,6 +716,20 @@ def test_default_geometry_rules():
         assert_exact(got, oracle.allreduce(bits, dt), dt, "1.5 MiB + 154 B")
 
 
+def test_ll128_default_geometry():
+    """LL128 defaults: one round keeps 256-thread workgroups while a slice
+    holds fewer than 32 lines of each owner and takes 512 from there; the
+    pipeline takes 512 threads and at most 32 slices."""
+    with comm_for(8, BF16, 2 << 20) as c:
+        geo = c.geometry(8192, llar.LL128)  # 265 lines, 34 per owner, one per slice
+        assert (geo["threads"], geo["slices"]) == (256, 34), geo
+        geo = c.geometry(1 << 20, llar.LL128)  # 33 826 lines, 4229 per owner, 67 per slice
+        assert (geo["threads"], geo["slices"]) == (512, 64), geo
+    with comm_for(8, F32, 4 << 20, chunk_bytes=65536) as c:
+        geo = c.geometry(1 << 20, llar.LL128_PIPELINED)  # 529 lines a chunk, 66-67 per owner
+        assert (geo["threads"], geo["slices"], geo["chunks"]) == (512, 32, 64), geo
+
+
 # --------------------------------------------------------------------------- the barrier ablation
 @pytest.mark.parametrize("placement", [1, 2], ids=["spread", "local"])
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
