@@ -202,7 +202,7 @@ int llar_clear_device_status(llar_comm* h);
  *   "spin_timeout_us"  device poll limit in microseconds (default 200000)
  *   "ll128_acc"        LL128 staging type: 0 = binary32 (default), 1 = the I/O type (16-bit packed)
  *   "chunk_bytes"      largest per-rank chunk of the pipelined protocols (0 = tuned default:
- *                      128 KiB for LL128, 1 MiB for the Sentinel; clamped to [1 KiB, 4 MiB]); a
+ *                      1 MiB for both; clamped to [1 KiB, 4 MiB]); a
  *                      message is cut into the fewest equal chunks of at most this size (whole
  *                      16-byte vectors for the Sentinel), so that every owner gets an even share
  *                      of every chunk
