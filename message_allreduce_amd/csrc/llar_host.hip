@@ -711,7 +711,9 @@ int run_multi(llar_comm* h, const void* const* ins, void* const* outs, int n_rec
     const size_t K = acc16 ? 63 : 31;
     const size_t lo_lines = ceil_div(count, K);
     if ((size_t)N * lo_lines * 128 > reg->parity_stride) return fail(LLAR_ERR_UNSUPPORTED);
-    const int slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(lo_lines, (size_t)8), 1, 64);
+    // one slice per line of an owner's segment, up to 64 (measured on
+    // MI355X: 16 KiB x 8 bf16 4.6 us against 5.7 at one slice per 8 lines)
+    const int slices = h->slices ? (int)h->slices : clampi((long long)lo_lines, 1, 64);
     LaunchSpec ls;
     memset(&ls, 0, sizeof(ls));
     ls.kind = h->kind;
