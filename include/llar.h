@@ -243,6 +243,18 @@ int llar_clear_device_status(llar_comm* h);
  *   "device_epoch"     1 = always read the device-resident epoch; otherwise the host numbers
  *                      stream-ordered calls and the device epoch is used only on a stream that is
  *                      being captured into a graph (replays then never reuse an epoch)
+ *                      Epochs (the LL flag, the agihunt.info summary's LL paragraph) run 1 .. 2^31-1
+ *                      for host-numbered calls and 2^31 + (1 .. 2^31-1) for device-numbered ones,
+ *                      then wrap.  The state that holds epoch values (LL staging, owner-credit
+ *                      progress words, per-workgroup epoch words) is cleared at the wrap, so no
+ *                      line written a whole cycle earlier can pass for a new one: by fills
+ *                      enqueued on the stream of the first host-numbered call after a host wrap,
+ *                      and by the wrapping device-numbered call itself on the device (its last
+ *                      workgroup waits for the others, clears, then advances the epoch)
+ *   "debug_host_epoch", "debug_device_epoch"
+ *                      tests: the epoch of the next host-numbered call (1 .. 2^31-1), or the
+ *                      device-resident epoch (2^31+1 .. 2^32-1; the per-workgroup epoch words are
+ *                      zeroed, staging is left as it is); llar_get_option reads them back
  *   "auto_threshold_sentinel", "auto_threshold_ll128", "auto_threshold_pipelined"
  *                      AUTO size boundaries in bytes per rank: LL up to 64 KiB, one-shot Sentinel
  *                      up to 512 KiB, pipelined Sentinel above; LL128 only above its own threshold

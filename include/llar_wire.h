@@ -33,7 +33,7 @@
  *   LL       line = {data0, epoch, data1, epoch}: each 8-byte half carries
  *            the flag, so either half may land first.  Empty buffer: zero
  *            bytes (epoch 0 never occurs).  No reset between uses: bump the
- *            epoch (next_epoch).
+ *            epoch (next_epoch), and zero the buffer when it wraps.
  *   Sentinel slot = 16 payload bytes; empty = all-ones (a negative NaN in
  *            binary32, binary16 and bfloat16).  The sender replaces a datum
  *            equal to all-ones by the pattern one below (still a negative
@@ -65,12 +65,19 @@ constexpr int kCpolSc1 = 16;
 enum Scope : int { kXcd = 0, kDevice = 1 };
 
 // ---- epochs --------------------------------------------------------------------
-// LL epochs are non-zero 32-bit values, a new one for every use of a buffer:
-// 1, 2, ..., 2^32 - 1, 1, ...
+// LL epochs are non-zero 31-bit values, a new one for every use of a buffer:
+// 1, 2, ..., 2^31 - 1, then 1 again (the library numbers its stream-ordered
+// calls in this range and its device-numbered ones in 2^31 + this range, so
+// the two never meet).  A wrap brings every value back: a line last written
+// at epoch e and left alone for a whole cycle would pass for a fresh line
+// when e comes round again, so the buffer must be zeroed before the first
+// use after a wrap -- epoch_wraps(e) is true for the last epoch of the range.
+constexpr uint32_t kEpochLast = 0x7FFFFFFFu;
 __host__ __device__ __forceinline__ uint32_t next_epoch(uint32_t e) {
-  const uint32_t n = e + 1u;
+  const uint32_t n = (e + 1u) & kEpochLast;
   return n == 0u ? 1u : n;
 }
+__host__ __device__ __forceinline__ bool epoch_wraps(uint32_t e) { return (e & kEpochLast) == kEpochLast; }
 
 // ---- the buffer ------------------------------------------------------------------
 // Descriptor of `bytes` bytes at `base` (device memory).  The inputs are

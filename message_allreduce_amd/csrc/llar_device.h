@@ -196,18 +196,27 @@ struct Ctrl {
   uint32_t pad4[31];
   uint32_t timing_grid[kTimingRing];  // per epoch slot: workgroups that recorded a span
   uint64_t* timing_wg;  // [kTimingRing][kTimingMaxWgs][2]: each workgroup's start, end (wall ticks)
+  // state that carries epoch values, cleared when the device epoch wraps:
+  // the LL region (lines {d0, e, d1, e}) and the owner-credit progress words
+  uint8_t* ll_base;
+  uint64_t ll_bytes;
+  uint8_t* credit_base;
+  uint64_t credit_bytes;
   uint32_t read_epoch[kTimingMaxWgs];  // device-numbered calls: the epoch workgroup b has read
 };
 
 // Epochs: host-numbered calls use 1 .. 2^31-1, device-numbered (graph
-// capture) calls use 2^31 + (1 .. 2^31-1); 0 never occurs.
-__host__ __device__ __forceinline__ uint32_t next_host_epoch(uint32_t e) {
-  uint32_t n = (e + 1u) & 0x7FFFFFFFu;
-  return n == 0u ? 1u : n;
-}
+// capture) calls use 2^31 + (1 .. 2^31-1); 0 never occurs.  Both sequences
+// wrap: the state that holds epoch values is cleared before the first call
+// after a wrap (host: stream-ordered fills before that call; device: by the
+// wrapping call itself, in wg_end).
+__host__ __device__ __forceinline__ uint32_t next_host_epoch(uint32_t e) { return llar_wire::next_epoch(e); }
 __host__ __device__ __forceinline__ uint32_t next_device_epoch(uint32_t e) {
-  return 0x80000000u | next_host_epoch(e & 0x7FFFFFFFu);
+  return 0x80000000u | llar_wire::next_epoch(e & llar_wire::kEpochLast);
 }
+// per-workgroup word written by every workgroup of a device-numbered call
+// that wraps the epoch once its staging accesses are done (never an epoch)
+constexpr uint32_t kWrapDone = 1u;
 
 __device__ __forceinline__ void raise_status(Ctrl* c, uint32_t bits) {
   __hip_atomic_fetch_or(&c->status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -252,37 +261,82 @@ __device__ __forceinline__ WgState wg_begin(Ctrl* ctrl, uint32_t host_epoch, boo
   return st;
 }
 
+// Wait (one wave) until words[0 .. grid) all equal `want`, reading them with
+// 16-byte loads, four per lane in flight (a pass costs one memory round trip
+// per 1024 workgroups); false when the wall-clock bound expires (every
+// workgroup is resident, so the wait ends; the bound is a safeguard).
+__device__ __forceinline__ bool wait_words(uint32_t* words, uint32_t grid, uint32_t want) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(words, grid * 4u);
+  llar_wire::Poll poll(100000000ull);  // 1 s
+  while (true) {
+    bool all = true;
+    for (uint32_t w0 = 0; w0 < grid; w0 += 1024u) {
+      u32x4 v[4];
+#pragma unroll
+      for (uint32_t k = 0; k < 4u; ++k) v[k] = ld16_coh(rr, (w0 + (k * 64u + lane) * 4u) * 4u);
+#pragma unroll
+      for (uint32_t k = 0; k < 4u; ++k)
+#pragma unroll
+        for (uint32_t t = 0; t < 4u; ++t) all &= (w0 + (k * 64u + lane) * 4u + t >= grid) | (v[k][t] == want);
+    }
+    if (__all((int)all)) return true;
+    if (poll.expired()) return false;
+  }
+}
+
+// Zero `bytes` (a multiple of 16) at `base` with device-coherent stores,
+// every thread of the workgroup taking 16-byte pieces.
+__device__ __forceinline__ void clear_region(uint8_t* base, uint64_t bytes) {
+  if (base == nullptr || bytes == 0u) return;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint32_t)bytes);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (uint64_t off = (uint64_t)threadIdx.x * 16u; off < bytes; off += (uint64_t)blockDim.x * 16u)
+    st16_coh(r, (uint32_t)off, zero);
+}
+
+// The last call of the device epoch range (2^32 - 1): the next epoch,
+// 2^31 + 1, was used 2^31 - 1 calls ago, and an LL line or progress word
+// that no call has written since would pass for a fresh one.  Every
+// workgroup of this call, once its own staging accesses are done, records
+// kWrapDone; the grid's last workgroup waits for all of them -- nothing of
+// this call touches staging any more -- zeroes the LL region, the
+// progress words and the per-workgroup epoch words, and only then
+// advances the epoch.  (A once-per-cycle clear of a few hundred MiB at most;
+// the next call is ordered after this one on the stream.)
+__device__ __forceinline__ void wrap_end(Ctrl* ctrl, const WgState& st, uint32_t grid) {
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&ctrl->read_epoch[blockIdx.x], kWrapDone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (blockIdx.x != grid - 1u) return;
+  if (threadIdx.x < 64u) {
+    // (an expired wait leaves the status set; the call's output is then
+    // undefined anyway, and the epoch still advances)
+    const bool ok = wait_words(ctrl->read_epoch, grid, kWrapDone);
+    if (threadIdx.x == 0 && !ok) raise_status(ctrl, kStatusTimeout);
+  }
+  __syncthreads();
+  clear_region(ctrl->ll_base, ctrl->ll_bytes);
+  clear_region(ctrl->credit_base, ctrl->credit_bytes);
+  clear_region(reinterpret_cast<uint8_t*>(ctrl->read_epoch), sizeof(ctrl->read_epoch));
+  drain_vm();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&ctrl->epoch, next_device_epoch(st.epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ void wg_end(Ctrl* ctrl, const WgState& st, uint32_t host_epoch, uint32_t grid, bool timing,
                                        bool idle) {
-  if (timing) {
+  const bool wrap = st.counted && llar_wire::epoch_wraps(st.epoch);
+  if (timing || wrap) {
     drain_vm();
     __syncthreads();
   }
-  if (st.counted && blockIdx.x == grid - 1u && threadIdx.x < 64u) {
-    // every workgroup of the grid has read this call's epoch (all of them
-    // are resident, so the wait ends; the wall-clock bound is a safeguard)
-    // (each pass reads every word with 16-byte loads, four per lane in
-    // flight, so a pass costs one memory round trip per 1024 workgroups)
-    const uint32_t lane = threadIdx.x;
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(ctrl->read_epoch, grid * 4u);
-    llar_wire::Poll poll(100000000ull);  // 1 s
-    while (true) {
-      bool all = true;
-      for (uint32_t w0 = 0; w0 < grid; w0 += 1024u) {
-        u32x4 v[4];
-#pragma unroll
-        for (uint32_t k = 0; k < 4u; ++k) v[k] = ld16_coh(rr, (w0 + (k * 64u + lane) * 4u) * 4u);
-#pragma unroll
-        for (uint32_t k = 0; k < 4u; ++k)
-#pragma unroll
-          for (uint32_t t = 0; t < 4u; ++t) all &= (w0 + (k * 64u + lane) * 4u + t >= grid) | (v[k][t] == st.epoch);
-      }
-      if (__all((int)all)) break;
-      if (poll.expired()) {
-        raise_status(ctrl, kStatusTimeout);
-        break;
-      }
-    }
+  if (wrap) {
+    wrap_end(ctrl, st, grid);
+  } else if (st.counted && blockIdx.x == grid - 1u && threadIdx.x < 64u) {
+    // every workgroup of the grid has read this call's epoch before it
+    // advances
+    if (!wait_words(ctrl->read_epoch, grid, st.epoch)) raise_status(ctrl, kStatusTimeout);
     if (threadIdx.x == 0)
       __hip_atomic_store(&ctrl->epoch, next_device_epoch(st.epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

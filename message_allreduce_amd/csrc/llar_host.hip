@@ -72,6 +72,7 @@ struct llar_comm {
   uint64_t* credit = nullptr;      // kCreditWords progress words of the pipelined Sentinel's owner credit
   int pipe_trace_grid = 0;
   uint32_t host_epoch = 1;         // epoch of the next host-numbered call
+  bool host_wrap_pending = false;  // the host epoch wrapped: clear the epoch-tagged state before the next call
   bool last_call_device = false;   // the last call read the device-resident epoch
   // options
   long long spin_timeout_us = 200000;
@@ -119,6 +120,10 @@ hipError_t init_ctrl(llar_comm* h) {
   memset(&c, 0, sizeof(c));
   c.epoch = 0x80000001u;  // first device-numbered epoch
   c.timing_wg = h->timing_wg;
+  c.ll_base = h->ll.ptr;
+  c.ll_bytes = h->ll.ptr ? h->ll.bytes : 0u;
+  c.credit_base = reinterpret_cast<uint8_t*>(h->credit);
+  c.credit_bytes = h->credit ? kCreditWords * sizeof(uint64_t) : 0u;
   return hipMemcpy(h->ctrl, &c, sizeof(c), hipMemcpyHostToDevice);
 }
 
@@ -412,7 +417,6 @@ llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes) {
 
   e = hipMalloc(&h->timing_wg, (size_t)kTimingRing * kTimingMaxWgs * 2 * sizeof(uint64_t));
   if (e == hipSuccess) e = hipMalloc(&h->ctrl, sizeof(Ctrl));
-  if (e == hipSuccess) e = init_ctrl(h);
   if (e == hipSuccess) e = hipMalloc(&h->trace, (size_t)kTraceMaxWgs * kTraceWords * sizeof(uint64_t));
   if (e == hipSuccess) e = hipMemset(h->trace, 0, (size_t)kTraceMaxWgs * kTraceWords * sizeof(uint64_t));
   if (e == hipSuccess) e = hipMalloc(&h->pipe_trace, (size_t)kPipeTraceMaxWgs * kPipeTraceWords * sizeof(uint64_t));
@@ -424,6 +428,8 @@ llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes) {
   if (e == hipSuccess) e = alloc_region(h->ll128, 2 * h->ll128.parity_stride, 0);
   if (e == hipSuccess) e = alloc_region(h->ll128_pipe, 2 * h->ll128_pipe.parity_stride, 0);
   if (e == hipSuccess) e = alloc_region(h->sent_pipe, kSentinelPipeMaxBuffers * h->sent_pipe.parity_stride, 0xFF);
+  // the control block names the regions that a wrap of the epoch clears
+  if (e == hipSuccess) e = init_ctrl(h);
   // every region is addressed with 32-bit offsets
   const Region* regs[] = {&h->ll, &h->sent, &h->ll128, &h->ll128_pipe, &h->sent_pipe};
   for (const Region* r : regs)
@@ -508,7 +514,25 @@ bool call_epoch(const llar_comm* h, hipStream_t stream, bool& device_epoch, uint
 
 void finish_call(llar_comm* h, bool device_epoch) {
   h->last_call_device = device_epoch;
-  if (!device_epoch) h->host_epoch = next_host_epoch(h->host_epoch);
+  if (!device_epoch) {
+    if (llar_wire::epoch_wraps(h->host_epoch)) h->host_wrap_pending = true;
+    h->host_epoch = next_host_epoch(h->host_epoch);
+  }
+}
+
+// After the host epoch wrapped, every epoch value comes round again: an LL
+// line or owner-credit progress word that no call has written for a whole
+// cycle of 2^31 - 1 calls would pass for the new call's.  The first
+// host-numbered call after the wrap therefore clears both first, ordered on
+// its own stream.  (Host-numbered calls are never captured into a graph;
+// device-numbered calls clear at their own wrap on the device.)
+hipError_t clear_after_host_wrap(llar_comm* h, bool device_epoch, hipStream_t stream) {
+  if (device_epoch || !h->host_wrap_pending) return hipSuccess;
+  hipError_t e = hipSuccess;
+  if (h->ll.ptr) e = hipMemsetAsync(h->ll.ptr, 0, h->ll.bytes, stream);
+  if (e == hipSuccess && h->credit) e = hipMemsetAsync(h->credit, 0, kCreditWords * sizeof(uint64_t), stream);
+  if (e == hipSuccess) h->host_wrap_pending = false;
+  return e;
 }
 
 // Issue one call of the planned kernel.  `n_launch` ranks take part (the
@@ -667,6 +691,7 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
     }
   }
   if (!reg->ptr) return fail(LLAR_ERR_UNSUPPORTED);
+  if (clear_after_host_wrap(h, device_epoch, stream) != hipSuccess) return fail(LLAR_ERR_HIP);
   hipError_t e = launch(ls, stream);
   if (e != hipSuccess) return fail(LLAR_ERR_HIP);
   finish_call(h, device_epoch);
@@ -747,6 +772,7 @@ int run_multi(llar_comm* h, const void* const* ins, void* const* outs, int n_rec
     a.keep = h->keep_staging ? 1u : 0u;
     a.drop_rank = h->debug_drop_rank < 0 ? 0xFFFFFFFFu : (uint32_t)h->debug_drop_rank;
     a.host_epoch = host_epoch;
+    if (clear_after_host_wrap(h, device_epoch, stream) != hipSuccess) return fail(LLAR_ERR_HIP);
     hipError_t e = launch(ls, stream);
     if (e != hipSuccess) return fail(LLAR_ERR_HIP);
     finish_call(h, device_epoch);
@@ -808,6 +834,7 @@ int run_multi(llar_comm* h, const void* const* ins, void* const* outs, int n_rec
   a.keep = h->keep_staging ? 1u : 0u;
   a.drop_rank = h->debug_drop_rank < 0 ? 0xFFFFFFFFu : (uint32_t)h->debug_drop_rank;
   a.host_epoch = host_epoch;
+  if (clear_after_host_wrap(h, device_epoch, stream) != hipSuccess) return fail(LLAR_ERR_HIP);
   hipError_t e = launch(ls, stream);
   if (e != hipSuccess) return fail(LLAR_ERR_HIP);
   finish_call(h, device_epoch);
@@ -933,8 +960,31 @@ static long long* option_slot(llar_comm* h, const char* key) {
   return nullptr;
 }
 
+// Tests of the epoch wrap: place the next call's epoch anywhere in its
+// range.  "debug_host_epoch" numbers the next stream-ordered call (1 ..
+// 2^31 - 1); "debug_device_epoch" sets the device-resident epoch (2^31 + 1 ..
+// 2^32 - 1) and zeroes the per-workgroup epoch words, as a fresh control
+// block has them.  Neither touches staging: lines written at earlier epochs
+// stay, as they would after a real cycle of calls.
+static int set_debug_epoch(llar_comm* h, bool device, long long value) {
+  if (!device) {
+    if (value < 1 || value > (long long)llar_wire::kEpochLast) return fail(LLAR_ERR_ARG);
+    h->host_epoch = (uint32_t)value;
+    return LLAR_OK;
+  }
+  if (value <= 0x80000000ll || value > 0xFFFFFFFFll) return fail(LLAR_ERR_ARG);
+  if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
+  const uint32_t e = (uint32_t)value;
+  if (hipMemcpy(&h->ctrl->epoch, &e, sizeof(e), hipMemcpyHostToDevice) != hipSuccess) return fail(LLAR_ERR_HIP);
+  if (hipMemset(h->ctrl->read_epoch, 0, sizeof(h->ctrl->read_epoch)) != hipSuccess) return fail(LLAR_ERR_HIP);
+  if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
+  return LLAR_OK;
+}
+
 int llar_set_option(llar_comm* h, const char* key, long long value) {
   if (!h || !key) return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "debug_host_epoch") == 0) return set_debug_epoch(h, false, value);
+  if (strcmp(key, "debug_device_epoch") == 0) return set_debug_epoch(h, true, value);
   long long* slot = option_slot(h, key);
   if (!slot) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "spin_timeout_us") == 0 && value < 1) return fail(LLAR_ERR_ARG);
@@ -967,6 +1017,17 @@ int llar_get_option(llar_comm* h, const char* key, long long* value) {
   if (!h || !key || !value) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "local_placement_ok") == 0) {
     *value = h->local_ok ? 1 : 0;
+    return LLAR_OK;
+  }
+  if (strcmp(key, "debug_host_epoch") == 0) {
+    *value = (long long)h->host_epoch;
+    return LLAR_OK;
+  }
+  if (strcmp(key, "debug_device_epoch") == 0) {
+    uint32_t e = 0;
+    if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
+    if (hipMemcpy(&e, &h->ctrl->epoch, sizeof(e), hipMemcpyDeviceToHost) != hipSuccess) return fail(LLAR_ERR_HIP);
+    *value = (long long)e;
     return LLAR_OK;
   }
   long long* slot = option_slot(h, key);

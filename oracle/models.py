@@ -43,10 +43,63 @@ LL_LINE_BYTES = 16
 LL_PAYLOAD_BYTES = 8
 
 
-def next_epoch(e: int) -> int:
-    """Epochs run 1, 2, ..., 2^32-1, 1, ...; 0 means 'never written'."""
-    e = (e + 1) & 0xFFFFFFFF
-    return 1 if e == 0 else e
+EPOCH_LAST = 0x7FFFFFFF       # last epoch of a range; 0 means 'never written'
+DEVICE_EPOCH_BIT = 0x80000000
+
+
+def next_epoch(e: int, last: int = EPOCH_LAST) -> int:
+    """Host-numbered epochs run 1, 2, ..., last, 1, ... (last = 2^31 - 1).
+    A smaller `last` gives the same policy on a short cycle for the models
+    below."""
+    e = e + 1
+    return 1 if e > last else e
+
+
+def next_device_epoch(e: int) -> int:
+    """Device-numbered epochs run 2^31 + (1 .. 2^31 - 1): the host range with
+    the top bit set, so the two ranges never meet."""
+    return DEVICE_EPOCH_BIT | next_epoch(e & EPOCH_LAST)
+
+
+def epoch_wraps(e: int, last: int = EPOCH_LAST) -> bool:
+    """True for the last epoch of a range: the next use reuses a value."""
+    return (e & EPOCH_LAST) == last
+
+
+class LLRegion:
+    """A receive buffer of LL lines reused by a sequence of calls, with the
+    epoch policy above.  The LL paragraph makes the flag the only arrival
+    signal, so a line the consumer accepts must have been written by the
+    producer of the same call.  A call of `n_lines` lines with epoch e has
+    its producer write lines [0, n_lines) with e; before that, the consumer
+    may look at any of them.  `stale_hits` records lines the consumer would
+    accept although this call's producer has not written them yet.
+
+    clear_at_wrap=True zeroes the region before the first call after a wrap
+    (what the library does); False keeps it (the failure mode)."""
+
+    def __init__(self, n_lines: int, last: int = EPOCH_LAST, clear_at_wrap: bool = True):
+        self.flags = np.zeros(n_lines, dtype=np.int64)  # epoch word of each line (0 = zeroed)
+        self.last = last
+        self.clear_at_wrap = clear_at_wrap
+        self.epoch = 1
+        self.pending_clear = False
+        self.stale_hits = 0
+
+    def call(self, n_lines: int) -> int:
+        """One call over the first n_lines lines; returns the stale lines the
+        consumer could have accepted before the producer wrote them."""
+        if self.pending_clear:
+            self.flags[:] = 0
+            self.pending_clear = False
+        e = self.epoch
+        hits = int(np.count_nonzero(self.flags[:n_lines] == e))
+        self.stale_hits += hits
+        self.flags[:n_lines] = e
+        if epoch_wraps(e, self.last) and self.clear_at_wrap:
+            self.pending_clear = True
+        self.epoch = next_epoch(e, self.last)
+        return hits
 
 
 def ll_pack(payload_words: np.ndarray, epoch: int) -> np.ndarray:

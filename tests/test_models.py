@@ -70,14 +70,50 @@ def test_ll_pack_unpack_roundtrip_and_stale_detection():
 
 
 def test_epoch_sequence_skips_zero():
+    """Host epochs: 1 .. 2^31-1, then 1 again; device epochs: the same with
+    bit 31 set; the two ranges never meet and neither holds 0 (the state of a
+    zeroed line)."""
     assert models.next_epoch(1) == 2
-    assert models.next_epoch(0xFFFFFFFF) == 1
-    e, seen = 0xFFFFFFF0, set()
-    for _ in range(40):
-        e = models.next_epoch(e)
-        assert e != 0
-        seen.add(e)
-    assert len(seen) == 40
+    assert models.next_epoch(0x7FFFFFFF) == 1
+    assert models.next_device_epoch(0xFFFFFFFF) == 0x80000001
+    assert models.next_device_epoch(0x80000001) == 0x80000002
+    assert models.epoch_wraps(0x7FFFFFFF) and models.epoch_wraps(0xFFFFFFFF)
+    assert not models.epoch_wraps(0x7FFFFFFE) and not models.epoch_wraps(0x80000001)
+    for start, step in ((0x7FFFFFF0, models.next_epoch), (0xFFFFFFF0, models.next_device_epoch)):
+        e, seen = start, []
+        for _ in range(40):
+            e = step(e)
+            assert e != 0
+            seen.append(e)
+        # one wrap inside the window: 15 values before it, then 1.., all distinct within a cycle
+        assert len(set(seen)) == 40
+        host = step is models.next_epoch
+        assert all(((x & 0x80000000) == 0) == host for x in seen)
+
+
+def test_ll_region_reuse_across_the_epoch_wrap():
+    """The LL flag is the only arrival signal (LL paragraph), so a line that
+    carries the current epoch must have been written by the current call.
+    On a short cycle (last epoch 7) a large message, then small ones for the
+    rest of the cycle, then the large one again: without clearing at the
+    wrap the large message's tail lines still carry their old epoch when it
+    comes round, and would be accepted before the producer writes them;
+    clearing at the wrap leaves none, over many cycles and random sizes."""
+    r = models.LLRegion(64, last=7, clear_at_wrap=False)
+    r.call(64)                   # epoch 1 writes every line
+    for _ in range(6):           # epochs 2..7 write only the first 4 lines
+        r.call(4)
+    assert r.call(64) == 60      # epoch 1 again: 60 stale lines look fresh
+    rng = np.random.default_rng(7)
+    for clear in (True, False):
+        r = models.LLRegion(64, last=7, clear_at_wrap=clear)
+        r.call(64)
+        for _ in range(6):
+            r.call(4)
+        r.call(64)
+        for _ in range(2000):
+            r.call(int(rng.integers(1, 65)))
+        assert (r.stale_hits == 0) == clear
 
 
 def test_ll_payload_padding_is_zero_and_bytes_are_preserved():
