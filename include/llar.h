@@ -104,6 +104,33 @@ llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes);
 int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t n_elems,
                    llar_dtype dtype, llar_protocol protocol, void* stream);
 
+/* The LL one-shot AllReduce of llar_allreduce (out[i] = partials[0][i] + ...
+ * + partials[n_ranks-1][i], binary64 in rank order, one rounding; bit for
+ * bit the result of llar_allreduce with LLAR_LL) for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It needs no communicator and calls no
+ * allocating routine: staging and control state live in one static device
+ * array of 2 MiB per GPU, held by each GPU the library runs on until the
+ * process ends.
+ *
+ * n_ranks:  1..8 (above 8: LLAR_ERR_UNSUPPORTED).
+ * partials: host array of n_ranks device pointers; out: device pointer; all
+ *           16-byte aligned; out may alias a partial.  dtype: any llar_dtype.
+ * n_elems:  at most 64 KiB per rank (n_elems * sizeof(dtype) <= 65536),
+ *           else LLAR_ERR_UNSUPPORTED with nothing enqueued; 0 is a no-op.
+ * The first call on a device sets that device's array up (synchronous
+ *   copies; LLAR_ERR_UNSUPPORTED if that call's stream is being captured --
+ *   make one eager call first).  Later calls only enqueue one kernel, and
+ *   may be captured into graphs (replays number themselves on the device).
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ *   contents: calls on one GPU must be ordered (one stream, or synchronised);
+ *   calls that overlap on one GPU race and their results are undefined.
+ * Device-side errors (a poll timeout) latch in the array's status word and
+ *   are not reported by this call; the communicator's status calls do not
+ *   see them. */
+int llar_allreduce_noalloc(int n_ranks, const void* const* partials, void* out, size_t n_elems,
+                           llar_dtype dtype, void* stream);
+
 /* Point-to-point copy: recv_buf[i] = send_buf[i] for i < n_elems, moved by
  * one sending rank to one receiving rank through the LL or Sentinel staging
  * of this communicator -- the stage-to-stage activation transfer of pipeline

@@ -26,7 +26,7 @@ import os
 __all__ = [
     "FP32", "FP16", "BF16", "AUTO", "LL", "SENTINEL", "LL128", "LL128_PIPELINED", "SENTINEL_PIPELINED",
     "PROTOCOLS", "LlarError", "lib", "library_path", "llar_create", "llar_allreduce", "llar_destroy",
-    "llar_send_recv", "llar_reduce_scatter", "llar_all_gather", "llar_set_option", "llar_get_option", "llar_get_device_status", "llar_clear_device_status",
+    "llar_send_recv", "llar_reduce_scatter", "llar_all_gather", "llar_allreduce_noalloc", "llar_set_option", "llar_get_option", "llar_get_device_status", "llar_clear_device_status",
     "llar_select_protocol", "llar_debug_copy_staging", "llar_staging_bytes", "llar_get_epoch",
     "llar_get_timing", "llar_wallclock_hz", "llar_launch_geometry", "llar_floor_measure",
     "llar_status_string", "llar_last_error", "llar_get_trace", "llar_get_pipeline_trace", "Communicator", "EXPORTED_SYMBOLS",
@@ -46,6 +46,7 @@ EXPORTED_SYMBOLS = (
     "llar_select_protocol", "llar_debug_copy_staging", "llar_staging_bytes", "llar_get_epoch",
     "llar_get_timing", "llar_wallclock_hz", "llar_launch_geometry", "llar_floor_measure",
     "llar_get_trace", "llar_get_pipeline_trace", "llar_send_recv", "llar_reduce_scatter", "llar_all_gather",
+    "llar_allreduce_noalloc",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +74,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "llar_create": (vp, [i32, i32, sz]),
         "llar_allreduce": (i32, [vp, ctypes.POINTER(vp), vp, sz, i32, i32, vp]),
+        "llar_allreduce_noalloc": (i32, [i32, ctypes.POINTER(vp), vp, sz, i32, vp]),
         "llar_send_recv": (i32, [vp, vp, vp, sz, i32, i32, vp]),
         "llar_reduce_scatter": (i32, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), sz, i32, i32, vp]),
         "llar_all_gather": (i32, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, sz, i32, i32, vp]),
@@ -121,6 +123,14 @@ def llar_allreduce(h: int, partials, out: int, n_elems: int, dtype: int, protoco
     arr = (ctypes.c_void_p * len(partials))(*[int(p) for p in partials])
     return lib().llar_allreduce(h, arr, ctypes.c_void_p(int(out)), int(n_elems), int(dtype), int(protocol),
                                 ctypes.c_void_p(int(stream)))
+
+
+def llar_allreduce_noalloc(n_ranks: int, partials, out: int, n_elems: int, dtype: int, stream: int) -> int:
+    """The LL AllReduce over the library's static per-GPU array (no
+    communicator, no allocation); partials: device pointers (ints)."""
+    arr = (ctypes.c_void_p * len(partials))(*[int(p) for p in partials])
+    return lib().llar_allreduce_noalloc(int(n_ranks), arr, ctypes.c_void_p(int(out)), int(n_elems), int(dtype),
+                                        ctypes.c_void_p(int(stream)))
 
 
 def llar_send_recv(h: int, send: int, recv: int, n_elems: int, dtype: int, protocol: int, stream: int) -> int:

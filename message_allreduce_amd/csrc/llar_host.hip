@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <new>
 #include <numeric>
 #include <vector>
@@ -1126,3 +1127,118 @@ double llar_wallclock_hz(void) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// llar_allreduce_noalloc: the LL one-shot AllReduce for callers that cannot
+// allocate device memory (code under graph capture, tight serving loops,
+// harnesses that forbid hipMalloc).  Its staging and control block live in
+// one static device array per GPU instead of a communicator's allocations.
+// ---------------------------------------------------------------------------
+namespace {
+
+// largest message per rank: the AUTO table's LL range
+constexpr size_t kNoAllocMaxBytes = 64u << 10;
+constexpr int kNoAllocMaxRanks = 8;
+constexpr size_t kNoAllocCtrlBytes = (sizeof(Ctrl) + 255u) / 256u * 256u;
+// LL region laid out for the largest rank count: [parity 2][sender 1..7][vector][2 lines]
+constexpr size_t kNoAllocRankStride = (kNoAllocMaxBytes / 16u + (size_t)kNoAllocMaxRanks) * 32u;
+constexpr size_t kNoAllocParityStride = kNoAllocRankStride * (size_t)(kNoAllocMaxRanks - 1);
+constexpr size_t kNoAllocLLBytes = 2u * kNoAllocParityStride;
+constexpr size_t kNoAllocScratchBytes = 2u << 20;
+static_assert(kNoAllocCtrlBytes + kNoAllocLLBytes <= kNoAllocScratchBytes, "no-alloc layout exceeds the scratch array");
+constexpr int kNoAllocMaxDevices = 64;
+
+struct NoAllocDevice {
+  bool ready = false;
+  uint8_t* ptr = nullptr;  // device address of this GPU's copy of `scratch`
+  llar_comm comm;          // its regions point into that copy
+};
+NoAllocDevice g_noalloc[kNoAllocMaxDevices];
+std::mutex g_noalloc_mu;
+
+}  // namespace
+
+// Each GPU the library runs on holds one copy of this array until the
+// process ends: the control block (epochs, status, per-workgroup epoch
+// words) followed by the LL staging.  Host code never names it except to
+// look up its device address.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// Once per device, with that device current and outside stream capture:
+// find this GPU's copy of the array, check the placement of workgroups on
+// XCDs (the probe writes into the staging, which is then zeroed), and write
+// a fresh control block.  No allocation.
+int noalloc_setup(NoAllocDevice& d, int dev, hipStream_t stream) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return LLAR_ERR_HIP;
+  if (cap != hipStreamCaptureStatusNone) return LLAR_ERR_UNSUPPORTED;  // set-up makes synchronous copies
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return LLAR_ERR_HIP;
+  uint8_t* const base = static_cast<uint8_t*>(p);
+  llar_comm& c = d.comm;
+  c.device = dev;
+  int cus = 0, wc = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return LLAR_ERR_HIP;
+  if (hipDeviceGetAttribute(&wc, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return LLAR_ERR_HIP;
+  c.cu_count = cus;
+  c.wall_hz = wc > 0 ? wc * 1000.0 : 100e6;
+  c.max_bytes = kNoAllocMaxBytes;
+  c.ctrl = reinterpret_cast<Ctrl*>(base);
+  c.ll.ptr = base + kNoAllocCtrlBytes;
+  c.ll.bytes = kNoAllocLLBytes;
+  c.ll.rank_stride = kNoAllocRankStride;
+  c.ll.parity_stride = kNoAllocParityStride;
+  // the other protocols' regions, the timing ring, traces and progress
+  // words stay absent: this entry point runs the LL exchange only
+  const int G = 64;
+  uint32_t hx[G];
+  uint32_t* probe = reinterpret_cast<uint32_t*>(c.ll.ptr);
+  if (launch_xcc_probe(probe, G, 0) != hipSuccess) return LLAR_ERR_HIP;
+  if (hipMemcpy(hx, probe, sizeof(hx), hipMemcpyDeviceToHost) != hipSuccess) return LLAR_ERR_HIP;
+  bool ok = true;
+  uint32_t seen = 0;
+  for (int i = 0; i < 8; ++i) seen |= 1u << (hx[i] & 31u);
+  ok &= (seen == 0xFFu);
+  for (int i = 8; i < G; ++i) ok &= (hx[i] == hx[i % 8]);
+  c.local_ok = ok;
+  if (hipMemset(c.ll.ptr, 0, c.ll.bytes) != hipSuccess) return LLAR_ERR_HIP;
+  if (init_ctrl(&c) != hipSuccess) return LLAR_ERR_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) return LLAR_ERR_HIP;
+  d.ptr = base;
+  d.ready = true;
+  return LLAR_OK;
+}
+
+}  // namespace
+
+extern "C" int llar_allreduce_noalloc(int n_ranks, const void* const* partials, void* out, size_t n_elems,
+                                      llar_dtype dtype, void* stream) {
+  if (n_ranks < 1 || !partials || (int)dtype < 0 || (int)dtype > 2) return fail(LLAR_ERR_ARG);
+  if (n_ranks > kNoAllocMaxRanks) return fail(LLAR_ERR_UNSUPPORTED);
+  if (n_elems == 0) return LLAR_OK;
+  const size_t elem = (size_t)elem_bytes_of(dtype);
+  if (n_elems > kNoAllocMaxBytes / elem) return fail(LLAR_ERR_UNSUPPORTED);
+  if (!out || !aligned16(out)) return fail(LLAR_ERR_ARG);
+  for (int r = 0; r < n_ranks; ++r)
+    if (!partials[r] || !aligned16(partials[r])) return fail(LLAR_ERR_ARG);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(LLAR_ERR_HIP);
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return fail(LLAR_ERR_UNSUPPORTED);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  NoAllocDevice& d = g_noalloc[dev];
+  if (!d.ready) {
+    const int s = noalloc_setup(d, dev, st);
+    if (s != LLAR_OK) return fail(s);
+  }
+  llar_comm* h = &d.comm;
+  h->n_ranks = n_ranks;
+  h->kind = (int)dtype;
+  h->elem = elem;
+  Geometry g;
+  const int s = plan(h, n_elems, LLAR_LL, g);
+  if (s != LLAR_OK) return fail(s);
+  return issue(h, partials, n_ranks, out, n_elems, LLAR_LL, g, st);
+}
