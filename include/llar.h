@@ -352,6 +352,20 @@ int llar_launch_geometry(llar_comm* h, size_t n_elems, llar_protocol protocol,
  *   kind 2: empty-kernel launch interval, ns per launch (host timed)
  *   kind 3: device-coherent returning-atomic latency, ns
  *   kind 4: streaming copy bandwidth, GB/s of read+write (param = MiB)
+ *   kind 5: L2 round trip to lines another XCD has just written -- a
+ *           dependent chain of device-coherent loads over 4096 lines that
+ *           workgroup `param` (1..63, on XCD param % 8) wrote, read once
+ *           each from XCD 0, ns per hop (param % 8 == 0: the same XCD)
+ *   kind 6: empty-kernel launch interval under graph replay (a graph of
+ *           param launches, default 100), ns per launch
+ *   kind 7: no-return device-scope float atomic throughput with the LL128
+ *           lane pattern (each wave instruction adds into two whole 128-byte
+ *           lines), G lane operations per second; param bits 0-1: 0 =
+ *           binary32, 1 = packed bfloat16 pair, 2 = packed binary16 pair;
+ *           bit 2: issued from one XCD only (else all 8); bits 3-4: 1 =
+ *           every workgroup adds into one shared 8 KiB window, 2 = each
+ *           group of eight consecutive workgroups (one per XCD) shares one
+ *           window -- the eight ranks of an LL128 line --, 0 = private windows
  * Results go to *value.  Synchronous. */
 int llar_floor_measure(int kind, int param, double* value);
 

@@ -111,6 +111,34 @@ def allreduce(partials: np.ndarray, dtype: int) -> np.ndarray:
     return out
 
 
+def allreduce_threads(partials: np.ndarray, dtype: int, threads: int) -> np.ndarray:
+    """``allreduce`` with the elements split into ``threads`` contiguous
+    ranges, each reduced by the same C routine on its own host thread (the
+    call releases the interpreter lock).  Every element is an independent
+    sum, so the result is identical; only the wall time changes."""
+    import concurrent.futures as cf
+    parts = np.ascontiguousarray(as_bits(np.asarray(partials), dtype))
+    n_ranks, n = parts.shape
+    out = np.empty(n, dtype=BITS_DTYPE[dtype])
+    threads = max(1, min(int(threads), n))
+    bounds = [n * t // threads for t in range(threads + 1)]
+    lib = _load()
+    esz = parts.dtype.itemsize
+
+    def run(t):
+        lo, hi = bounds[t], bounds[t + 1]
+        if hi <= lo:
+            return 0
+        arr = (ctypes.c_void_p * n_ranks)(*[parts[r].ctypes.data + lo * esz for r in range(n_ranks)])
+        return lib.oracle_allreduce(arr, n_ranks, hi - lo, dtype, out.ctypes.data + lo * esz)
+
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        rcs = list(ex.map(run, range(threads)))
+    if any(rcs):
+        raise ValueError("oracle_allreduce rejected its arguments")
+    return out
+
+
 def reduce_scatter(partials: np.ndarray, dtype: int) -> list:
     """Rank j keeps segment j of the element-wise sum: the yololab.net article
     on network architecture for LLM inference, table of its All-Reduce /

@@ -273,3 +273,15 @@ def test_sum_f64_matches_plain_python_sum():
         for r in range(1, 4):
             acc += pyref.decode(int(parts[r, i]), BF16)
         assert (math.isnan(acc) and math.isnan(s[i])) or acc == s[i]
+
+
+def test_threaded_oracle_equals_the_single_call():
+    """Splitting the elements over host threads changes nothing: every
+    element is its own sum (ragged ranges, more threads than useful)."""
+    rng = np.random.default_rng(11)
+    for dt, n in ((oracle.F32, 1001), (oracle.F16, 4099), (oracle.BF16, 7)):
+        bits = rng.integers(0, 2 ** (8 * oracle.ELEM_BYTES[dt]), size=(5, n), dtype=np.uint64).astype(oracle.BITS_DTYPE[dt])
+        want = oracle.allreduce(bits, dt)
+        for t in (1, 3, 16):
+            got = oracle.allreduce_threads(bits, dt, t)
+            assert np.array_equal(oracle.same_result(got, want, dt), np.ones(n, bool))
