@@ -229,7 +229,8 @@ int llar_clear_device_status(llar_comm* h);
  *   "spin_timeout_us"  device poll limit in microseconds (default 200000)
  *   "ll128_acc"        LL128 staging type: 0 = binary32 (default), 1 = the I/O type (16-bit packed)
  *   "chunk_bytes"      largest per-rank chunk of the pipelined protocols (0 = tuned default:
- *                      1 MiB for both; clamped to [1 KiB, 4 MiB]); a
+ *                      1 MiB for the Sentinel pipeline and the alternating LL128 one, 256 KiB for
+ *                      the wave-split LL128 pipeline; clamped to [1 KiB, 4 MiB]); a
  *                      message is cut into the fewest equal chunks of at most this size (whole
  *                      16-byte vectors for the Sentinel), so that every owner gets an even share
  *                      of every chunk
@@ -237,9 +238,17 @@ int llar_clear_device_status(llar_comm* h);
  *                      upper bound: every owner slice of a full chunk keeps at least one line
  *                      (LL128) or vector (Sentinel), because the credit is earned by consuming
  *   "threads"          threads per workgroup: 64, 128, 256 or 512, or 1024 for the slot-handshake
- *                      and owner-credit Sentinel pipelines (0 = tuned default); the pipelined
- *                      Sentinel splits a workgroup into producer and consumer waves and needs at
- *                      least 128
+ *                      and owner-credit Sentinel pipelines and the wave-split LL128 pipeline (0 =
+ *                      tuned default: 1024 for the latter); the pipelined Sentinel splits a
+ *                      workgroup into producer and consumer waves and needs at least 128, and the
+ *                      LL128 pipeline alternates in one-wave workgroups
+ *   "ll128_kernel"     LL128 pipeline: 0 = wave split (default: producer waves and consumer waves
+ *                      each take whole chunks in turn, B buffers, a producer adds chunk c once its
+ *                      own workgroup's consumers finished chunk c - B/2); 1 = the alternating
+ *                      kernel (every wave produces then consumes each chunk, two buffers)
+ *   "ll128_buffers"    wave-split LL128 pipeline: staging buffers B, even, 2..64 (0 = 32); fewer
+ *                      when they do not fit the region, and a multiple of the consumer waves'
+ *                      count (the consumer of chunk c - B is the consumer of chunk c)
  *   "pipeline_buffers" staging buffers of the pipelined Sentinel: 2 to 64 (default 4), as many as
  *                      fit the staging allocated for the largest chunk (a call that needs more
  *                      returns LLAR_ERR_UNSUPPORTED).  Workgroup credit: an even count, and a
@@ -251,9 +260,10 @@ int llar_clear_device_status(llar_comm* h);
  *                      1 = slot handshake (a producer stores into a slot once it reads the owner's
  *                      reset there); 2 = owner credit (every owner's consumer waves publish a
  *                      progress word; a producer stores chunk c once every owner finished c - B)
- *   "consumer_waves"   slot handshake and owner credit: consumer waves per workgroup (0 = default:
- *                      a quarter of the waves for the handshake, (waves - 1) / 2 for the owner
- *                      credit, which keeps one wave to read the progress words; at most 8 there)
+ *   "consumer_waves"   slot handshake, owner credit and the wave-split LL128 pipeline: consumer
+ *                      waves per workgroup (0 = default: a quarter of the waves for the handshake
+ *                      and the LL128 pipeline, (waves - 1) / 2 for the owner credit, which keeps
+ *                      one wave to read the progress words; at most 8 there)
  *   "placement"        0 = auto, 1 = spread (rank r on XCD r mod 8), 2 = local (one slice's ranks share an XCD);
  *                      auto: local for the LL and Sentinel AllReduce and send/recv, spread for LL128, and
  *                      for ReduceScatter / AllGather local from 8 slices per rank up, spread below

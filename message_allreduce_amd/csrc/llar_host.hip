@@ -35,6 +35,11 @@ constexpr size_t kCapLL = 8ull << 20;
 constexpr size_t kCapSentinel = 16ull << 20;
 constexpr size_t kCapLL128 = 16ull << 20;
 constexpr size_t kCapChunk = 4ull << 20;  // largest chunk of the pipelined protocols
+// default chunk of the wave-split LL128 pipeline; measured on MI355X (1024
+// threads, 4 consumer waves, 32 buffers): 16 MiB x 8 fp32 237 us at 256 KiB
+// against 258 / 357 us at 128 / 64 KiB; 64 MiB x 8 bf16 1521 us against
+// 1680 / 1901 us
+constexpr size_t kLL128PipeChunk = 256ull << 10;
 constexpr int kTraceMaxWgs = 4096;
 constexpr int kPipeTraceMaxWgs = 1024;
 // The pipelined Sentinel's region holds 8 staging buffers of the largest
@@ -91,6 +96,8 @@ struct llar_comm {
   long long sentinel_credit = 0;  // pipelined Sentinel: 0 = workgroup credit, 1 = slot handshake, 2 = owner credit
   long long cons_waves = 0;       // slot handshake: consumer waves per workgroup (0 = a quarter)
   long long barrier_ablation = 0;  // 1: LL/Sentinel AllReduce behind a grid-wide barrier (measurement)
+  long long ll128_kernel = 0;      // pipelined LL128: 0 = producer/consumer waves, B buffers; 1 = alternating, 2 parities
+  long long ll128_buffers = 0;     // pipelined LL128, wave-split kernel: staging buffers (0 = 8, fewer if they do not fit)
   long long thr_sentinel = 64ll << 10;    // AUTO: LL up to (<=) this many bytes
   long long thr_ll128 = 1ll << 62;        // AUTO: one-shot Sentinel up to here (LL128 one round above)
   long long thr_pipelined = 512ll << 10;  // AUTO: pipelined Sentinel above this
@@ -170,10 +177,11 @@ uint32_t sentinel_shard_cap(size_t chunk_bytes, int n_ranks) {
 
 size_t effective_chunk(const llar_comm* h, int proto) {
   size_t c = (size_t)h->chunk_bytes;
-  // default 1 MiB for both pipelines; measured on MI355X for the LL128 one
-  // (N = 8, default geometry): 16 MiB fp32 562 -> 213 us, 64 MiB bf16
-  // 2985 -> 1620 us against 128 KiB chunks
-  if (c == 0) c = 1u << 20;
+  // default: 1 MiB for the Sentinel pipeline and the alternating LL128 one
+  // (measured on MI355X for the latter, N = 8: 16 MiB fp32 562 -> 213 us,
+  // 64 MiB bf16 2985 -> 1620 us against 128 KiB chunks); 256 KiB for the
+  // wave-split LL128 pipeline, whose 32 buffers keep many chunks in flight
+  if (c == 0) c = (proto == LLAR_LL128_PIPELINED && h->ll128_kernel == 0) ? kLL128PipeChunk : ((size_t)1 << 20);
   c = std::min(c, kCapChunk);
   c = std::min(c, ceil_div(h->max_bytes, 16) * 16);  // never beyond one whole message
   c = std::max(c, (size_t)1024);
@@ -248,6 +256,15 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
       g.slices = h->slices ? (int)h->slices : clampi((long long)per_owner, 1, piped ? 32 : 64);
       const size_t per_slice = ceil_div(per_owner, (size_t)g.slices);
       g.threads = h->threads ? (int)h->threads : ((piped || per_slice >= 32) ? 512 : 256);
+      // the pipeline splits a workgroup into producer and consumer waves
+      // (two waves at least; a one-wave workgroup alternates).  Measured on
+      // MI355X, 4 MiB x 8 fp32 in 64 KiB chunks: 249 us alternating; split
+      // 512 threads / 4 consumer waves / 8 buffers 185 us; 1024 / 8 / 16
+      // 110 us; 1024 / 4 / 32 74 us (1024 / 2 / 32 81, 1024 / 8 / 32 95)
+      if (piped && h->ll128_kernel == 0 && (h->threads == 0 || h->threads >= 128)) {
+        g.kernel = acc16 ? kKernLL128WsAcc16 : kKernLL128WsAcc32;
+        if (!h->threads) g.threads = 1024;
+      }
       if (g.chunks > 1) {
         // the implicit credit reaches a workgroup only through lines of its
         // own: every owner slice of a full chunk must hold at least one line
@@ -310,7 +327,8 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
   if (g.threads != 64 && g.threads != 128 && g.threads != 256 && g.threads != 512 && g.threads != 1024)
     return LLAR_ERR_ARG;
   if (g.threads == 1024 && g.kernel != kKernSentinelHs && g.kernel != kKernSentinelHsLocal &&
-      g.kernel != kKernSentinelOc && g.kernel != kKernSentinelOcLocal)
+      g.kernel != kKernSentinelOc && g.kernel != kKernSentinelOcLocal && g.kernel != kKernLL128WsAcc32 &&
+      g.kernel != kKernLL128WsAcc16)
     return LLAR_ERR_ARG;
   return LLAR_OK;
 }
@@ -408,10 +426,13 @@ llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes) {
   // whole lines, fit)
   size_t l_one = ceil_div(std::min(mb, kCapLL128) / h->elem, 31) + 1 + (size_t)N;
   h->ll128.parity_stride = l_one * 128;
-  // LL128 pipelined: [parity][line] for the largest chunk
+  // LL128 pipelined: [buffer][line]: two buffers of the largest chunk, or
+  // 32 of a chunk up to 256 KiB (the wave-split pipeline's default), which
+  // ever is larger
   const size_t chunk_cap = std::max(std::min(ceil_div(mb, 16) * 16, kCapChunk), (size_t)1024);
   size_t l_pipe = ceil_div(chunk_cap / h->elem, 31) + 1;
-  h->ll128_pipe.parity_stride = l_pipe * 128;
+  size_t l_pipe32 = ceil_div(std::min(chunk_cap, kLL128PipeChunk) / h->elem, 31) + 1;
+  h->ll128_pipe.parity_stride = std::max(l_pipe, 16 * l_pipe32) * 128;
   // Sentinel pipelined: [parity][owner][sender][shard vector] 16 B
   size_t cap = sentinel_shard_cap(chunk_cap, N);
   h->sent_pipe.parity_stride = (size_t)N * (size_t)N * cap * 16;
@@ -666,6 +687,33 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
       if (stride * a.n_buffers > reg->bytes) return fail(LLAR_ERR_UNSUPPORTED);
       a.parity_stride = (uint32_t)stride;
     }
+    const bool ll128_ws = g.kernel == kKernLL128WsAcc32 || g.kernel == kKernLL128WsAcc16;
+    if (ll128_ws) {
+      // producer and consumer waves; B buffers spaced by this chunk's lines.
+      // The workgroup credit needs an even B (run-ahead B/2 - 1 chunks) and
+      // the consumer of chunk c - B must be the consumer of chunk c
+      // (n_cons divides B).  B shrinks to what the region holds.
+      const uint32_t n_waves = (uint32_t)g.threads / 64u;
+      uint32_t n_cons = h->cons_waves > 0 ? (uint32_t)h->cons_waves : std::max(1u, n_waves / 4u);
+      if (n_waves < 2u || n_cons >= n_waves || n_cons > 16u) return fail(LLAR_ERR_ARG);
+      const size_t K = g.kernel == kKernLL128WsAcc16 ? 63 : 31;
+      const size_t stride = ceil_div((size_t)g.chunk_elems, K) * 128;
+      const uint32_t fit = (uint32_t)std::min<size_t>(reg->bytes / stride, 64);
+      uint32_t B = std::min<uint32_t>(h->ll128_buffers > 0 ? (uint32_t)h->ll128_buffers : 32u, fit);
+      B -= B % 2u;
+      if (B < 2u) return fail(LLAR_ERR_UNSUPPORTED);
+      if (h->cons_waves > 0) {
+        B -= B % std::lcm(2u, n_cons);
+        if (B < 2u) return fail(LLAR_ERR_UNSUPPORTED);
+      } else {
+        n_cons = std::gcd(n_cons, B);  // the default split adapts to the buffers that fit
+      }
+      // kept staging is never zeroed, so no buffer may be used twice
+      if (h->keep_staging && g.chunks > (int)B) return fail(LLAR_ERR_UNSUPPORTED);
+      a.n_buffers = B;
+      a.cons_waves = n_cons;
+      a.parity_stride = (uint32_t)stride;
+    }
     a.grid = (uint32_t)ls.grid;
     a.slices = (uint32_t)g.slices;
     a.placement = g.placement;
@@ -685,7 +733,7 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
     if (proto == LLAR_SENTINEL_PIPELINED) {
       uint32_t need = sentinel_shard_cap((size_t)g.chunk_elems * h->elem, h->n_ranks);
       if (need > a.shard_cap) return fail(LLAR_ERR_UNSUPPORTED);
-    } else {
+    } else if (!ll128_ws) {
       size_t K = (g.kernel == kKernLL128Acc16) ? 63 : 31;
       size_t lines = ceil_div((size_t)g.chunk_elems, K);  // the nominal chunk's lines
       if (lines * 128 > reg->parity_stride) return fail(LLAR_ERR_UNSUPPORTED);
@@ -952,6 +1000,8 @@ static long long* option_slot(llar_comm* h, const char* key) {
       {"sentinel_credit", &llar_comm::sentinel_credit},
       {"consumer_waves", &llar_comm::cons_waves},
       {"barrier_ablation", &llar_comm::barrier_ablation},
+      {"ll128_kernel", &llar_comm::ll128_kernel},
+      {"ll128_buffers", &llar_comm::ll128_buffers},
       {"auto_threshold_sentinel", &llar_comm::thr_sentinel},
       {"auto_threshold_ll128", &llar_comm::thr_ll128},
       {"auto_threshold_pipelined", &llar_comm::thr_pipelined},
@@ -999,6 +1049,9 @@ int llar_set_option(llar_comm* h, const char* key, long long value) {
   if (strcmp(key, "pipeline_buffers") == 0 && !(value >= 2 && value <= 64)) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "sentinel_credit") == 0 && (value < 0 || value > 2)) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "consumer_waves") == 0 && (value < 0 || value > 15)) return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "ll128_kernel") == 0 && (value < 0 || value > 1)) return fail(LLAR_ERR_ARG);
+  if (strcmp(key, "ll128_buffers") == 0 && !(value == 0 || (value >= 2 && value <= 64 && value % 2 == 0)))
+    return fail(LLAR_ERR_ARG);
   if (strcmp(key, "placement") == 0 && value == 2 && !h->local_ok) return fail(LLAR_ERR_UNSUPPORTED);
   if ((strcmp(key, "timing") == 0 || strcmp(key, "keep_staging") == 0 || strcmp(key, "trace") == 0 ||
        strcmp(key, "device_epoch") == 0 || strcmp(key, "barrier_ablation") == 0) &&

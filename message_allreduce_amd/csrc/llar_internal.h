@@ -56,7 +56,10 @@ enum KernelId : int {
   // pipelined Sentinel with the owner credit (llar_kernels.hip)
   kKernSentinelOc = 26,
   kKernSentinelOcLocal = 27,
-  kKernCount = 28
+  // pipelined LL128 with producer and consumer waves and B buffers
+  kKernLL128WsAcc32 = 28,
+  kKernLL128WsAcc16 = 29,
+  kKernCount = 30
 };
 constexpr int kKernFirstMulti = kKernRsLL;
 // kernels that live in llar_multi.hip

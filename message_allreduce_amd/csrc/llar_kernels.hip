@@ -454,6 +454,251 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// two-shot LL128 atomic, chunked, B buffers, producer and consumer waves
+// ---------------------------------------------------------------------------
+// The same lines, owners, slices and flag counting as k_twoshot_ll128, with
+// the work of a workgroup (r, w) split by role so that several chunks are in
+// flight at once instead of one chain of atomics, drain, flags, polls and
+// zeroing per chunk:
+//   producer waves: whole chunks dealt round-robin (wave p takes chunks p,
+//            p + n_prod, ...).  For its chunk c a wave adds rank r's elements
+//            into slice w of every owner's lines in buffer c % B, drains,
+//            then adds 1.0 to each of those lines' slot 0 -- once this
+//            workgroup's consumers have finished every chunk below c - lag;
+//   consumer waves: whole chunks dealt round-robin as well (wave q takes
+//            chunks q, q + n_cons, ...): poll owner r's slice w lines of chunk
+//            c until slot 0 reads N, round, write `out`, zero the lines;
+//            drain (the zeroing is performed), then count the chunk in LDS.
+// Credit (the page's implicit one, as for the pipelined Sentinel): a
+// producer adds chunk c after this workgroup's consumers finished chunk
+// c - 1 - lag; they finished it only after every rank's slice-w producer
+// flagged it, which each did only after its own consumers had finished chunk
+// c - 2 - 2 lag and their zeroing was performed.  With B >= 2 lag + 2
+// buffers that covers chunk c - B, the previous user of chunk c's buffer.
+// The consumer of chunk c - B is the consumer of chunk c (the host makes
+// n_cons divide B), so a wave never polls a buffer that still holds the
+// previous chunk's full lines: it zeroed them itself and drained before.
+// The host keeps every owner slice of a full chunk non-empty (the credit
+// travels through lines of this workgroup's own).
+template <int kKind, int kAcc16, int N>
+__global__ void __launch_bounds__(1024) k_twoshot_ll128_ws(TwoShotArgs a) {
+  int r_l, r_s;
+  uint32_t w_l, w_s;
+  decode_role_t<true, N>(blockIdx.x, r_l, w_l);
+  decode_role_t<false, N>(blockIdx.x, r_s, w_s);
+  const uint8_t* const src_l = a.part[r_l];
+  const uint8_t* const src_s = a.part[r_s];
+  LLAR_UNIFORM_AT_ENTRY("s"(src_l), "s"(src_s), "s"(a.out), "s"(a.stage), "s"(a.ctrl), "s"(a.n), "s"(a.spin_limit),
+                        "s"(a.chunk_elems), "s"(a.n_chunks), "s"(a.stage_bytes), "s"(a.parity_stride), "s"(a.grid),
+                        "s"(a.slices), "s"(a.placement), "s"(a.timing), "s"(a.keep), "s"(a.drop_rank),
+                        "s"(a.host_epoch), "s"(a.n_buffers), "s"(a.cons_waves));
+  const bool local = (a.placement == kPlaceLocal);
+  const int r = local ? r_l : r_s;
+  const uint32_t w = local ? w_l : w_s;
+  const bool idle = (w >= a.slices);
+  WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
+  using E = Elem<kKind>;
+  constexpr int kSlots = kAcc16 ? 64 : 32;
+  constexpr int K = kSlots - 1;
+  __shared__ uint32_t s_cnt[16];  // per consumer wave: chunks it has finished
+  __shared__ uint32_t s_dead;     // some wave's poll expired: everyone stops
+  if (threadIdx.x < 16) s_cnt[threadIdx.x] = 0u;
+  if (threadIdx.x == 0) s_dead = 0u;
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.stage, a.stage_bytes);
+  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
+  const uint32_t n_cons = a.cons_waves, n_prod = n_waves - n_cons;
+  const uint32_t n_buf = a.n_buffers, lag = n_buf / 2u - 1u;
+  const uint8_t* src = local ? src_l : src_s;
+  uint32_t flag_full;
+  if constexpr (!kAcc16) flag_full = __float_as_uint((float)N);
+  else flag_full = E::from_f32((float)N);
+  // lines of the nominal chunk, owners' ranges and this slice of each (as in
+  // k_twoshot_ll128: a line keeps its (owner, slice) in every chunk)
+  const uint32_t L = (a.chunk_elems + K - 1) / K;
+  uint32_t sl0[N], sl1[N];
+#pragma unroll
+  for (int s = 0; s < N; ++s) {
+    const uint32_t o0 = (uint32_t)s * L / (uint32_t)N, o1 = ((uint32_t)s + 1u) * L / (uint32_t)N;
+    sl0[s] = o0 + w * (o1 - o0) / a.slices;
+    sl1[s] = o0 + (w + 1u) * (o1 - o0) / a.slices;
+  }
+  auto any_dead = [&]() { return __hip_atomic_load(&s_dead, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u; };
+  auto die = [&]() {
+    raise_status(a.ctrl, kStatusTimeout);
+    __hip_atomic_store(&s_dead, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  // every chunk below the returned one has been finished by this
+  // workgroup's consumers (consumer wave q has finished chunks q, q + n_cons,
+  // ..., below q + s_cnt[q] * n_cons)
+  auto consumed_below = [&]() {
+    uint32_t f = ~0u;
+    for (uint32_t q = 0; q < n_cons; ++q)
+      f = min(f, q + __hip_atomic_load(&s_cnt[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) * n_cons);
+    return f;
+  };
+
+  if (idle) {
+    // padding workgroup of the local placement: nothing to do
+  } else if (wave < n_prod) {
+    // ---------------- producer waves
+    const bool silent = ((uint32_t)r == a.drop_rank);
+    for (uint32_t c = wave; c < a.n_chunks && !silent; c += n_prod) {
+      const uint64_t cbase = (uint64_t)c * a.chunk_elems;
+      const uint32_t len = (uint32_t)min((uint64_t)a.chunk_elems, a.n - cbase);
+      const uint32_t Lr = (len + K - 1) / K;
+      const uint32_t poff = (c % n_buf) * a.parity_stride;
+      if (c > lag) {
+        Spin spin(a.spin_limit);
+        bool ok = true;
+        while (consumed_below() + lag < c) {
+          if (any_dead()) {
+            ok = false;
+            break;
+          }
+          if (spin.expired()) {
+            die();
+            ok = false;
+            break;
+          }
+        }
+        if (!ok) break;
+      }
+      // This chunk's lines of slice w, every owner's in turn, numbered
+      // 0 .. total-1: owner s holds local lines [pre[s], pre[s+1]).  A wave
+      // instruction covers two consecutive local lines (64 dwords) whichever
+      // owners they belong to, so a slice of a few lines per owner costs a
+      // few instructions, not four per owner.
+      uint32_t pre[N + 1];
+      pre[0] = 0u;
+#pragma unroll
+      for (int s = 0; s < N; ++s) {
+        const uint32_t l1 = min(sl1[s], Lr);
+        pre[s + 1] = pre[s] + (l1 > sl0[s] ? l1 - sl0[s] : 0u);
+      }
+      const uint32_t total = pre[N];
+      // line of local line i (i < total): the last owner whose range starts
+      // at or before i holds it (empty owners never are the last such)
+      auto line_of = [&](uint32_t i) {
+        uint32_t line = 0u;
+#pragma unroll
+        for (int s = 0; s < N; ++s) line = (i >= pre[s]) ? sl0[s] + (i - pre[s]) : line;
+        return line;
+      };
+      // data: 8 local lines (four wave instructions) at a time, loads first
+      for (uint32_t i0 = 0; i0 < total; i0 += 8u) {
+        float fv[4];
+        s16x2 hv[4];
+        bool on[4];
+        uint32_t off[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t d = (uint32_t)k * 64u + lane;  // dword of the 8-line block
+          const uint32_t i = i0 + d / 32u, q = d % 32u;
+          const uint32_t line = line_of(i);
+          on[k] = i < total;
+          off[k] = poff + line * 128u + q * 4u;
+          if constexpr (!kAcc16) {
+            const uint32_t e_idx = line * K + q - 1u;
+            on[k] = on[k] && q != 0u && e_idx < len;
+            if constexpr (E::kBytes == 4) fv[k] = on[k] ? __uint_as_float(reinterpret_cast<const uint32_t*>(src)[cbase + e_idx]) : 0.f;
+            else fv[k] = on[k] ? E::to_f32(reinterpret_cast<const uint16_t*>(src)[cbase + e_idx]) : 0.f;
+          } else {
+            // two 16-bit slots per dword: slots 2q and 2q + 1
+            const uint32_t e0 = line * K + 2u * q - 1u, e1 = line * K + 2u * q;
+            const uint32_t lo = (on[k] && q != 0u && e0 < len) ? reinterpret_cast<const uint16_t*>(src)[cbase + e0] : 0u;
+            const uint32_t hi = (on[k] && e1 < len) ? reinterpret_cast<const uint16_t*>(src)[cbase + e1] : 0u;
+            on[k] = on[k] && (lo | hi) != 0u;  // nothing to add (both +0)
+            hv[k] = s16x2{(short)lo, (short)hi};
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (!on[k]) continue;
+          if constexpr (!kAcc16) llar_wire::ll128_add(reinterpret_cast<float*>(a.stage + off[k]), fv[k]);
+          else llar_wire::ll128_add2<kKind == kKindBF16>(a.stage + off[k], hv[k]);
+        }
+      }
+      // the wave's data acknowledged before any of its flags
+      drain_vm();
+      for (uint32_t i = lane; i < total; i += 64u) {
+        const uint32_t off = poff + line_of(i) * 128u;
+        if constexpr (!kAcc16) llar_wire::ll128_flag(reinterpret_cast<float*>(a.stage + off));
+        else llar_wire::ll128_flag2<kKind == kKindBF16>(a.stage + off, E::from_f32(1.0f));
+      }
+    }
+  } else {
+    // ---------------- consumer waves: owner r's slice w, 8 lanes per line
+    const uint32_t cw = wave - n_prod;
+    uint32_t l0 = sl0[0], l1 = sl1[0];
+#pragma unroll
+    for (int s = 1; s < N; ++s) {
+      l0 = (s == r) ? sl0[s] : l0;
+      l1 = (s == r) ? sl1[s] : l1;
+    }
+    const uint32_t grp = lane >> 3, j = lane & 7u;
+    uint32_t done = 0u;
+    bool dead = false;
+    for (uint32_t c = cw; c < a.n_chunks && !dead; c += n_cons) {
+      const uint64_t cbase = (uint64_t)c * a.chunk_elems;
+      const uint32_t len = (uint32_t)min((uint64_t)a.chunk_elems, a.n - cbase);
+      const uint32_t l1c = min(l1, (len + K - 1) / K);
+      const uint32_t poff = (c % n_buf) * a.parity_stride;
+      for (uint32_t lb = l0; lb < l1c && !dead; lb += 8u) {
+        const uint32_t line = lb + grp;
+        const bool mine = line < l1c;
+        const uint32_t loff = poff + line * 128u;
+        if (mine) {
+          Spin spin(a.spin_limit);
+          while (true) {
+            uint32_t f = ld4_coh(rs, loff);
+            if constexpr (kAcc16 != 0) f &= 0xFFFFu;
+            if (f == flag_full) break;
+            if (any_dead()) {
+              dead = true;
+              break;
+            }
+            if (spin.expired()) {
+              die();
+              dead = true;
+              break;
+            }
+          }
+        }
+        dead = __any((int)dead) != 0;
+        if (dead || !mine) continue;
+        u32x4 v = llar_wire::ll128_read16(rs, loff + j * 16u);
+        if constexpr (!kAcc16) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t q = j * 4u + (uint32_t)t;
+            const uint32_t e_idx = line * K + q - 1u;
+            if (q == 0u || e_idx >= len) continue;
+            if constexpr (E::kBytes == 4) reinterpret_cast<uint32_t*>(a.out)[cbase + e_idx] = v[t];
+            else reinterpret_cast<uint16_t*>(a.out)[cbase + e_idx] = (uint16_t)E::from_f32(__uint_as_float(v[t]));
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const uint32_t q = j * 8u + (uint32_t)t;
+            const uint32_t e_idx = line * K + q - 1u;
+            if (q == 0u || e_idx >= len) continue;
+            reinterpret_cast<uint16_t*>(a.out)[cbase + e_idx] = (uint16_t)(v[t >> 1] >> ((t & 1) * 16));
+          }
+        }
+        if (!a.keep) llar_wire::ll128_reset16(rs, loff + j * 16u);
+      }
+      if (dead) break;
+      // the zeroing is performed before the producers may count on it
+      drain_vm();
+      ++done;
+      if (lane == 0) __hip_atomic_store(&s_cnt[cw], done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  wg_end(a.ctrl, st, a.host_epoch, a.grid, a.timing, idle);
+}
+
+// ---------------------------------------------------------------------------
 // two-shot Sentinel, chunked and multi-buffered, producer/consumer waves
 // ---------------------------------------------------------------------------
 // Staging: [buffer][owner s][sender r][vector of s's shard] 16 B, all-ones
@@ -1269,6 +1514,16 @@ static hipError_t launch_n(const LaunchSpec& ls, hipStream_t stream) {
         return hipErrorInvalidValue;
       }
       break;
+    case kKernLL128WsAcc32:
+      hipLaunchKernelGGL((k_twoshot_ll128_ws<kKind, 0, N>), grid, block, 0, stream, ls.twoshot);
+      break;
+    case kKernLL128WsAcc16:
+      if constexpr (kKind != kKindF32) {
+        hipLaunchKernelGGL((k_twoshot_ll128_ws<kKind, 1, N>), grid, block, 0, stream, ls.twoshot);
+      } else {
+        return hipErrorInvalidValue;
+      }
+      break;
     case kKernSentinelPipe:
       hipLaunchKernelGGL((k_twoshot_sentinel<kKind, N, false>), grid, block, 0, stream, ls.twoshot);
       break;
@@ -1348,6 +1603,10 @@ static int occupancy_n(int kernel, int threads) {
     case kKernLL128Acc32: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_ll128<kKind, 0, N>, threads, 0); break;
     case kKernLL128Acc16:
       if constexpr (kKind != kKindF32) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_ll128<kKind, 1, N>, threads, 0);
+      break;
+    case kKernLL128WsAcc32: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_ll128_ws<kKind, 0, N>, threads, 0); break;
+    case kKernLL128WsAcc16:
+      if constexpr (kKind != kKindF32) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_ll128_ws<kKind, 1, N>, threads, 0);
       break;
     case kKernSentinelPipe: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_sentinel<kKind, N, false>, threads, 0); break;
     case kKernSentinelPipeLocal: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_twoshot_sentinel<kKind, N, true>, threads, 0); break;

@@ -719,7 +719,9 @@ def test_default_geometry_rules():
 def test_ll128_default_geometry():
     """LL128 defaults: one round keeps 256-thread workgroups while a slice
     holds fewer than 32 lines of each owner and takes 512 from there; the
-    pipeline takes 512 threads and at most 32 slices."""
+    pipeline splits 1024-thread workgroups into producer and consumer waves,
+    with at most 32 slices and 256 KiB chunks (the alternating pipeline,
+    option ll128_kernel = 1, keeps 512 threads and 1 MiB chunks)."""
     with comm_for(8, BF16, 2 << 20) as c:
         geo = c.geometry(8192, llar.LL128)  # 265 lines, 34 per owner, one per slice
         assert (geo["threads"], geo["slices"]) == (256, 34), geo
@@ -727,7 +729,65 @@ def test_ll128_default_geometry():
         assert (geo["threads"], geo["slices"]) == (512, 64), geo
     with comm_for(8, F32, 4 << 20, chunk_bytes=65536) as c:
         geo = c.geometry(1 << 20, llar.LL128_PIPELINED)  # 529 lines a chunk, 66-67 per owner
+        assert (geo["threads"], geo["slices"], geo["chunks"]) == (1024, 32, 64), geo
+        c.set_option("ll128_kernel", 1)
+        geo = c.geometry(1 << 20, llar.LL128_PIPELINED)
         assert (geo["threads"], geo["slices"], geo["chunks"]) == (512, 32, 64), geo
+    with comm_for(8, F32, 4 << 20) as c:
+        assert c.geometry(1 << 20, llar.LL128_PIPELINED)["chunks"] == 16   # 256 KiB chunks
+        c.set_option("ll128_kernel", 1)
+        assert c.geometry(1 << 20, llar.LL128_PIPELINED)["chunks"] == 4    # 1 MiB chunks
+
+
+@pytest.mark.parametrize("threads,cons,buffers", [(1024, 0, 0), (1024, 8, 16), (1024, 2, 2), (512, 0, 4), (512, 3, 6),
+                                                  (256, 1, 2), (128, 1, 64), (1024, 15, 30)])
+@pytest.mark.parametrize("acc", [0, 1])
+def test_ll128_wave_split_pipeline_configurations(threads, cons, buffers, acc):
+    """The wave-split LL128 pipeline over wave splits and buffer counts
+    (B = 2 lag + 2, the consumer of chunk c - B is the consumer of chunk c):
+    integer data is exact in every order (bfloat16 with binary32 staging;
+    binary16 with 16-bit staging, whose 11 bits hold every partial sum of
+    eight integers up to 64), normal data within tolerance; the alternating
+    pipeline on the same staging in between stays right."""
+    dt, name = (BF16, "bf16") if acc == 0 else (F16, "fp16")
+    n = 3 * 8192 + 333   # ragged: 13 chunks of 4 KiB, the last one short
+    with comm_for(8, dt, n * 2, chunk_bytes=4096, threads=threads, consumer_waves=cons, ll128_buffers=buffers,
+                  ll128_acc=acc) as c:
+        for rep in range(3):
+            bits = make_partials(2900 + acc, rep, 8, name, n, "integer", 1.0)
+            got = run(c, bits, "ll128_pipelined", dt)
+            assert_exact(got, oracle.allreduce(bits, dt), dt, "integer rep %d" % rep)
+            bits = make_partials(2910 + acc, rep, 8, name, n, "normal", 0.02)
+            got = run(c, bits, "ll128_pipelined", dt)
+            assert_tol(got, oracle.allreduce(bits, dt), dt, "normal rep %d" % rep)
+        c.set_option("ll128_kernel", 1)
+        c.set_option("threads", 512 if threads == 1024 else threads)
+        bits = make_partials(2920, acc, 8, name, n, "integer", 1.0)
+        assert_exact(run(c, bits, "ll128_pipelined", dt), oracle.allreduce(bits, dt), dt, "alternating kernel")
+        c.set_option("ll128_kernel", 0)
+        c.set_option("threads", threads)
+        assert_exact(run(c, bits, "ll128_pipelined", dt), oracle.allreduce(bits, dt), dt, "wave split again")
+
+
+def test_ll128_wave_split_refuses_what_cannot_work():
+    """Too many consumer waves for the workgroup, or kept staging that a
+    later chunk would have to reuse, are refused with nothing launched."""
+    dt = BF16
+    n = 8192
+    bits = make_partials(2930, 0, 4, "bf16", n, "normal", 1.0)
+    parts = [to_device(bits[r], dt) for r in range(4)]
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    with comm_for(4, dt, n * 2, chunk_bytes=1024, threads=256, consumer_waves=4) as c:
+        with pytest.raises(llar.LlarError):
+            c.allreduce(parts, out, "ll128_pipelined")   # 4 waves, 4 consumers, no producer
+        c.set_option("consumer_waves", 0)
+        c.set_option("keep_staging", 1)
+        c.set_option("ll128_buffers", 2)
+        with pytest.raises(llar.LlarError):
+            c.allreduce(parts, out, "ll128_pipelined")   # 16 chunks through 2 kept buffers
+        c.set_option("keep_staging", 0)
+        got = run(c, bits, "ll128_pipelined", dt)
+        assert_tol(got, oracle.allreduce(bits, dt), dt, "after the refusals")
 
 
 # --------------------------------------------------------------------------- the barrier ablation
