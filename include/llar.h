@@ -296,9 +296,30 @@ int llar_clear_device_status(llar_comm* h);
  *                      AUTO size boundaries in bytes per rank: LL up to 64 KiB, one-shot Sentinel
  *                      up to 512 KiB, pipelined Sentinel above; LL128 only above its own threshold
  *                      (default: never, its atomics are slower than the Sentinel exchange here)
+ *   "auto_protocol"    0 = AUTO follows the thresholds above; 1..5 = AllReduce calls that pass
+ *                      LLAR_AUTO run this protocol (send/recv, ReduceScatter and AllGather keep
+ *                      their own AUTO rule)
+ *   "log"              1 = print every call's operation, protocol and launch geometry (kernel,
+ *                      grid, threads, chunks, placement, epoch source) on stderr
  * llar_get_option also answers "local_placement_ok" (read-only): 1 when
  * workgroup ids equal mod 8 were seen to share an XCD, which the local
  * placement requires.
+ *
+ * h == NULL reads or sets the process-wide defaults that every communicator
+ * created afterwards starts from (the keys above, same ranges).  They start
+ * from the environment, read once (the pwwt.cn small-message latency
+ * article closes with NCCL's buffer-size variable as the model of such
+ * knobs):
+ *   LLAR_SPIN_TIMEOUT_US     "spin_timeout_us"
+ *   LLAR_PROTOCOL            "auto_protocol": auto, ll, sentinel, ll128, ll128_pipelined,
+ *                            sentinel_pipelined
+ *   LLAR_ACCUM               "ll128_acc": fp32 or 16
+ *   LLAR_TUNE                path of a file of "key value" (or key=value) lines, any key
+ *                            above, '#' comments -- e.g. AUTO thresholds tuned on a machine
+ *   LLAR_LOG                 "log"
+ *   LLAR_DEBUG_KEEP_STAGING  "keep_staging"
+ * A value that does not parse or is out of range is reported on stderr and
+ * ignored.
  * Returns LLAR_ERR_ARG for an unknown key or a bad value. */
 int llar_set_option(llar_comm* h, const char* key, long long value);
 int llar_get_option(llar_comm* h, const char* key, long long* value);

@@ -97,6 +97,8 @@ struct llar_comm {
   long long cons_waves = 0;       // slot handshake: consumer waves per workgroup (0 = a quarter)
   long long barrier_ablation = 0;  // 1: LL/Sentinel AllReduce behind a grid-wide barrier (measurement)
   long long ll128_kernel = 0;      // pipelined LL128: 0 = producer/consumer waves, B buffers; 1 = alternating, 2 parities
+  long long auto_proto = 0;        // 0: AUTO follows the threshold table; 1..5: AUTO AllReduce calls run this protocol
+  long long log = 0;               // 1: print every call's protocol and launch geometry to stderr
   long long ll128_buffers = 0;     // pipelined LL128, wave-split kernel: staging buffers (0 = 8, fewer if they do not fit)
   long long thr_sentinel = 64ll << 10;    // AUTO: LL up to (<=) this many bytes
   long long thr_ll128 = 1ll << 62;        // AUTO: one-shot Sentinel up to here (LL128 one round above)
@@ -334,6 +336,7 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
 }
 
 int auto_protocol(const llar_comm* h, size_t nbytes) {
+  if (h->auto_proto > 0) return (int)h->auto_proto;  // forced (option auto_protocol, LLAR_PROTOCOL)
   if ((long long)nbytes <= h->thr_sentinel && nbytes <= kCapLL) return LLAR_LL;
   if ((long long)nbytes > h->thr_pipelined) return LLAR_SENTINEL_PIPELINED;
   if ((long long)nbytes > h->thr_ll128 && nbytes <= kCapLL128) return LLAR_LL128;
@@ -353,6 +356,175 @@ const Region* region_of(const llar_comm* h, int proto) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---- options ------------------------------------------------------------
+struct OptionEntry {
+  const char* name;
+  long long llar_comm::*field;
+};
+const OptionEntry kOptions[] = {
+    {"spin_timeout_us", &llar_comm::spin_timeout_us},
+    {"ll128_acc", &llar_comm::ll128_acc},
+    {"chunk_bytes", &llar_comm::chunk_bytes},
+    {"slices", &llar_comm::slices},
+    {"threads", &llar_comm::threads},
+    {"placement", &llar_comm::placement},
+    {"timing", &llar_comm::timing},
+    {"keep_staging", &llar_comm::keep_staging},
+    {"debug_drop_rank", &llar_comm::debug_drop_rank},
+    {"trace", &llar_comm::trace_on},
+    {"device_epoch", &llar_comm::device_epoch},
+    {"pipeline_buffers", &llar_comm::pipe_buffers},
+    {"sentinel_credit", &llar_comm::sentinel_credit},
+    {"consumer_waves", &llar_comm::cons_waves},
+    {"barrier_ablation", &llar_comm::barrier_ablation},
+    {"ll128_kernel", &llar_comm::ll128_kernel},
+    {"ll128_buffers", &llar_comm::ll128_buffers},
+    {"auto_protocol", &llar_comm::auto_proto},
+    {"log", &llar_comm::log},
+    {"auto_threshold_sentinel", &llar_comm::thr_sentinel},
+    {"auto_threshold_ll128", &llar_comm::thr_ll128},
+    {"auto_threshold_pipelined", &llar_comm::thr_pipelined},
+};
+
+long long* option_slot(llar_comm* h, const char* key) {
+  for (const auto& t : kOptions)
+    if (strcmp(t.name, key) == 0) return &(h->*(t.field));
+  return nullptr;
+}
+
+// Range checks of an option value that need no device (n_ranks: the
+// communicator's rank count, or 0 for the process defaults).
+bool option_value_ok(const char* key, long long value, int n_ranks) {
+  auto is = [&](const char* k) { return strcmp(key, k) == 0; };
+  if (is("spin_timeout_us")) return value >= 1;
+  if (is("ll128_acc") || is("ll128_kernel")) return value == 0 || value == 1;
+  if (is("chunk_bytes")) return value >= 0 && (size_t)value <= kCapChunk;
+  if (is("slices")) return value >= 0 && value <= 1024;
+  if (is("threads")) return value == 0 || value == 64 || value == 128 || value == 256 || value == 512 || value == 1024;
+  if (is("placement")) return value >= 0 && value <= 2;
+  if (is("pipeline_buffers")) return value >= 2 && value <= 64;
+  if (is("sentinel_credit")) return value >= 0 && value <= 2;
+  if (is("consumer_waves")) return value >= 0 && value <= 15;
+  if (is("ll128_buffers")) return value == 0 || (value >= 2 && value <= 64 && value % 2 == 0);
+  if (is("auto_protocol")) return value >= 0 && value <= LLAR_SENTINEL_PIPELINED;
+  if (is("timing") || is("keep_staging") || is("trace") || is("device_epoch") || is("barrier_ablation") || is("log"))
+    return value == 0 || value == 1;
+  if (is("debug_drop_rank")) return value >= -1 && (n_ranks == 0 || value < n_ranks);
+  if (is("auto_threshold_sentinel") || is("auto_threshold_ll128") || is("auto_threshold_pipelined")) return value >= 0;
+  return true;
+}
+
+// Process-wide defaults that every communicator starts from: the option
+// table's values, then the environment, read once:
+//   LLAR_SPIN_TIMEOUT_US  device poll limit (us)
+//   LLAR_PROTOCOL         protocol of AllReduce calls that pass LLAR_AUTO:
+//                         auto, ll, sentinel, ll128, ll128_pipelined or
+//                         sentinel_pipelined
+//   LLAR_ACCUM            LL128 staging: fp32 (binary32) or 16 (packed 16-bit)
+//   LLAR_TUNE             path of a file of option settings, one "key value"
+//                         or "key=value" a line ('#' starts a comment) --
+//                         e.g. the AUTO thresholds measured on a machine
+//   LLAR_LOG              1: print each call's protocol and launch geometry
+//   LLAR_DEBUG_KEEP_STAGING  1: consumers leave staging as it is (tests)
+// A value that does not parse or is out of range is reported on stderr and
+// ignored.  llar_set_option / llar_get_option with a NULL handle change and
+// read these defaults.
+std::mutex g_defaults_mu;
+
+void env_warn(const char* var, const char* value, const char* why) {
+  fprintf(stderr, "llar: ignoring %s=%s (%s)\n", var, value, why);
+}
+
+bool parse_ll(const char* s, long long& v) {
+  if (!s || !*s) return false;
+  char* end = nullptr;
+  v = strtoll(s, &end, 0);
+  while (end && (*end == ' ' || *end == '\t' || *end == '\r' || *end == '\n')) ++end;
+  return end && *end == '\0';
+}
+
+void set_default(llar_comm& d, const char* var, const char* key, const char* text, long long value) {
+  long long* slot = option_slot(&d, key);
+  if (!slot) return env_warn(var, text, "unknown option");
+  if (!option_value_ok(key, value, 0)) return env_warn(var, text, "value out of range");
+  *slot = value;
+}
+
+void load_env_defaults(llar_comm& d) {
+  if (const char* e = getenv("LLAR_SPIN_TIMEOUT_US")) {
+    long long v = 0;
+    if (parse_ll(e, v)) set_default(d, "LLAR_SPIN_TIMEOUT_US", "spin_timeout_us", e, v);
+    else env_warn("LLAR_SPIN_TIMEOUT_US", e, "not a number");
+  }
+  if (const char* e = getenv("LLAR_PROTOCOL")) {
+    static const char* const names[] = {"auto", "ll", "sentinel", "ll128", "ll128_pipelined", "sentinel_pipelined"};
+    long long v = -1;
+    for (int i = 0; i < 6; ++i)
+      if (strcmp(e, names[i]) == 0) v = i;
+    if (v < 0 && !parse_ll(e, v)) v = -1;
+    if (v >= 0) set_default(d, "LLAR_PROTOCOL", "auto_protocol", e, v);
+    else env_warn("LLAR_PROTOCOL", e, "not a protocol name");
+  }
+  if (const char* e = getenv("LLAR_ACCUM")) {
+    if (strcmp(e, "fp32") == 0 || strcmp(e, "binary32") == 0 || strcmp(e, "32") == 0) d.ll128_acc = 0;
+    else if (strcmp(e, "16") == 0 || strcmp(e, "packed") == 0 || strcmp(e, "native") == 0) d.ll128_acc = 1;
+    else env_warn("LLAR_ACCUM", e, "expected fp32 or 16");
+  }
+  if (const char* e = getenv("LLAR_LOG")) {
+    long long v = 0;
+    if (parse_ll(e, v)) set_default(d, "LLAR_LOG", "log", e, v);
+    else env_warn("LLAR_LOG", e, "not a number");
+  }
+  if (const char* e = getenv("LLAR_DEBUG_KEEP_STAGING")) {
+    long long v = 0;
+    if (parse_ll(e, v)) set_default(d, "LLAR_DEBUG_KEEP_STAGING", "keep_staging", e, v);
+    else env_warn("LLAR_DEBUG_KEEP_STAGING", e, "not a number");
+  }
+  if (const char* e = getenv("LLAR_TUNE")) {
+    FILE* f = fopen(e, "r");
+    if (!f) return env_warn("LLAR_TUNE", e, "cannot open the file");
+    char line[512];
+    while (fgets(line, sizeof(line), f)) {
+      char* hash = strchr(line, '#');
+      if (hash) *hash = '\0';
+      for (char* c = line; *c; ++c)
+        if (*c == '=' || *c == '\t' || *c == '\r' || *c == '\n') *c = ' ';
+      char key[128], val[128];
+      if (sscanf(line, "%127s %127s", key, val) != 2) continue;
+      long long v = 0;
+      if (parse_ll(val, v)) set_default(d, "LLAR_TUNE", key, val, v);
+      else env_warn("LLAR_TUNE", val, "not a number");
+    }
+    fclose(f);
+  }
+}
+
+llar_comm& defaults_locked() {
+  static llar_comm d;
+  static bool loaded = false;
+  if (!loaded) {
+    load_env_defaults(d);
+    loaded = true;
+  }
+  return d;
+}
+
+void copy_options(llar_comm* dst, const llar_comm& src) {
+  for (const auto& t : kOptions) dst->*(t.field) = src.*(t.field);
+}
+
+void log_call(const llar_comm* h, const char* what, int proto, size_t n_elems, const LaunchSpec& ls, uint32_t placement,
+              int chunks, bool device_epoch) {
+  static const char* const names[] = {"auto", "ll", "sentinel", "ll128", "ll128_pipelined", "sentinel_pipelined"};
+  static const char* const dtypes[] = {"fp32", "fp16", "bf16"};
+  fprintf(stderr,
+          "llar: %s n_ranks=%d dtype=%s elems=%zu bytes=%zu protocol=%s kernel=%d grid=%d threads=%d chunks=%d "
+          "placement=%s epoch=%s\n",
+          what, h->n_ranks, dtypes[h->kind], n_elems, n_elems * h->elem, (proto >= 0 && proto <= 5) ? names[proto] : "?",
+          ls.kernel, ls.grid, ls.threads, chunks, placement == kPlaceLocal ? "local" : "spread",
+          device_epoch ? "device" : "host");
+}
 
 }  // namespace
 
@@ -489,8 +661,12 @@ llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes) {
     fail(st);
     return nullptr;
   }
-  const char* env = getenv("LLAR_SPIN_TIMEOUT_US");
-  if (env) h->spin_timeout_us = std::max(1ll, atoll(env));
+  {
+    std::lock_guard<std::mutex> lock(g_defaults_mu);
+    copy_options(h, defaults_locked());
+  }
+  if (h->placement == 2 && !h->local_ok) h->placement = 0;
+  if (h->debug_drop_rank >= h->n_ranks) h->debug_drop_rank = -1;
   g_last_error = LLAR_OK;
   return h;
 }
@@ -741,6 +917,10 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
   }
   if (!reg->ptr) return fail(LLAR_ERR_UNSUPPORTED);
   if (clear_after_host_wrap(h, device_epoch, stream) != hipSuccess) return fail(LLAR_ERR_HIP);
+  if (h->log) {
+    const bool p2p = g.kernel >= kKernP2PLL && g.kernel <= kKernP2PSentinelLocal;
+    log_call(h, p2p ? "send_recv" : "allreduce", proto, n_elems, ls, g.placement, g.chunks, device_epoch);
+  }
   hipError_t e = launch(ls, stream);
   if (e != hipSuccess) return fail(LLAR_ERR_HIP);
   finish_call(h, device_epoch);
@@ -822,6 +1002,7 @@ int run_multi(llar_comm* h, const void* const* ins, void* const* outs, int n_rec
     a.drop_rank = h->debug_drop_rank < 0 ? 0xFFFFFFFFu : (uint32_t)h->debug_drop_rank;
     a.host_epoch = host_epoch;
     if (clear_after_host_wrap(h, device_epoch, stream) != hipSuccess) return fail(LLAR_ERR_HIP);
+    if (h->log) log_call(h, "reduce_scatter", proto, count, ls, kPlaceSpread, 1, device_epoch);
     hipError_t e = launch(ls, stream);
     if (e != hipSuccess) return fail(LLAR_ERR_HIP);
     finish_call(h, device_epoch);
@@ -884,6 +1065,7 @@ int run_multi(llar_comm* h, const void* const* ins, void* const* outs, int n_rec
   a.drop_rank = h->debug_drop_rank < 0 ? 0xFFFFFFFFu : (uint32_t)h->debug_drop_rank;
   a.host_epoch = host_epoch;
   if (clear_after_host_wrap(h, device_epoch, stream) != hipSuccess) return fail(LLAR_ERR_HIP);
+  if (h->log) log_call(h, gather ? "all_gather" : "reduce_scatter", proto, count, ls, place, 1, device_epoch);
   hipError_t e = launch(ls, stream);
   if (e != hipSuccess) return fail(LLAR_ERR_HIP);
   finish_call(h, device_epoch);
@@ -980,37 +1162,6 @@ int llar_clear_device_status(llar_comm* h) {
   return LLAR_OK;
 }
 
-static long long* option_slot(llar_comm* h, const char* key) {
-  struct {
-    const char* name;
-    long long llar_comm::*field;
-  } static const table[] = {
-      {"spin_timeout_us", &llar_comm::spin_timeout_us},
-      {"ll128_acc", &llar_comm::ll128_acc},
-      {"chunk_bytes", &llar_comm::chunk_bytes},
-      {"slices", &llar_comm::slices},
-      {"threads", &llar_comm::threads},
-      {"placement", &llar_comm::placement},
-      {"timing", &llar_comm::timing},
-      {"keep_staging", &llar_comm::keep_staging},
-      {"debug_drop_rank", &llar_comm::debug_drop_rank},
-      {"trace", &llar_comm::trace_on},
-      {"device_epoch", &llar_comm::device_epoch},
-      {"pipeline_buffers", &llar_comm::pipe_buffers},
-      {"sentinel_credit", &llar_comm::sentinel_credit},
-      {"consumer_waves", &llar_comm::cons_waves},
-      {"barrier_ablation", &llar_comm::barrier_ablation},
-      {"ll128_kernel", &llar_comm::ll128_kernel},
-      {"ll128_buffers", &llar_comm::ll128_buffers},
-      {"auto_threshold_sentinel", &llar_comm::thr_sentinel},
-      {"auto_threshold_ll128", &llar_comm::thr_ll128},
-      {"auto_threshold_pipelined", &llar_comm::thr_pipelined},
-  };
-  for (const auto& t : table)
-    if (strcmp(t.name, key) == 0) return &(h->*(t.field));
-  return nullptr;
-}
-
 // Tests of the epoch wrap: place the next call's epoch anywhere in its
 // range.  "debug_host_epoch" numbers the next stream-ordered call (1 ..
 // 2^31 - 1); "debug_device_epoch" sets the device-resident epoch (2^31 + 1 ..
@@ -1033,42 +1184,40 @@ static int set_debug_epoch(llar_comm* h, bool device, long long value) {
 }
 
 int llar_set_option(llar_comm* h, const char* key, long long value) {
-  if (!h || !key) return fail(LLAR_ERR_ARG);
+  if (!key) return fail(LLAR_ERR_ARG);
+  if (!h) {
+    // the process-wide defaults of communicators created from now on
+    std::lock_guard<std::mutex> lock(g_defaults_mu);
+    llar_comm& d = defaults_locked();
+    long long* slot = option_slot(&d, key);
+    if (!slot || !option_value_ok(key, value, 0)) return fail(LLAR_ERR_ARG);
+    *slot = value;
+    return LLAR_OK;
+  }
   if (strcmp(key, "debug_host_epoch") == 0) return set_debug_epoch(h, false, value);
   if (strcmp(key, "debug_device_epoch") == 0) return set_debug_epoch(h, true, value);
   long long* slot = option_slot(h, key);
   if (!slot) return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "spin_timeout_us") == 0 && value < 1) return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "ll128_acc") == 0 && (value < 0 || value > 1)) return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "chunk_bytes") == 0 && (value < 0 || (size_t)value > kCapChunk)) return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "slices") == 0 && (value < 0 || value > 1024)) return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "threads") == 0 && !(value == 0 || value == 64 || value == 128 || value == 256 || value == 512 ||
-                                        value == 1024))
-    return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "placement") == 0 && (value < 0 || value > 2)) return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "pipeline_buffers") == 0 && !(value >= 2 && value <= 64)) return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "sentinel_credit") == 0 && (value < 0 || value > 2)) return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "consumer_waves") == 0 && (value < 0 || value > 15)) return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "ll128_kernel") == 0 && (value < 0 || value > 1)) return fail(LLAR_ERR_ARG);
-  if (strcmp(key, "ll128_buffers") == 0 && !(value == 0 || (value >= 2 && value <= 64 && value % 2 == 0)))
-    return fail(LLAR_ERR_ARG);
+  if (!option_value_ok(key, value, h->n_ranks)) return fail(LLAR_ERR_ARG);
   if (strcmp(key, "placement") == 0 && value == 2 && !h->local_ok) return fail(LLAR_ERR_UNSUPPORTED);
-  if ((strcmp(key, "timing") == 0 || strcmp(key, "keep_staging") == 0 || strcmp(key, "trace") == 0 ||
-       strcmp(key, "device_epoch") == 0 || strcmp(key, "barrier_ablation") == 0) &&
-      (value < 0 || value > 1))
-    return fail(LLAR_ERR_ARG);
   if (strcmp(key, "timing") == 0 && value == 1 && h->timing == 0) {
     // start from an empty timing ring (the epoch and status words are kept)
     if (hipDeviceSynchronize() != hipSuccess) return fail(LLAR_ERR_HIP);
     if (hipMemset(h->ctrl->timing_grid, 0, sizeof(uint32_t) * kTimingRing) != hipSuccess) return fail(LLAR_ERR_HIP);
   }
-  if (strcmp(key, "debug_drop_rank") == 0 && (value < -1 || value >= h->n_ranks)) return fail(LLAR_ERR_ARG);
   *slot = value;
   return LLAR_OK;
 }
 
 int llar_get_option(llar_comm* h, const char* key, long long* value) {
-  if (!h || !key || !value) return fail(LLAR_ERR_ARG);
+  if (!key || !value) return fail(LLAR_ERR_ARG);
+  if (!h) {
+    std::lock_guard<std::mutex> lock(g_defaults_mu);
+    long long* slot = option_slot(&defaults_locked(), key);
+    if (!slot) return fail(LLAR_ERR_ARG);
+    *value = *slot;
+    return LLAR_OK;
+  }
   if (strcmp(key, "local_placement_ok") == 0) {
     *value = h->local_ok ? 1 : 0;
     return LLAR_OK;
@@ -1256,6 +1405,13 @@ int noalloc_setup(NoAllocDevice& d, int dev, hipStream_t stream) {
   ok &= (seen == 0xFFu);
   for (int i = 8; i < G; ++i) ok &= (hx[i] == hx[i % 8]);
   c.local_ok = ok;
+  {
+    // of the process defaults only these apply here: the other options
+    // name regions and modes this entry point does not have
+    std::lock_guard<std::mutex> lock(g_defaults_mu);
+    c.spin_timeout_us = defaults_locked().spin_timeout_us;
+    c.log = defaults_locked().log;
+  }
   if (hipMemset(c.ll.ptr, 0, c.ll.bytes) != hipSuccess) return LLAR_ERR_HIP;
   if (init_ctrl(&c) != hipSuccess) return LLAR_ERR_HIP;
   if (hipDeviceSynchronize() != hipSuccess) return LLAR_ERR_HIP;

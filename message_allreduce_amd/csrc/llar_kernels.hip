@@ -543,6 +543,20 @@ __global__ void __launch_bounds__(1024) k_twoshot_ll128_ws(TwoShotArgs a) {
   } else if (wave < n_prod) {
     // ---------------- producer waves
     const bool silent = ((uint32_t)r == a.drop_rank);
+    // the slice bounds in this rank's owner order r, r + 1, ... (mod N),
+    // chosen with selects so that the arrays stay in registers
+    uint32_t rsl0[N], rsl1[N];
+#pragma unroll
+    for (int t = 0; t < N; ++t) {
+      rsl0[t] = sl0[0];
+      rsl1[t] = sl1[0];
+#pragma unroll
+      for (int s = 1; s < N; ++s) {
+        const bool pick = ((r + t) % N) == s;
+        rsl0[t] = pick ? sl0[s] : rsl0[t];
+        rsl1[t] = pick ? sl1[s] : rsl1[t];
+      }
+    }
     for (uint32_t c = wave; c < a.n_chunks && !silent; c += n_prod) {
       const uint64_t cbase = (uint64_t)c * a.chunk_elems;
       const uint32_t len = (uint32_t)min((uint64_t)a.chunk_elems, a.n - cbase);
@@ -564,17 +578,20 @@ __global__ void __launch_bounds__(1024) k_twoshot_ll128_ws(TwoShotArgs a) {
         }
         if (!ok) break;
       }
-      // This chunk's lines of slice w, every owner's in turn, numbered
-      // 0 .. total-1: owner s holds local lines [pre[s], pre[s+1]).  A wave
-      // instruction covers two consecutive local lines (64 dwords) whichever
-      // owners they belong to, so a slice of a few lines per owner costs a
-      // few instructions, not four per owner.
+      // This chunk's lines of slice w, every owner's in turn starting with
+      // owner r (so that the N ranks add into different owners' lines at
+      // the same moment instead of all into owner 0's, then owner 1's, ...),
+      // numbered 0 .. total-1: the t-th owner in that order holds local
+      // lines [pre[t], pre[t+1]).  A wave instruction covers two consecutive
+      // local lines (64 dwords) whichever owners they belong to, so a slice
+      // of a few lines per owner costs a few instructions, not four per
+      // owner.
       uint32_t pre[N + 1];
       pre[0] = 0u;
 #pragma unroll
-      for (int s = 0; s < N; ++s) {
-        const uint32_t l1 = min(sl1[s], Lr);
-        pre[s + 1] = pre[s] + (l1 > sl0[s] ? l1 - sl0[s] : 0u);
+      for (int t = 0; t < N; ++t) {
+        const uint32_t l1 = min(rsl1[t], Lr);
+        pre[t + 1] = pre[t] + (l1 > rsl0[t] ? l1 - rsl0[t] : 0u);
       }
       const uint32_t total = pre[N];
       // line of local line i (i < total): the last owner whose range starts
@@ -582,7 +599,7 @@ __global__ void __launch_bounds__(1024) k_twoshot_ll128_ws(TwoShotArgs a) {
       auto line_of = [&](uint32_t i) {
         uint32_t line = 0u;
 #pragma unroll
-        for (int s = 0; s < N; ++s) line = (i >= pre[s]) ? sl0[s] + (i - pre[s]) : line;
+        for (int t = 0; t < N; ++t) line = (i >= pre[t]) ? rsl0[t] + (i - pre[t]) : line;
         return line;
       };
       // data: 8 local lines (four wave instructions) at a time, loads first

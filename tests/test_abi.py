@@ -64,7 +64,7 @@ def test_null_handle_is_rejected_without_touching_the_gpu(L):
     assert L.llar_allreduce(None, None, None, 16, 0, 0, None) == -1
     assert L.llar_destroy(None) == 0
     assert L.llar_send_recv(None, None, None, 16, 0, 1, None) == -1
-    assert L.llar_set_option(None, b"timing", 1) == -1
+    assert L.llar_set_option(None, b"timing", 2) == -1  # NULL: the process defaults; 2 is out of range
     assert L.llar_get_device_status(None, None) == -1
     assert L.llar_staging_bytes(None, 1) == 0
     v = ctypes.c_double(0)
@@ -134,3 +134,79 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=60)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and not r.stdout
+
+
+_ENV_PROBE = r'''
+import ctypes, json, sys
+L = ctypes.CDLL(sys.argv[1])
+L.llar_get_option.argtypes = [ctypes.c_void_p, ctypes.c_char_p, ctypes.POINTER(ctypes.c_longlong)]
+L.llar_set_option.argtypes = [ctypes.c_void_p, ctypes.c_char_p, ctypes.c_longlong]
+out = {}
+for key in sys.argv[2:]:
+    v = ctypes.c_longlong(-99)
+    st = L.llar_get_option(None, key.encode(), ctypes.byref(v))
+    out[key] = v.value if st == 0 else ("error", st)
+print(json.dumps(out))
+'''
+
+
+def _read_defaults(env, keys):
+    import json
+    import sys
+    import message_allreduce_amd as m
+    full = dict(os.environ)
+    for k in list(full):
+        if k.startswith("LLAR_"):
+            del full[k]
+    full.update(env)
+    r = subprocess.run([sys.executable, "-c", _ENV_PROBE, m.library_path, *keys], capture_output=True, text=True,
+                       env=full, timeout=120)
+    assert r.returncode == 0, r.stderr
+    return json.loads(r.stdout), r.stderr
+
+
+def test_environment_knobs_set_the_process_defaults(L, tmp_path):
+    """Each knob lands in the option table that communicators start from,
+    readable through llar_get_option with a NULL handle (no device needed)."""
+    keys = ["spin_timeout_us", "auto_protocol", "ll128_acc", "log", "keep_staging", "auto_threshold_sentinel",
+            "chunk_bytes", "threads"]
+    base, _ = _read_defaults({}, keys)
+    assert base == {"spin_timeout_us": 200000, "auto_protocol": 0, "ll128_acc": 0, "log": 0, "keep_staging": 0,
+                    "auto_threshold_sentinel": 65536, "chunk_bytes": 0, "threads": 0}
+    tune = tmp_path / "tune.txt"
+    tune.write_text("# thresholds measured elsewhere\nauto_threshold_sentinel 4096\nchunk_bytes=131072\n\nthreads 256\n")
+    got, err = _read_defaults({"LLAR_SPIN_TIMEOUT_US": "1234", "LLAR_PROTOCOL": "sentinel_pipelined",
+                               "LLAR_ACCUM": "16", "LLAR_LOG": "1", "LLAR_DEBUG_KEEP_STAGING": "1",
+                               "LLAR_TUNE": str(tune)}, keys)
+    assert got == {"spin_timeout_us": 1234, "auto_protocol": 5, "ll128_acc": 1, "log": 1, "keep_staging": 1,
+                   "auto_threshold_sentinel": 4096, "chunk_bytes": 131072, "threads": 256}, (got, err)
+    assert err == ""
+    for env, name in (({"LLAR_PROTOCOL": "ll"}, 1), ({"LLAR_PROTOCOL": "3"}, 3), ({"LLAR_ACCUM": "fp32"}, 0)):
+        got, _ = _read_defaults(env, ["auto_protocol", "ll128_acc"])
+        assert name in got.values()
+
+
+def test_environment_knobs_with_bad_values_are_reported_and_ignored(L, tmp_path):
+    tune = tmp_path / "tune.txt"
+    tune.write_text("threads 300\nno_such_key 1\nchunk_bytes abc\nslices 16\n")
+    got, err = _read_defaults({"LLAR_SPIN_TIMEOUT_US": "0", "LLAR_PROTOCOL": "fastest", "LLAR_ACCUM": "8",
+                               "LLAR_LOG": "yes", "LLAR_TUNE": str(tune)},
+                              ["spin_timeout_us", "auto_protocol", "ll128_acc", "log", "threads", "chunk_bytes",
+                               "slices"])
+    assert got == {"spin_timeout_us": 200000, "auto_protocol": 0, "ll128_acc": 0, "log": 0, "threads": 0,
+                   "chunk_bytes": 0, "slices": 16}
+    for word in ("LLAR_SPIN_TIMEOUT_US=0", "LLAR_PROTOCOL=fastest", "LLAR_ACCUM=8", "LLAR_LOG=yes",
+                 "LLAR_TUNE=300", "LLAR_TUNE=abc"):
+        assert "ignoring " + word in err, (word, err)
+    got, err = _read_defaults({"LLAR_TUNE": str(tmp_path / "missing.txt")}, ["threads"])
+    assert got == {"threads": 0} and "cannot open" in err
+
+
+def test_null_handle_options_are_the_process_defaults(L):
+    v = ctypes.c_longlong(0)
+    assert L.llar_set_option(None, b"threads", 300) == -1
+    assert L.llar_set_option(None, b"no_such_key", 1) == -1
+    assert L.llar_get_option(None, b"local_placement_ok", ctypes.byref(v)) == -1
+    assert L.llar_set_option(None, b"auto_threshold_pipelined", 1 << 20) == 0
+    assert L.llar_get_option(None, b"auto_threshold_pipelined", ctypes.byref(v)) == 0 and v.value == 1 << 20
+    assert L.llar_set_option(None, b"auto_threshold_pipelined", 512 << 10) == 0

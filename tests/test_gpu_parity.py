@@ -842,3 +842,32 @@ def test_barrier_ablation_every_rank_count_and_graph_replays(n_ranks):
             assert_exact(to_host(out, dt), oracle.allreduce(bits, dt), dt, "N=%d replay %d" % (n_ranks, rep))
     finally:
         c.close()
+
+
+# --------------------------------------------------------------------------- process defaults and logging
+def test_process_defaults_reach_new_communicators_and_log_prints_geometry(capfd):
+    """Defaults set with a NULL handle (as the LLAR_* environment knobs do)
+    are what a new communicator starts from: a forced AUTO protocol runs and
+    stays exact, and "log" prints each call's protocol and geometry."""
+    dt = BF16
+    n = 4096
+    bits = make_partials(3000, 0, 8, "bf16", n, "normal", 1.0)
+    assert llar.llar_set_option(None, "auto_protocol", llar.SENTINEL_PIPELINED) == 0
+    assert llar.llar_set_option(None, "log", 1) == 0
+    try:
+        with comm_for(8, dt, n * 2) as c:
+            assert c.get_option("auto_protocol") == llar.SENTINEL_PIPELINED and c.get_option("log") == 1
+            assert c.select_protocol(n * 2) == llar.SENTINEL_PIPELINED
+            capfd.readouterr()
+            got = run(c, bits, "auto", dt)
+            assert_exact(got, oracle.allreduce(bits, dt), dt, "forced sentinel_pipelined")
+            err = capfd.readouterr().err
+            assert "llar: allreduce n_ranks=8 dtype=bf16 elems=4096" in err and "protocol=sentinel_pipelined" in err, err
+            c.set_option("log", 0)
+            run(c, bits, "ll", dt)
+            assert "llar:" not in capfd.readouterr().err
+    finally:
+        assert llar.llar_set_option(None, "auto_protocol", 0) == 0
+        assert llar.llar_set_option(None, "log", 0) == 0
+    with comm_for(8, dt, n * 2) as c:
+        assert c.get_option("auto_protocol") == 0 and c.select_protocol(n * 2) == llar.LL
