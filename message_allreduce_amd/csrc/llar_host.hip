@@ -75,7 +75,7 @@ struct llar_comm {
   uint64_t* trace = nullptr;  // kTraceMaxWgs x kTraceWords stamps of the last traced one-shot call
   int trace_grid = 0;
   uint64_t* pipe_trace = nullptr;  // kPipeTraceMaxWgs x kPipeTraceWords stamps of the last traced pipeline call
-  uint64_t* credit = nullptr;      // kCreditWords progress words of the pipelined Sentinel's owner credit
+  uint32_t* credit = nullptr;      // kCreditEntries {count, epoch} progress entries of the pipelined Sentinel's owner credit
   int pipe_trace_grid = 0;
   uint32_t host_epoch = 1;         // epoch of the next host-numbered call
   bool host_wrap_pending = false;  // the host epoch wrapped: clear the epoch-tagged state before the next call
@@ -133,7 +133,7 @@ hipError_t init_ctrl(llar_comm* h) {
   c.ll_base = h->ll.ptr;
   c.ll_bytes = h->ll.ptr ? h->ll.bytes : 0u;
   c.credit_base = reinterpret_cast<uint8_t*>(h->credit);
-  c.credit_bytes = h->credit ? kCreditWords * sizeof(uint64_t) : 0u;
+  c.credit_bytes = h->credit ? kCreditBytes : 0u;
   return hipMemcpy(h->ctrl, &c, sizeof(c), hipMemcpyHostToDevice);
 }
 
@@ -146,7 +146,7 @@ hipError_t reset_staging(llar_comm* h) {
   if (h->sent_pipe.ptr && (e = hipMemset(h->sent_pipe.ptr, 0xFF, h->sent_pipe.bytes)) != hipSuccess) return e;
   // progress words carry the epoch of the call that wrote them, and the
   // device-resident epoch restarts with the control block
-  if (h->credit && (e = hipMemset(h->credit, 0, kCreditWords * sizeof(uint64_t))) != hipSuccess) return e;
+  if (h->credit && (e = hipMemset(h->credit, 0, kCreditBytes)) != hipSuccess) return e;
   return hipDeviceSynchronize();
 }
 
@@ -615,8 +615,8 @@ llar_comm* llar_create(int n_ranks, llar_dtype dtype, size_t max_bytes) {
   if (e == hipSuccess) e = hipMemset(h->trace, 0, (size_t)kTraceMaxWgs * kTraceWords * sizeof(uint64_t));
   if (e == hipSuccess) e = hipMalloc(&h->pipe_trace, (size_t)kPipeTraceMaxWgs * kPipeTraceWords * sizeof(uint64_t));
   if (e == hipSuccess) e = hipMemset(h->pipe_trace, 0, (size_t)kPipeTraceMaxWgs * kPipeTraceWords * sizeof(uint64_t));
-  if (e == hipSuccess) e = hipMalloc(&h->credit, kCreditWords * sizeof(uint64_t));
-  if (e == hipSuccess) e = hipMemset(h->credit, 0, kCreditWords * sizeof(uint64_t));
+  if (e == hipSuccess) e = hipMalloc(&h->credit, kCreditBytes);
+  if (e == hipSuccess) e = hipMemset(h->credit, 0, kCreditBytes);
   if (e == hipSuccess) e = alloc_region(h->ll, 2 * h->ll.parity_stride, 0);
   if (e == hipSuccess) e = alloc_region(h->sent, 2 * h->sent.parity_stride, 0xFF);
   if (e == hipSuccess) e = alloc_region(h->ll128, 2 * h->ll128.parity_stride, 0);
@@ -728,7 +728,7 @@ hipError_t clear_after_host_wrap(llar_comm* h, bool device_epoch, hipStream_t st
   if (device_epoch || !h->host_wrap_pending) return hipSuccess;
   hipError_t e = hipSuccess;
   if (h->ll.ptr) e = hipMemsetAsync(h->ll.ptr, 0, h->ll.bytes, stream);
-  if (e == hipSuccess && h->credit) e = hipMemsetAsync(h->credit, 0, kCreditWords * sizeof(uint64_t), stream);
+  if (e == hipSuccess && h->credit) e = hipMemsetAsync(h->credit, 0, kCreditBytes, stream);
   if (e == hipSuccess) h->host_wrap_pending = false;
   return e;
 }

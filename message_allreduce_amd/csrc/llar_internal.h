@@ -109,7 +109,7 @@ struct TwoShotArgs {
   uint32_t drop_rank;
   uint32_t host_epoch;
   uint64_t* trace;       // per-workgroup, per-chunk stamps (kPipeTraceWords each), or null
-  uint64_t* credit;      // Sentinel pipeline, owner credit: [rank][slice][consumer wave] progress, or null
+  uint32_t* credit;      // Sentinel pipeline, owner credit: [rank][slice][consumer wave] {count, epoch}, or null
 };
 
 // ReduceScatter / AllGather over the LL or Sentinel wire.  A block is what
@@ -143,10 +143,12 @@ struct MultiArgs {
 // ready, consumer done) of the first kPipeTraceChunks chunks
 constexpr int kPipeTraceChunks = 128;
 constexpr int kPipeTraceWords = 4 * kPipeTraceChunks;
-// owner credit of the pipelined Sentinel: one progress word per (rank, slice,
-// consumer wave)
+// owner credit of the pipelined Sentinel: one progress entry per (rank,
+// slice, consumer wave), two 32-bit words: chunks finished, and the epoch of
+// the call that wrote them
 constexpr int kCreditSlices = 64, kCreditWaves = 8;
-constexpr size_t kCreditWords = (size_t)8 * kCreditSlices * kCreditWaves;
+constexpr size_t kCreditEntries = (size_t)8 * kCreditSlices * kCreditWaves;
+constexpr size_t kCreditBytes = kCreditEntries * 2 * sizeof(uint32_t);
 
 // phase trace of the one-shot kernel: per workgroup, thread 0 records
 constexpr int kTraceWords = 8;  // start, epoch, input, ready, out-acked, end, id, spare

@@ -1228,14 +1228,15 @@ __global__ void __launch_bounds__(1024) k_twoshot_sentinel_hs(TwoShotArgs a) {
 //            rank r's vectors of slice w of every owner's shard (one per
 //            owner per lane), and stores them into [c % B][s][r] once the
 //            chunk is free (below); two pairs in flight per wave;
-//   credit wave: reads the progress word of every (owner s, consumer wave)
+//   credit wave: reads the progress words of every (owner s, consumer wave)
 //            of slice w and publishes in LDS the first chunk that some owner
 //            has not consumed yet; chunk c is free once that is > c - B;
 //   consumer waves: whole chunks dealt round-robin; for each vector of
 //            owner r's slice w, poll the N slots, add them in binary64 in
 //            rank order, round, write `out` and reset the slots; after the
 //            chunk, drain (the resets are performed) and advance the wave's
-//            progress word (tagged with the call's epoch).
+//            progress count (a 32-bit word beside a 32-bit word holding the
+//            call's epoch, written once the first count is performed).
 // Chunk c reuses the buffer of chunk c - B only after every owner has
 // consumed chunk c - B and its resets were performed, so B buffers give a
 // run-ahead of B - 1 chunks (a credit read from the owners themselves, not
@@ -1384,15 +1385,21 @@ __global__ void __launch_bounds__(1024) k_twoshot_sentinel_oc(TwoShotArgs a) {
     // q + count * n_cons that it owns is consumed
     const uint32_t target = n_chunks > n_buf ? n_chunks - n_buf : 0u;  // producers never need more
     const uint32_t q = lane % n_cons;
-    uint64_t* const cp =
-        lane < (uint32_t)N * n_cons ? a.credit + ((size_t)(lane / n_cons) * kCreditSlices + w) * kCreditWaves + q : nullptr;
+    // progress entry: [count, epoch] 32-bit words (see the consumer waves)
+    uint32_t* const cp =
+        lane < (uint32_t)N * n_cons ? a.credit + 2 * (((size_t)(lane / n_cons) * kCreditSlices + w) * kCreditWaves + q)
+                                    : nullptr;
     uint32_t have = 0u;
     SpinBulk spin(a.spin_limit);
     while (!dead && have < target) {
       uint32_t f = ~0u;
       if (cp != nullptr) {
-        const uint64_t v = __hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t cnt = ((uint32_t)(v >> 32) == st.epoch) ? (uint32_t)v : 0u;
+        // the count only once its epoch word carries this call's epoch: the
+        // writer stored the count first, then the epoch, so a count read
+        // after that epoch is this call's (not a stale word of another call)
+        uint32_t cnt = 0u;
+        if (__hip_atomic_load(cp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == st.epoch)
+          cnt = __hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         f = q + cnt * n_cons;
       }
 #pragma unroll
@@ -1411,7 +1418,7 @@ __global__ void __launch_bounds__(1024) k_twoshot_sentinel_oc(TwoShotArgs a) {
     const uint32_t cw = wave - n_prod - 1u;
     uint32_t o0, s0, s1n;
     slice_of((uint32_t)r, o0, s0, s1n);
-    uint64_t* const my_word = a.credit + ((size_t)r * kCreditSlices + w) * kCreditWaves + cw;
+    uint32_t* const my_word = a.credit + 2 * (((size_t)r * kCreditSlices + w) * kCreditWaves + cw);
     uint32_t done = 0u;
     for (uint32_t c = cw; c < n_chunks && !dead; c += n_cons) {
       // chunk c - B, the previous user of these slots, may belong to another
@@ -1492,8 +1499,14 @@ __global__ void __launch_bounds__(1024) k_twoshot_sentinel_oc(TwoShotArgs a) {
       drain_vm();
       ++done;
       if (lane == 0) {
-        __hip_atomic_store(my_word, ((uint64_t)st.epoch << 32) | (uint64_t)done, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        // 32-bit words like every other polled word: the count, and on the
+        // first chunk of the call (after the count is performed) the epoch
+        // that makes it this call's
+        __hip_atomic_store(my_word, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == 1u) {
+          drain_vm();
+          __hip_atomic_store(my_word + 1, st.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         __hip_atomic_store(&s_cons[cw], done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
       stamp(3, c);
