@@ -299,6 +299,11 @@ int llar_clear_device_status(llar_comm* h);
  *   "auto_protocol"    0 = AUTO follows the thresholds above; 1..5 = AllReduce calls that pass
  *                      LLAR_AUTO run this protocol (send/recv, ReduceScatter and AllGather keep
  *                      their own AUTO rule)
+ *   "local_xcds"       one-shot LL / Sentinel (and send/recv) under the local placement: keep the
+ *                      slices on XCDs 0 .. k-1 (slice w on XCD w mod k, the workgroups that land on
+ *                      the other XCDs idle); 0 = all eight.  XCDs start a launch at different times
+ *                      (measured: XCDs 0-2 within 0.16 us, XCD 3 about 0.3 us later, XCDs 4-7 about
+ *                      1 us later), so a small exchange can avoid the late ones
  *   "log"              1 = print every call's operation, protocol and launch geometry (kernel,
  *                      grid, threads, chunks, placement, epoch source) on stderr
  * llar_get_option also answers "local_placement_ok" (read-only): 1 when

@@ -99,6 +99,7 @@ struct llar_comm {
   long long ll128_kernel = 0;      // pipelined LL128: 0 = producer/consumer waves, B buffers; 1 = alternating, 2 parities
   long long auto_proto = 0;        // 0: AUTO follows the threshold table; 1..5: AUTO AllReduce calls run this protocol
   long long log = 0;               // 1: print every call's protocol and launch geometry to stderr
+  long long local_xcds = 0;        // one-shot LL/Sentinel, local placement: slices use XCDs 0 .. n-1 (0 = 8)
   long long ll128_buffers = 0;     // pipelined LL128, wave-split kernel: staging buffers (0 = 8, fewer if they do not fit)
   long long thr_sentinel = 64ll << 10;    // AUTO: LL up to (<=) this many bytes
   long long thr_ll128 = 1ll << 62;        // AUTO: one-shot Sentinel up to here (LL128 one round above)
@@ -199,6 +200,7 @@ struct Geometry {
   int chunks = 1;
   uint32_t chunk_elems = 0;
   uint32_t placement = kPlaceSpread;
+  int xcd_span = 8;  // local one-shot: XCDs its slices use
 };
 
 int clampi(long long v, int lo, int hi) { return (int)std::max<long long>(lo, std::min<long long>(hi, v)); }
@@ -318,7 +320,10 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
   if (place == kPlaceLocal && !h->local_ok) place = kPlaceSpread;
   g.grid_slices = g.slices;
   if (place == kPlaceLocal) {
-    g.grid_slices = (int)ceil_div((size_t)g.slices, 8) * 8;
+    // one-shot LL / Sentinel may keep their slices on the first few XCDs
+    const bool oneshot = proto == LLAR_LL || proto == LLAR_SENTINEL;
+    g.xcd_span = (oneshot && h->local_xcds > 0) ? (int)h->local_xcds : 8;
+    g.grid_slices = (int)ceil_div((size_t)g.slices, (size_t)g.xcd_span) * 8;
     if (g.kernel == kKernSentinelPipe) g.kernel = kKernSentinelPipeLocal;
     if (g.kernel == kKernSentinelHs) g.kernel = kKernSentinelHsLocal;
     if (g.kernel == kKernSentinelOc) g.kernel = kKernSentinelOcLocal;
@@ -382,6 +387,7 @@ const OptionEntry kOptions[] = {
     {"ll128_buffers", &llar_comm::ll128_buffers},
     {"auto_protocol", &llar_comm::auto_proto},
     {"log", &llar_comm::log},
+    {"local_xcds", &llar_comm::local_xcds},
     {"auto_threshold_sentinel", &llar_comm::thr_sentinel},
     {"auto_threshold_ll128", &llar_comm::thr_ll128},
     {"auto_threshold_pipelined", &llar_comm::thr_pipelined},
@@ -408,6 +414,7 @@ bool option_value_ok(const char* key, long long value, int n_ranks) {
   if (is("consumer_waves")) return value >= 0 && value <= 15;
   if (is("ll128_buffers")) return value == 0 || (value >= 2 && value <= 64 && value % 2 == 0);
   if (is("auto_protocol")) return value >= 0 && value <= LLAR_SENTINEL_PIPELINED;
+  if (is("local_xcds")) return value >= 0 && value <= 8;
   if (is("timing") || is("keep_staging") || is("trace") || is("device_epoch") || is("barrier_ablation") || is("log"))
     return value == 0 || value == 1;
   if (is("debug_drop_rank")) return value >= -1 && (n_ranks == 0 || value < n_ranks);
@@ -792,6 +799,7 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
     a.trace = (h->trace_on && ls.grid <= kTraceMaxWgs) ? h->trace : nullptr;
     if (a.trace) h->trace_grid = ls.grid;
     a.host_epoch = host_epoch;
+    a.xcd_span = (uint32_t)g.xcd_span;
   } else {
     TwoShotArgs& a = ls.twoshot;
     for (int r = 0; r < n_launch; ++r) a.part[r] = static_cast<const uint8_t*>(parts[r]);
@@ -1094,6 +1102,10 @@ int llar_allreduce(llar_comm* h, const void* const* partials, void* out, size_t 
     // the same one-shot geometry, synchronised by a grid-wide barrier
     if (nbytes > kCapLL) return fail(LLAR_ERR_UNSUPPORTED);
     g.kernel = g.placement == kPlaceLocal ? kKernBarrierLocal : kKernBarrier;
+    if (g.placement == kPlaceLocal && g.xcd_span != 8) {
+      g.xcd_span = 8;
+      g.grid_slices = (int)ceil_div((size_t)g.slices, 8) * 8;
+    }
   }
   return issue(h, partials, h->n_ranks, out, n_elems, proto, g, static_cast<hipStream_t>(stream));
 }
@@ -1117,7 +1129,7 @@ int llar_send_recv(llar_comm* h, const void* send_buf, void* recv_buf, size_t n_
   if (!h->threads) g.threads = 512;
   if (!h->slices) {
     g.slices = clampi((long long)ceil_div(2 * ceil_div(nbytes, 16), (size_t)1024), 2, 64);
-    g.grid_slices = g.placement == kPlaceLocal ? (int)ceil_div((size_t)g.slices, 8) * 8 : g.slices;
+    g.grid_slices = g.placement == kPlaceLocal ? (int)ceil_div((size_t)g.slices, (size_t)g.xcd_span) * 8 : g.slices;
   }
   // the one-shot exchange with a single producer, in copy mode
   switch (g.kernel) {

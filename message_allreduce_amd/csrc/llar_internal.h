@@ -85,6 +85,7 @@ struct OneShotArgs {
   uint32_t drop_rank;    // tests: this rank's producers write nothing (0xFFFFFFFF = none)
   uint32_t host_epoch;   // this call's epoch, or 0: read the device-resident epoch
   uint64_t* trace;       // per-workgroup phase stamps (kTraceWords each), or null
+  uint32_t xcd_span;     // local placement: slices use XCDs 0 .. xcd_span-1 (8 = all)
 };
 
 struct TwoShotArgs {

@@ -169,7 +169,19 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
   const uint64_t t_entry = wall_ticks();
   int r;
   uint32_t w;
-  decode_role_t<kLocal, N>(blockIdx.x, r, w);
+  // local placement over the first xcd_span XCDs: workgroup b runs on XCD
+  // b mod 8; slice w lives on XCD w mod span with its N ranks, and the
+  // workgroups on the other XCDs idle (span 8: decode_role_t's placement)
+  const uint32_t span = a.xcd_span;
+  bool off_span = false;
+  if constexpr (kLocal) {
+    const uint32_t x = blockIdx.x & 7u, q = blockIdx.x >> 3;
+    r = (int)(q % (uint32_t)N);
+    w = (q / (uint32_t)N) * span + x;
+    off_span = x >= span;
+  } else {
+    decode_role_t<false, N>(blockIdx.x, r, w);
+  }
   // every kernel argument used below, requested at entry as one batch
   const uint8_t* const src = a.part[r];
   uint8_t* const out = a.out;
@@ -183,7 +195,7 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
   LLAR_UNIFORM_AT_ENTRY("s"(src), "s"(out), "s"(stage), "s"(ctrl), "s"(trace), "s"(nbytes), "s"(spin_limit),
                         "s"(slices), "s"(vq), "s"(vr), "s"(stage_bytes), "s"(parity_stride), "s"(rank_stride),
                         "s"(grid), "s"(timing), "s"(keep), "s"(drop_rank), "s"(host_epoch));
-  const bool idle = (w >= slices);
+  const bool idle = off_span || (w >= slices);
   // slice w: 16-byte vectors [v0, v1) for producers, 8-byte units [2 v0, 2 v1)
   // for the consumer (one LL line, or half a Sentinel slot, per lane)
   const uint32_t v0 = idle ? 0u : w * vq + min(w, vr);

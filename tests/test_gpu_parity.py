@@ -871,3 +871,29 @@ def test_process_defaults_reach_new_communicators_and_log_prints_geometry(capfd)
         assert llar.llar_set_option(None, "log", 0) == 0
     with comm_for(8, dt, n * 2) as c:
         assert c.get_option("auto_protocol") == 0 and c.select_protocol(n * 2) == llar.LL
+
+
+@pytest.mark.parametrize("xcds", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("proto", ["ll", "sentinel"])
+def test_one_shot_on_the_first_xcds(proto, xcds):
+    """Option local_xcds keeps a one-shot call's slices on XCDs 0 .. k-1
+    (slice w on XCD w mod k, the other workgroups idle): bit-exact over
+    ragged sizes and slice counts, send/recv too, and the barrier ablation
+    (which keeps all eight XCDs) still right beside it."""
+    dt = BF16
+    with comm_for(8, dt, 64 << 10, local_xcds=xcds, threads=256) as c:
+        for i, n in enumerate((1, 999, 8192, 8192 + 5, 32768)):
+            bits = make_partials(3100 + xcds, i, 8, "bf16", n, "normal", 1.0)
+            got = run(c, bits, proto, dt)
+            assert_exact(got, oracle.allreduce(bits, dt), dt, "%s n=%d xcds=%d" % (proto, n, xcds))
+        c.set_option("slices", 7)
+        bits = make_partials(3110 + xcds, 0, 8, "bf16", 20000, "normal", 1.0)
+        assert_exact(run(c, bits, proto, dt), oracle.allreduce(bits, dt), dt, "7 slices")
+        c.set_option("slices", 0)
+        send = to_device(bits[3], dt)
+        recv = torch.empty(20000, dtype=torch.bfloat16, device="cuda")
+        c.send_recv(send, recv, proto)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(recv, dt), models.p2p_transfer(bits[3], dt, proto))
+        c.set_option("barrier_ablation", 1)
+        assert_exact(run(c, bits, proto, dt), oracle.allreduce(bits, dt), dt, "barrier ablation")
