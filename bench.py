@@ -317,11 +317,19 @@ def measure_workloads(stream, steps, floor_us, ceiling, checks):
                 geo = c.geometry(w.n_elems, llar.PROTOCOLS[w.protocol])
                 chunk = -(-w.n_elems // geo["chunks"])
                 ops = ll128_lane_ops(w.n_ranks, w.n_elems, chunk, bool(acc16))
+                reqs = ll128_requests(w.n_ranks, w.n_elems, chunk, bool(acc16))
                 rate = ops / (dmed * 1e-6) / 1e9
+                rreq = reqs / (dmed * 1e-6) / 1e9
                 ceil = ceiling["pk_bf16_8way_cross_xcd" if acc16 else "f32_8way_cross_xcd"]
+                # the microbenchmark's requests carry 16 lanes each (64 bytes;
+                # TCC_ATOMIC counts 8 388 608 requests for its 134 M lanes)
+                ceil_req = ceil / 16.0
                 row.update({"staging": "16-bit packed" if acc16 else "binary32", "atomic_lane_ops": ops,
                             "atomic_G_lane_ops_per_s": round(rate, 2), "atomic_ceiling_G_per_s": ceil,
-                            "frac_of_atomic_ceiling": round(rate / ceil, 4) if ceil else None})
+                            "frac_of_atomic_ceiling": round(rate / ceil, 4) if ceil else None,
+                            "atomic_requests": reqs, "atomic_G_requests_per_s": round(rreq, 3),
+                            "atomic_request_ceiling_G_per_s": round(ceil_req, 3),
+                            "frac_of_atomic_request_ceiling": round(rreq / ceil_req, 4) if ceil else None})
             rows[name] = row
             log("workload %d %s: %.3f us per call (graph), device %.3f us, %.1f GB/s%s"
                 % (k, name, us, dmed, gbps, "" if "atomic_G_lane_ops_per_s" not in row else
@@ -660,6 +668,22 @@ def measure_atomic_ceiling():
     return res
 
 
+def ll128_requests(n_ranks, n, chunk_elems, acc16):
+    """Memory-side atomic requests one LL128 call issues: per rank and line,
+    one for each 64-byte half of the line that holds data (the first half
+    always does; the second once the line holds more than 15 binary32 or 31
+    16-bit elements) and one for the count -- three per full line, which
+    the TCC_ATOMIC counter confirms."""
+    K = 63 if acc16 else 31
+    half = 31 if acc16 else 15
+    total = 0
+    for c0 in range(0, n, chunk_elems):
+        ln = min(chunk_elems, n - c0)
+        full, rest = divmod(ln, K)
+        total += full * 3 + ((3 if rest > half else 2) if rest else 0)
+    return total * n_ranks
+
+
 def ll128_lane_ops(n_ranks, n, chunk_elems, acc16):
     """Atomic lane operations one LL128 call issues: every rank adds each of
     its elements into its line (one binary32 add per element, or one packed
@@ -756,7 +780,8 @@ def main():
     out_big = torch.empty(n_big, dtype=torch.bfloat16, device="cuda")
     proto_big = comm.select_protocol(BIG_BYTES)
     geo_big = comm.geometry(n_big, 0)
-    us_big_min, us_big, us_big_p90 = time_batches(comm, parts_big, out_big, 0, args.big_steps, 5, stream)
+    big_calls = max(50, args.big_steps)  # 5 batches of >= 10 back-to-back calls: the first launch's gap amortised
+    us_big_min, us_big, us_big_p90 = time_batches(comm, parts_big, out_big, 0, big_calls, 5, stream)
     torch.cuda.synchronize()
     checks.append(("allreduce_64MiB_x8_bf16_auto", bits_big, to_bits(out_big), 2, True))
     alg_bytes = (N_RANKS + 1) * BIG_BYTES
@@ -819,7 +844,7 @@ def main():
                              "barrier_cost_device_us": round(ab_dev_med - ll_dev_med, 3)},
         "bandwidth_64MiB": {"protocol": PROTO_NAMES[proto_big], "geometry": geo_big,
                             "us": {"min": round(us_big_min, 2), "median": round(us_big, 2), "p90": round(us_big_p90, 2)},
-                            "calls_timed": {"batches": 5, "calls_per_batch": max(1, args.big_steps // 5)},
+                            "calls_timed": {"batches": 5, "calls_per_batch": big_calls // 5},
                             "GBps": round(gbps, 1), "algorithmic_bytes": alg_bytes,
                             "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                             "copy_GBps_measured": round(copy_gbps, 1),
