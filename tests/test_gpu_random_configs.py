@@ -2,7 +2,8 @@
 AllGather, send/recv), protocol, rank count, dtype, size, placement,
 workgroup size, the pipelined Sentinel's credit and the epoch source, each
 checked against the oracle (bit-exact for LL and Sentinel, within the atomic
-protocol's tolerance for LL128)."""
+protocol's tolerance for LL128); and draws over the tuning options (chunk,
+slices, LL128 kernel, staging, buffers and consumer waves, first-XCDs span)."""
 import numpy as np
 import pytest
 import torch
@@ -102,6 +103,82 @@ def test_random_configuration(index):
             assert c.device_status()[0] == 0
             wire = "sentinel" if proto == "sentinel" or (proto == "auto" and n * esize > 64 << 10) else "ll"
             assert np.array_equal(to_host(recv, dt), models.p2p_transfer(bits, dt, wire)), str(case)
+    except llar.LlarError as e:
+        if e.status == -2:  # a geometry this device cannot hold at once: a documented refusal
+            pytest.skip("unsupported on this device: %s" % e)
+        raise
+    finally:
+        c.close()
+
+
+# ----------------------------------------------------------------------------- tuning options
+def draw_tuning(rng):
+    """An AllReduce under the kernel-selection and geometry options: chunk
+    size, slices, workgroup size, LL128 kernel, staging and buffers, consumer
+    waves, pipelined-Sentinel buffers and credit, and the first-XCDs span of
+    the one-shot reduce."""
+    dtype = str(rng.choice(DTYPES))
+    n_ranks = int(rng.integers(1, 9))
+    esize = 4 if dtype == "fp32" else 2
+    nbytes = int(rng.choice([rng.integers(1, 4096), rng.integers(4096, 1 << 17), rng.integers(1 << 17, 2 << 20)]))
+    n = max(1, nbytes // esize)
+    proto = str(rng.choice(["ll", "sentinel", "ll128", "ll128_pipelined", "sentinel_pipelined"]))
+    opts = {"placement": int(rng.integers(0, 3)), "slices": int(rng.choice([0, 0, rng.integers(1, 65)])),
+            "chunk_bytes": int(rng.choice([0, 2048, 8192, 32768, 131072]))}
+    # 16-bit LL128 staging: integer data whose partial sums the 16-bit type holds
+    acc16 = dtype != "fp32" and proto.startswith("ll128") and rng.random() < 0.5
+    if acc16 and dtype == "bf16":
+        n_ranks = min(n_ranks, 4)  # |sum| <= 256: exact in bfloat16
+    opts["ll128_acc"] = int(acc16)
+    if proto in ("ll", "sentinel"):
+        opts["local_xcds"] = int(rng.integers(0, 9))
+        opts["threads"] = int(rng.choice([0, 64, 128, 256, 512]))
+    elif proto == "ll128":
+        opts["threads"] = int(rng.choice([0, 64, 128, 256, 512]))
+    elif proto == "ll128_pipelined":
+        kernel = int(rng.integers(0, 2))
+        opts["ll128_kernel"] = kernel
+        if kernel == 0:
+            threads = int(rng.choice([0, 128, 256, 512, 1024]))
+            waves = (threads or 1024) // 64
+            opts["threads"] = threads
+            opts["consumer_waves"] = int(rng.choice([0, rng.integers(1, min(waves - 1, 15) + 1)]))
+            opts["ll128_buffers"] = int(rng.choice([0, 2 * rng.integers(1, 33)]))
+        else:
+            opts["threads"] = int(rng.choice([0, 64, 128, 256, 512]))
+    else:
+        credit = int(rng.integers(0, 3))
+        opts["sentinel_credit"] = credit
+        # the owner credit needs a credit wave beside a producer and a consumer
+        opts["threads"] = int(rng.choice(([0, 128, 256, 512] if credit < 2 else [0, 256, 512])
+                                         + ([1024] if credit else [])))
+        if credit == 0:
+            opts["pipeline_buffers"] = int(rng.choice([4, 6, 8]))
+    return dtype, n_ranks, n, proto, acc16, opts
+
+
+TUNING = [draw_tuning(np.random.default_rng([7500, i])) for i in range(120)]
+
+
+@pytest.mark.parametrize("index", range(len(TUNING)),
+                         ids=["%s-N%d-n%d-%s-a%d" % c[:5] for c in TUNING])
+def test_random_tuning(index):
+    dtype, n_ranks, n, proto, acc16, opts = TUNING[index]
+    dt = CODE[dtype]
+    esize = 4 if dtype == "fp32" else 2
+    c = llar.Communicator(n_ranks, TORCH_DT[dt], n * esize)
+    try:
+        c.set_option("spin_timeout_us", 100_000)
+        for k, v in opts.items():
+            c.set_option(k, v)
+        what = "%s %s N=%d n=%d %s" % (dtype, proto, n_ranks, n, opts)
+        if acc16:
+            bits = make_partials(7600, index, n_ranks, dtype, n, "integer", 1.0)
+            assert_exact(run(c, bits, proto, dt), oracle.allreduce(bits, dt), dt, what)
+        else:
+            bits = make_partials(7600, index, n_ranks, dtype, n, "normal", 0.5)
+            (assert_tol if proto.startswith("ll128") else assert_exact)(
+                run(c, bits, proto, dt), oracle.allreduce(bits, dt), dt, what)
     except llar.LlarError as e:
         if e.status == -2:  # a geometry this device cannot hold at once: a documented refusal
             pytest.skip("unsupported on this device: %s" % e)
