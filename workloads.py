@@ -58,38 +58,61 @@ WORKLOADS = {
 
 
 def draw_values(cfg_id: int, rep: int, n_ranks: int, n_elems: int, dist: str, scale: float) -> np.ndarray:
-    """(n_ranks, n_elems) float32 draws from numpy's PCG64 seeded by [cfg_id, rep]."""
+    """(n_ranks, n_elems) binary64 draws from numpy's PCG64 seeded by [cfg_id, rep]."""
     rng = np.random.default_rng([int(cfg_id), int(rep)])
     shape = (n_ranks, n_elems)
     if dist == "uniform":
-        v = rng.random(shape, dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
+        v = rng.random(shape) * 2.0 - 1.0
     elif dist == "normal":
-        v = rng.standard_normal(shape, dtype=np.float32)
+        v = rng.standard_normal(shape)
     elif dist == "integer":
         # small integers: every partial sum is exact in all three formats
-        v = rng.integers(-64, 65, size=shape).astype(np.float32)
+        v = rng.integers(-64, 65, size=shape).astype(np.float64)
     else:
         raise ValueError(dist)
     if scale != 1.0:
-        v = v * np.float32(scale)
+        v *= scale
     return v
 
 
-def to_bits(values_f32: np.ndarray, dtype: str) -> np.ndarray:
-    """Element bit patterns of the drawn values in the I/O type.
+def _bf16_bits(v: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns of finite binary64 values, rounded once to
+    nearest, ties to even (numpy has no bfloat16).  The values must be zero or
+    within bfloat16's normal range, which every draw above is."""
+    b = np.ascontiguousarray(v, dtype=np.float64).view(np.uint64)
+    sign = (b >> np.uint64(63)).astype(np.uint16) << np.uint16(15)
+    mag = b & np.uint64(0x7FFFFFFFFFFFFFFF)
+    # keep the exponent and the top 7 of the 52 fraction bits: add just under
+    # half of the dropped 45 bits, plus the lowest kept bit (ties to even); a
+    # carry out of the fraction moves into the exponent, as it must
+    lsb = (mag >> np.uint64(45)) & np.uint64(1)
+    r = (mag + np.uint64((1 << 44) - 1) + lsb) >> np.uint64(45)
+    exp = (r >> np.uint64(7)).astype(np.int64)
+    zero = mag == 0
+    e16 = exp - 1023 + 127
+    if np.any(~zero & ((e16 < 1) | (e16 > 254))):
+        raise ValueError("a value outside bfloat16's normal range")
+    out = ((np.where(zero, 0, e16).astype(np.uint16) << np.uint16(7))
+           | (r & np.uint64(0x7F)).astype(np.uint16))
+    return out | sign
 
-    fp32: the float32 draw itself.  fp16: numpy's float16 conversion.  bf16:
-    the upper 16 bits of the float32 pattern (a plain truncation; it only
-    shapes the input distribution).
-    """
-    v = np.ascontiguousarray(values_f32, dtype=np.float32)
-    if dtype == "fp32":
-        return v.view(np.uint32).copy()
-    if dtype == "fp16":
-        return v.astype(np.float16).view(np.uint16).copy()
-    if dtype == "bf16":
-        return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
-    raise ValueError(dtype)
+
+def to_bits(values: np.ndarray, dtype: str) -> np.ndarray:
+    """Element bit patterns of the binary64 draws in the I/O type, each rounded
+    once to nearest, ties to even (numpy's float32 and float16 conversions of
+    a double round that way; bfloat16 is rounded from the binary64 bits)."""
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(v.shape, dtype=BITS_NP[dtype])
+    for r in range(v.shape[0]):  # row by row: bounded temporaries for 64 MiB ranks
+        if dtype == "fp32":
+            out[r] = v[r].astype(np.float32).view(np.uint32)
+        elif dtype == "fp16":
+            out[r] = v[r].astype(np.float16).view(np.uint16)
+        elif dtype == "bf16":
+            out[r] = _bf16_bits(v[r])
+        else:
+            raise ValueError(dtype)
+    return out
 
 
 def make_partials(cfg_id: int, rep: int, n_ranks: int, dtype: str, n_elems: int,
