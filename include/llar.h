@@ -303,7 +303,10 @@ int llar_clear_device_status(llar_comm* h);
  *                      slices on XCDs 0 .. k-1 (slice w on XCD w mod k, the workgroups that land on
  *                      the other XCDs idle); 0 = all eight.  XCDs start a launch at different times
  *                      (measured: XCDs 0-2 within 0.16 us, XCD 3 about 0.3 us later, XCDs 4-7 about
- *                      1 us later), so a small exchange can avoid the late ones
+ *                      1 us later), so a small exchange can avoid the late ones.  All workgroups
+ *                      of a call must be resident at once, so without a "slices" setting the slice
+ *                      count shrinks to what k XCDs hold; an explicit one beyond that is
+ *                      LLAR_ERR_UNSUPPORTED
  *   "log"              1 = print every call's operation, protocol and launch geometry (kernel,
  *                      grid, threads, chunks, placement, epoch source) on stderr
  * llar_get_option also answers "local_placement_ok" (read-only): 1 when

@@ -337,6 +337,16 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
       g.kernel != kKernSentinelOc && g.kernel != kKernSentinelOcLocal && g.kernel != kKernLL128WsAcc32 &&
       g.kernel != kKernLL128WsAcc16)
     return LLAR_ERR_ARG;
+  // a one-shot call kept on the first k XCDs needs all of its workgroups
+  // resident there at once: by default its slices shrink to what those
+  // XCDs' CUs hold (slice w runs on XCD w mod k with its N ranks)
+  if (g.placement == kPlaceLocal && g.xcd_span < 8 && !h->slices) {
+    const int occ = occupancy(h->kind, N, g.kernel, g.threads);
+    if (occ <= 0) return LLAR_ERR_HIP;
+    const long long fit = (long long)g.xcd_span * ((long long)occ * (h->cu_count / 8) / N);
+    g.slices = clampi(std::min<long long>(g.slices, fit), 1, g.slices);
+    g.grid_slices = (int)ceil_div((size_t)g.slices, (size_t)g.xcd_span) * 8;
+  }
   return LLAR_OK;
 }
 

@@ -897,3 +897,22 @@ def test_one_shot_on_the_first_xcds(proto, xcds):
         assert np.array_equal(to_host(recv, dt), models.p2p_transfer(bits[3], dt, proto))
         c.set_option("barrier_ablation", 1)
         assert_exact(run(c, bits, proto, dt), oracle.allreduce(bits, dt), dt, "barrier ablation")
+
+
+@pytest.mark.parametrize("xcds", [1, 2])
+@pytest.mark.parametrize("proto", ["ll", "sentinel"])
+def test_first_xcds_default_slices_fit_the_span(proto, xcds):
+    """With local_xcds = k and no slice count given, a message that would
+    take more slices than k XCDs hold at once gets fewer slices (every
+    workgroup must be resident together) and is still bit-exact; an explicit
+    slice count beyond that stays a refusal with nothing launched."""
+    dt, n = BF16, 1 << 19  # 1 MiB per rank: 64 slices by default on all eight XCDs
+    # 512-thread workgroups: a CU holds at most four, fewer than 8 x 64 / k / 32
+    with comm_for(8, dt, n * 2, local_xcds=xcds, threads=512) as c:
+        geo = c.geometry(n, llar.PROTOCOLS[proto])
+        assert geo["slices"] < 64, geo
+        bits = make_partials(3300 + xcds, 0, 8, "bf16", n, "normal", 1.0)
+        assert_exact(run(c, bits, proto, dt), oracle.allreduce(bits, dt), dt, "%s xcds=%d %s" % (proto, xcds, geo))
+        c.set_option("slices", 64 * xcds)  # 8 x 64 workgroups on each XCD: more than its CUs hold
+        with pytest.raises(llar.LlarError):
+            run(c, bits, proto, dt)
