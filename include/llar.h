@@ -33,6 +33,9 @@
  *   - Device pointers are HIP device allocations on the device that was
  *     current when the communicator was created.
  *   - Streams are hipStream_t passed as void* (0 = the null stream).
+ *   - A communicator serves one host thread at a time (a call advances its
+ *     epoch and reads its options and cached launch limits); different
+ *     communicators may be used from different threads at once.
  *   - Workgroups of one call wait on each other, so a call needs all of its
  *     workgroups resident at once: the library checks that its grid fits the
  *     device's occupancy, but kernels from other streams that fill the GPU

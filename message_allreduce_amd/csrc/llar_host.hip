@@ -104,11 +104,27 @@ struct llar_comm {
   long long thr_sentinel = 64ll << 10;    // AUTO: LL up to (<=) this many bytes
   long long thr_ll128 = 1ll << 62;        // AUTO: one-shot Sentinel up to here (LL128 one round above)
   long long thr_pipelined = 512ll << 10;  // AUTO: pipelined Sentinel above this
+  // resident workgroups per CU by [ranks - 1][kernel][threads 64 .. 1024],
+  // 0 = not asked yet: the occupancy query costs more host time than the
+  // rest of a call's set-up
+  mutable int occ_cache[8][kKernCount][5] = {};
 };
 
 namespace {
 
 int elem_bytes_of(int dtype) { return dtype == LLAR_FP32 ? 4 : 2; }
+
+// Workgroups of `kernel` at `threads` that one CU holds at once, for this
+// communicator's device and dtype (0 on a failed query, which is asked again
+// next time).
+int occupancy_of(const llar_comm* h, int n_launch, int kernel, int threads) {
+  const int ti = threads == 64 ? 0 : threads == 128 ? 1 : threads == 256 ? 2 : threads == 512 ? 3 : threads == 1024 ? 4 : -1;
+  if (ti < 0 || kernel < 0 || kernel >= kKernCount || n_launch < 1 || n_launch > 8)
+    return occupancy(h->kind, n_launch, kernel, threads);
+  int& slot = h->occ_cache[n_launch - 1][kernel][ti];
+  if (slot <= 0) slot = occupancy(h->kind, n_launch, kernel, threads);
+  return slot;
+}
 
 hipError_t alloc_region(Region& r, size_t bytes, int fill) {
   r.bytes = bytes;
@@ -341,7 +357,7 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
   // resident there at once: by default its slices shrink to what those
   // XCDs' CUs hold (slice w runs on XCD w mod k with its N ranks)
   if (g.placement == kPlaceLocal && g.xcd_span < 8 && !h->slices) {
-    const int occ = occupancy(h->kind, N, g.kernel, g.threads);
+    const int occ = occupancy_of(h, N, g.kernel, g.threads);
     if (occ <= 0) return LLAR_ERR_HIP;
     const long long fit = (long long)g.xcd_span * ((long long)occ * (h->cu_count / 8) / N);
     g.slices = clampi(std::min<long long>(g.slices, fit), 1, g.slices);
@@ -770,7 +786,7 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
   ls.grid = n_launch * g.grid_slices;
 
   // every workgroup must be resident at once: consumers spin on producers
-  int occ = occupancy(h->kind, n_launch, g.kernel, g.threads);
+  int occ = occupancy_of(h, n_launch, g.kernel, g.threads);
   if (occ <= 0) return fail(LLAR_ERR_HIP);
   if (ls.grid > occ * h->cu_count) return fail(LLAR_ERR_UNSUPPORTED);
   if (h->timing && ls.grid > kTimingMaxWgs) return fail(LLAR_ERR_UNSUPPORTED);
@@ -993,7 +1009,7 @@ int run_multi(llar_comm* h, const void* const* ins, void* const* outs, int n_rec
     ls.kernel = acc16 ? kKernRsLL128Acc16 : kKernRsLL128Acc32;
     ls.threads = threads;
     ls.grid = N * slices;
-    int occ = occupancy(h->kind, N, ls.kernel, threads);
+    int occ = occupancy_of(h, N, ls.kernel, threads);
     if (occ <= 0) return fail(LLAR_ERR_HIP);
     if (ls.grid > occ * h->cu_count) return fail(LLAR_ERR_UNSUPPORTED);
     if (h->timing && ls.grid > kTimingMaxWgs) return fail(LLAR_ERR_UNSUPPORTED);
@@ -1052,7 +1068,7 @@ int run_multi(llar_comm* h, const void* const* ins, void* const* outs, int n_rec
   ls.kernel = kernel;
   ls.threads = threads;
   ls.grid = N * grid_slices;
-  int occ = occupancy(h->kind, N, kernel, threads);
+  int occ = occupancy_of(h, N, kernel, threads);
   if (occ <= 0) return fail(LLAR_ERR_HIP);
   if (ls.grid > occ * h->cu_count) return fail(LLAR_ERR_UNSUPPORTED);
   if (h->timing && ls.grid > kTimingMaxWgs) return fail(LLAR_ERR_UNSUPPORTED);
