@@ -489,7 +489,7 @@ def measure_floor():
         "t_l2_round_trip_written_by_xcd_ns": {str(k): round(v, 1) for k, v in rt_written.items()},
         "t_l2_round_trip_written_same_xcd_ns": round(rt_written_same, 1),
         # the floor with the cross-XCD round trip in both terms (reported; the
-        # judged floor keeps the smaller L2-hit round trip)
+        # floor the targets use keeps the smaller L2-hit round trip)
         "floor_cross_xcd_rt_us": round((2 * rt_cross + t_store) / 1e3, 4),
         "empty_launch_graph_us": round(launch_graph / 1e3, 3),
         "t_l2_round_trip_ns": round(rt, 1),
