@@ -41,6 +41,7 @@ constexpr size_t kCapChunk = 4ull << 20;  // largest chunk of the pipelined prot
 // 1680 / 1901 us
 constexpr size_t kLL128PipeChunk = 256ull << 10;
 constexpr int kTraceMaxWgs = 4096;
+constexpr int kSmallSpan = 3;  // XCDs of a one-shot call of 5 to 8 default slices
 constexpr int kPipeTraceMaxWgs = 1024;
 // The pipelined Sentinel's region holds 8 staging buffers of the largest
 // chunk (a call spaces its buffers by its own chunk, so more of a smaller
@@ -235,12 +236,10 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
       // measured on MI355X (graph replay, N = 8): 256 threads below 64
       // slices' worth of units, 512 from there (fp16 Sentinel per call:
       // 128 KiB 4.13 -> 4.01 us, 256 KiB 5.49 -> 5.19, 512 KiB 8.13 -> 7.22;
-      // 64 KiB keeps 256: 3.70 against 3.96).  Up to 4 x 512 units the
-      // exchange stays on at most four XCDs (slices): each slice runs on its
-      // own XCD, and the call waits for the slowest one (16 KiB x 8 bf16 LL:
-      // device span 2.0 -> 1.73 us, graph replay 3.40 -> 3.17 us per call)
+      // 64 KiB keeps 256: 3.70 against 3.96).  Between 4 and 8 slices the
+      // exchange keeps to the first three XCDs under the local placement
+      // (below, kSmallSpan)
       g.threads = h->threads ? (int)h->threads : (units >= (size_t)256 * 64 ? 512 : 256);
-      if (!h->threads && units > (size_t)4 * 256 && units <= (size_t)4 * 512) g.threads = 512;
       g.slices = h->slices ? (int)h->slices : clampi((long long)ceil_div(units, (size_t)g.threads), 1, 64);
       break;
     }
@@ -339,6 +338,16 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
     // one-shot LL / Sentinel may keep their slices on the first few XCDs
     const bool oneshot = proto == LLAR_LL || proto == LLAR_SENTINEL;
     g.xcd_span = (oneshot && h->local_xcds > 0) ? (int)h->local_xcds : 8;
+    // The XCDs start a launch at different times (XCDs 0-2 first, XCD 3
+    // about 0.3 us and XCDs 4-7 about 1 us later) and the call waits for its
+    // slowest slice.  So a one-shot call of 5 to 8 default 256-thread slices
+    // keeps them on XCDs 0-2, two or three per XCD.  Measured on MI355X,
+    // 16 KiB x 8 bf16 LL against four 512-thread slices on XCDs 0-3 (five
+    // boxes, medians of 60 calls): device span 1.46-1.58 against
+    // 1.64-1.81 us; graph replay 2.96-3.51 against 3.25-3.65 us per call.
+    // From 32 KiB on, eight XCDs are faster again.
+    if (oneshot && h->local_xcds == 0 && !h->threads && !h->slices && g.slices > 4 && g.slices <= 8)
+      g.xcd_span = kSmallSpan;
     g.grid_slices = (int)ceil_div((size_t)g.slices, (size_t)g.xcd_span) * 8;
     if (g.kernel == kKernSentinelPipe) g.kernel = kKernSentinelPipeLocal;
     if (g.kernel == kKernSentinelHs) g.kernel = kKernSentinelHsLocal;
@@ -1153,10 +1162,9 @@ int llar_send_recv(llar_comm* h, const void* send_buf, void* recv_buf, size_t n_
   // measured on MI355X (8 KB and 256 KiB fp16): a single sender streams
   // best from 512-thread workgroups, one slice per 1024 8-byte units
   if (!h->threads) g.threads = 512;
-  if (!h->slices) {
-    g.slices = clampi((long long)ceil_div(2 * ceil_div(nbytes, 16), (size_t)1024), 2, 64);
-    g.grid_slices = g.placement == kPlaceLocal ? (int)ceil_div((size_t)g.slices, (size_t)g.xcd_span) * 8 : g.slices;
-  }
+  if (!h->local_xcds) g.xcd_span = 8;  // the AllReduce's small-call span is not measured for it
+  if (!h->slices) g.slices = clampi((long long)ceil_div(2 * ceil_div(nbytes, 16), (size_t)1024), 2, 64);
+  g.grid_slices = g.placement == kPlaceLocal ? (int)ceil_div((size_t)g.slices, (size_t)g.xcd_span) * 8 : g.slices;
   // the one-shot exchange with a single producer, in copy mode
   switch (g.kernel) {
     case kKernOneShotLL: g.kernel = kKernP2PLL; break;

@@ -690,17 +690,27 @@ def test_pipelined_short_last_chunk_regression(proto):
 
 def test_default_geometry_rules():
     """The host's default geometry: one-shot workgroups of 256 threads below
-    64 slices' worth of 8-byte units, 512 from there, and 512 as well while
-    that keeps a small message on at most four slices (XCDs) where 256 would
-    need more; pipelined messages cut into the fewest chunks of at most the
-    configured size, and a message shorter than the chunk as one chunk."""
+    64 slices' worth of 8-byte units, 512 from there; under the local
+    placement a call of 5 to 8 slices keeps to XCDs 0-2 (the grid covers
+    three slices per round of eight XCDs), others use all eight; pipelined
+    messages cut into the fewest chunks of at most the configured size, and
+    a message shorter than the chunk as one chunk."""
     with comm_for(8, BF16, 8 << 20) as c:
-        for nbytes, threads in ((8192, 256), (8192 + 16, 512), (16384, 512), (16384 + 16, 256),
-                                (131072 - 16, 256), (131072, 512), (524288, 512)):
-            geo = c.geometry(nbytes // 2, llar.SENTINEL)
-            assert geo["threads"] == threads, (nbytes, geo)
-            units = 2 * (-(-nbytes // 16))
-            assert geo["slices"] == min(64, -(-units // threads)), (nbytes, geo)
+        local = c.get_option("local_placement_ok") == 1
+        for nbytes, threads, span in ((8192, 256, 8), (8192 + 16, 256, 3), (16384, 256, 3), (16384 + 16, 256, 8),
+                                      (131072 - 16, 256, 8), (131072, 512, 8), (524288, 512, 8)):
+            for proto in (llar.LL, llar.SENTINEL):
+                geo = c.geometry(nbytes // 2, proto)
+                assert geo["threads"] == threads, (nbytes, geo)
+                units = 2 * (-(-nbytes // 16))
+                slices = min(64, -(-units // threads))
+                assert geo["slices"] == slices, (nbytes, geo)
+                if local:
+                    assert geo["grid"] == 8 * 8 * (-(-slices // span)), (nbytes, geo)
+        # a given thread count or slice count keeps all eight XCDs
+        c.set_option("threads", 256)
+        assert c.geometry(8192, llar.LL)["grid"] == 64
+        c.set_option("threads", 0)
         for nbytes in (128, 65536, (1 << 20) - 16, 1 << 20, (1 << 20) + 16, (3 << 19), 8 << 20):
             geo = c.geometry(nbytes // 2, llar.SENTINEL_PIPELINED)
             assert geo["chunks"] == max(1, -(-nbytes // (1 << 20))), (nbytes, geo)
