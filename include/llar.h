@@ -302,6 +302,11 @@ int llar_clear_device_status(llar_comm* h);
  *   "auto_protocol"    0 = AUTO follows the thresholds above; 1..5 = AllReduce calls that pass
  *                      LLAR_AUTO run this protocol (send/recv, ReduceScatter and AllGather keep
  *                      their own AUTO rule)
+ *   "consumer_groups"  pipelined Sentinel, workgroup credit: deal the chunks to G groups of the
+ *                      consumer waves (group g takes chunks g, g + G, ...), so that up to G chunks
+ *                      are consumed at once; G must divide the consumer waves (half of the
+ *                      workgroup's) and "pipeline_buffers", else LLAR_ERR_ARG.  0 = two groups
+ *                      where the consumer waves split evenly, else one
  *   "local_xcds"       one-shot LL / Sentinel (and send/recv) under the local placement: keep the
  *                      slices on XCDs 0 .. k-1 (slice w on XCD w mod k, the workgroups that land on
  *                      the other XCDs idle); 0 = all eight.  XCDs start a launch at different times

@@ -102,6 +102,7 @@ struct TwoShotArgs {
   uint32_t shard_cap;    // Sentinel: 16-byte vectors per (owner, sender) slot
   uint32_t n_buffers;    // Sentinel pipeline: staging buffers
   uint32_t cons_waves;   // Sentinel slot handshake: consumer waves per workgroup
+  uint32_t cons_groups;  // Sentinel pipeline, workgroup credit: consumer groups (chunks dealt round-robin)
   uint32_t grid;
   uint32_t slices;
   uint32_t placement;

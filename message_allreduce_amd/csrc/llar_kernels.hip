@@ -740,17 +740,21 @@ __global__ void __launch_bounds__(1024) k_twoshot_ll128_ws(TwoShotArgs a) {
 //            consumer waves have finished chunks 0..c-1-lag -- store them,
 //            sentinel-canonicalised, into [c % B][s][r].  The loads are
 //            issued before the credit wait, so HBM reads overlap it;
-//   consumer waves: for each vector of slice (r, w) of chunk c, poll the N-1
-//            slots [c % B][r][*], add the own partial (requested one chunk
-//            early) and the N-1 staged ones in binary64 in rank order, round,
-//            write `out`, reset the slots; drain (the resets are performed),
-//            then publish "chunk c done" to the producer waves through LDS.
+//   consumer waves, in G groups (group g takes chunks g, g + G, ...): for
+//            each vector of slice (r, w) of its chunk c, poll the N-1 slots
+//            [c % B][r][*], add the own partial (requested one chunk early)
+//            and the N-1 staged ones in binary64 in rank order, round, write
+//            `out`, reset the slots; drain (the resets are performed), then
+//            count the chunk in LDS for the producer waves.
 // The credit: a producer stores chunk c only after this workgroup's
-// consumers finished chunk c-1-lag.  They finished it only after every
-// peer's producer stored chunk c-1-lag, which each did only after its own
-// consumers had finished chunk c-2-2*lag and drained those resets; with
-// B >= 2*lag + 2 buffers that covers chunk c-B, the previous user of chunk
-// c's buffer.
+// consumers finished every chunk up to c-1-lag.  They finished it only
+// after every peer's producer stored chunk c-1-lag, which each did only
+// after its own consumers had finished chunk c-2-2*lag and drained those
+// resets; with B >= 2*lag + 2 buffers that covers chunk c-B, the previous
+// user of chunk c's buffer.  G divides B, so the group that polls chunk c
+// reset chunk c-B's slots itself before (a poll never finds an old chunk's
+// full slot).  With G > 1 up to G chunks are consumed at once, each group's
+// poll, reduce, reset and drain overlapping the others'.
 template <int kKind, int N, bool kLocal>
 __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   constexpr int kU = 2;   // vectors per producer lane per owner per batch
@@ -763,12 +767,15 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   LLAR_UNIFORM_AT_ENTRY("s"(src), "s"(a.out), "s"(a.stage), "s"(a.ctrl), "s"(a.n), "s"(a.spin_limit),
                         "s"(a.chunk_elems), "s"(a.n_chunks), "s"(a.stage_bytes), "s"(a.parity_stride),
                         "s"(a.shard_cap), "s"(a.n_buffers), "s"(a.grid), "s"(a.slices), "s"(a.timing), "s"(a.keep),
-                        "s"(a.drop_rank), "s"(a.host_epoch), "s"(a.trace));
+                        "s"(a.drop_rank), "s"(a.host_epoch), "s"(a.trace), "s"(a.cons_groups));
   const bool idle = (w >= a.slices);
   WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
   using E = Elem<kKind>;
-  __shared__ uint32_t s_done[8];  // per consumer wave: chunks finished
-  if (threadIdx.x < 8) s_done[threadIdx.x] = 0u;
+  // per consumer wave: the next chunk of its group it has not finished (its
+  // group's chunks below are done); a group starts at its first chunk
+  __shared__ uint32_t s_done[8];
+  const uint32_t n_waves_ = blockDim.x >> 6, n_cons_ = n_waves_ - n_waves_ / 2;
+  if (threadIdx.x < 8) s_done[threadIdx.x] = threadIdx.x / max(n_cons_ / max(a.cons_groups, 1u), 1u);
   __syncthreads();
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.stage, a.stage_bytes);
   const uint64_t nbytes = a.n * (uint64_t)E::kBytes;
@@ -781,6 +788,8 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   const uint32_t n_prod = n_waves / 2, n_cons = n_waves - n_prod;
   const uint32_t n_buf = a.n_buffers;
   const uint32_t lag = n_buf / 2u - 1u;
+  // consumer groups: G divides both the consumer waves and B (host-checked)
+  const uint32_t n_grp = a.cons_groups, gw = n_cons / n_grp;
   // the partition uses the nominal chunk so that a slot keeps its (owner,
   // slice) in every chunk; vectors past the end of the message are masked
   const uint32_t nv = chunk_vecs;
@@ -837,6 +846,7 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
         }
         if (b0 == 0 && c > lag) {
           // credit: this workgroup's consumers have finished chunks 0..c-1-lag
+          // (consumer wave i has finished its group's chunks below s_done[i])
           Spin spin(a.spin_limit);
           while (true) {
             uint32_t done = ~0u;
@@ -880,24 +890,30 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   } else {
     // ---------------- consumer waves
     const uint32_t cw = wave - n_prod;
-    const uint32_t cl = cw * 64u + lane, CL = n_cons * 64u;
+    const uint32_t grp = cw / gw, gi = cw % gw;  // group, and wave within it
+    const uint32_t cl = gi * 64u + lane, CL = gw * 64u;
     const uint32_t nv = chunk_vecs;
     const uint32_t o0 = (uint32_t)r * nv / (uint32_t)N, o1 = ((uint32_t)r + 1u) * nv / (uint32_t)N;
     const uint32_t s0 = o0 + w * (o1 - o0) / a.slices;
     const uint32_t s1n = o0 + (w + 1u) * (o1 - o0) / a.slices;
-    // own vectors of the first batch of the next chunk, requested early
+    // own vectors of the first batch of the group's next chunk, requested early
     u32x4 own_next[kUc];
+    auto request_own = [&](uint32_t cn) {
+      const uint64_t nb = (uint64_t)cn * chunk_vecs;
+      const uint32_t nv_next = cn < a.n_chunks ? (uint32_t)min((uint64_t)chunk_vecs, total_vecs - nb) : 0u;
 #pragma unroll
-    for (int u = 0; u < kUc; ++u) {
-      const uint32_t v = s0 + cl + (uint32_t)u * CL;
-      own_next[u] = (!dead && v < s1n && v < total_vecs) ? load_vec(src, v, nbytes) : u32x4{0u, 0u, 0u, 0u};
-    }
-    for (uint32_t c = 0; c < a.n_chunks && !__any((int)dead); ++c) {
+      for (int u = 0; u < kUc; ++u) {
+        const uint32_t v = s0 + cl + (uint32_t)u * CL;
+        own_next[u] = (!dead && v < s1n && v < nv_next) ? load_vec(src, nb + v, nbytes) : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    request_own(grp);
+    for (uint32_t c = grp; c < a.n_chunks && !__any((int)dead); c += n_grp) {
       const uint64_t vbase = (uint64_t)c * chunk_vecs;
       const uint32_t nv_real = (uint32_t)min((uint64_t)chunk_vecs, total_vecs - vbase);
       const uint32_t s1 = min(s1n, max(nv_real, s0));
       const uint32_t my = (c % n_buf) * a.parity_stride + (uint32_t)(r * N) * slot_bytes;
-      if (s1 == s0 && cw == 0) stamp(2, c);  // nothing of this chunk here
+      if (s1 == s0 && gi == 0) stamp(2, c);  // nothing of this chunk here
       for (uint32_t b0 = 0; b0 < s1 - s0 && !dead; b0 += kUc * CL) {
         u32x4 own[kUc];
         bool valid[kUc];
@@ -931,7 +947,7 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
           }
         }
         if (dead) break;
-        if (b0 == 0 && cw == 0) stamp(2, c);
+        if (b0 == 0 && gi == 0) stamp(2, c);
 #pragma unroll
         for (int u = 0; u < kUc; ++u) {
           if (!valid[u]) continue;
@@ -950,19 +966,11 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
       }
       // the resets are performed before the producers may reuse the buffer
       drain_vm();
-      if (cw == 0) stamp(3, c);
+      if (gi == 0) stamp(3, c);
       if (lane == 0 && !__any((int)dead))
-        __hip_atomic_store(&s_done[cw], c + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      // request the next chunk's own vectors while the producers fill it
-      if (c + 1 < a.n_chunks) {
-        const uint64_t nb = (uint64_t)(c + 1) * chunk_vecs;
-        const uint32_t nv_next = (uint32_t)min((uint64_t)chunk_vecs, total_vecs - nb);
-#pragma unroll
-        for (int u = 0; u < kUc; ++u) {
-          const uint32_t v = s0 + cl + (uint32_t)u * CL;
-          own_next[u] = (v < s1n && v < nv_next) ? load_vec(src, nb + v, nbytes) : u32x4{0u, 0u, 0u, 0u};
-        }
-      }
+        __hip_atomic_store(&s_done[cw], c + n_grp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      // request the group's next chunk's own vectors while the producers fill it
+      request_own(c + n_grp);
     }
   }
   wg_end(a.ctrl, st, a.host_epoch, a.grid, a.timing, idle);

@@ -483,17 +483,20 @@ def _check_split(n_ranks, slices, chunks, parities, max_states, credit_lag=0):
 
 
 def check_owner_credit(n_ranks: int, slices: int, chunks: int, buffers: int, cons_waves: int = 1,
-                       wave_order: bool = True, credit: str = "owner",
+                       wave_order: bool = True, credit: str = "owner", lag: int = 0,
                        max_states: int = 2_000_000) -> PipelineResult:
     """Model of the owner-credit schedule over B rotating Sentinel buffers.
 
-    Per (rank r, slice w) a producer P and cons_waves consumer waves.  Chunk
-    c lives in buffer c % B; line (buffer, owner s, slice w) collects one
-    contribution per rank (the rank's own shard included).
+    Per (rank r, slice w) a producer P and cons_waves consumer waves (or
+    groups of waves that take a chunk together).  Chunk c lives in buffer
+    c % B; line (buffer, owner s, slice w) collects one contribution per
+    rank (the rank's own shard included).
       P emits chunk c (one contribution per owner, separate steps) once the
         credit allows it: credit "owner" -- every owner s has consumed every
         chunk <= c - B; credit "own" -- only P's own consumer has (a weaker
-        credit, which the checker must catch);
+        credit, which the checker must catch); credit "workgroup" -- P's own
+        consumers have consumed every chunk < c - lag (the implicit credit of
+        the workgroup pipeline: safe with B >= 2 lag + 2 buffers);
       consumer wave q consumes chunks q, q + Q, ... in order; with
         ``wave_order`` chunk c also waits until chunk c - B (another wave's,
         the previous user of the line) is consumed.  Like the Sentinel, a
@@ -538,6 +541,8 @@ def check_owner_credit(n_ranks: int, slices: int, chunks: int, buffers: int, con
                 need = c - buffers + 1  # chunks below this must be consumed
                 if credit == "owner":
                     ok = all(all_below(cons[idx[(o, w)]], need) for o in range(n_ranks))
+                elif credit == "workgroup":
+                    ok = all_below(cons[ai], c - lag)
                 else:
                     ok = all_below(cons[ai], need)
                 if ok:

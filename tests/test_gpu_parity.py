@@ -324,12 +324,13 @@ def test_sentinel_pipelined_buffers_and_credit_order(buffers):
     """Every staging-buffer count gives the exact sum, and the per-chunk
     stamps of each workgroup follow the credit rule: with B buffers the
     producers enter chunk c only after this workgroup's consumers finished
-    chunk c - B/2 (lag B/2 - 1), and the consumers take the chunks in order."""
+    chunk c - B/2 (lag B/2 - 1), and one consumer group takes the chunks in
+    order (several groups: test_sentinel_pipelined_consumer_groups)."""
     dt = BF16
     n = (3 << 20) // 2 + 11  # 3 MiB + a ragged tail: 49 chunks of 64 KiB
     chunk = 65536
     bits = make_partials(1050, buffers, 8, "bf16", n, "normal", 1.0)
-    with comm_for(8, dt, n * 2, chunk_bytes=chunk, pipeline_buffers=buffers, trace=1) as c:
+    with comm_for(8, dt, n * 2, chunk_bytes=chunk, pipeline_buffers=buffers, consumer_groups=1, trace=1) as c:
         got = run(c, bits, "sentinel_pipelined", dt)
         assert_exact(got, oracle.allreduce(bits, dt), dt, "buffers %d" % buffers)
         assert (c.staging(llar.SENTINEL_PIPELINED) == 0xFF).all()
@@ -349,6 +350,58 @@ def test_sentinel_pipelined_buffers_and_credit_order(buffers):
         assert (done >= ready).all()
         assert (ready[:, 1:] >= done[:, :-1]).all()
         assert (credit[:, lag + 1:] >= done[:, :chunks - lag - 1]).all()
+
+
+@pytest.mark.parametrize("groups,buffers", [(2, 4), (2, 8), (4, 4), (4, 8), (2, 16)])
+def test_sentinel_pipelined_consumer_groups(groups, buffers):
+    """Chunks dealt to G consumer groups (group g takes chunks g, g + G, ...)
+    under the workgroup credit: exact, the staging left all-ones, and the
+    per-chunk stamps follow the rules -- a group takes its chunks in order,
+    and the producers enter chunk c only after every chunk up to c - 1 - lag
+    is done, whichever group had it."""
+    dt = BF16
+    n = (3 << 20) // 2 + 11  # 3 MiB + a ragged tail: 49 chunks of 64 KiB
+    chunk = 65536
+    bits = make_partials(1060, 10 * groups + buffers, 8, "bf16", n, "normal", 1.0)
+    with comm_for(8, dt, n * 2, chunk_bytes=chunk, pipeline_buffers=buffers, consumer_groups=groups, trace=1) as c:
+        got = run(c, bits, "sentinel_pipelined", dt)
+        assert_exact(got, oracle.allreduce(bits, dt), dt, "groups %d buffers %d" % (groups, buffers))
+        assert (c.staging(llar.SENTINEL_PIPELINED) == 0xFF).all()
+        geo = c.geometry(n, llar.SENTINEL_PIPELINED)
+        chunks = geo["chunks"]
+        tr = llar.llar_get_pipeline_trace(c.h).astype(np.int64)
+        lag = buffers // 2 - 1
+        working = tr[:, 0] != 0
+        credit, stored = tr[working, 0:chunks], tr[working, 128:128 + chunks]
+        ready, done = tr[working, 256:256 + chunks], tr[working, 384:384 + chunks]
+        for a_ in (credit, stored, ready, done):
+            assert (a_ > 0).all()
+        assert (stored >= credit).all() and (done >= ready).all()
+        assert (ready[:, groups:] >= done[:, :-groups]).all()
+        for ch in range(lag + 1, chunks):
+            assert (credit[:, ch] >= done[:, :ch - lag].max(axis=1)).all(), ch
+        # a second call through the same buffers stays exact
+        bits = make_partials(1061, 10 * groups + buffers, 8, "bf16", n, "normal", 1.0)
+        assert_exact(run(c, bits, "sentinel_pipelined", dt), oracle.allreduce(bits, dt), dt, "second call")
+
+
+def test_sentinel_pipelined_consumer_groups_refusals():
+    """Groups that do not divide the consumer waves or the buffer count are
+    refused with nothing launched; the default afterwards is exact."""
+    dt = BF16
+    n = 200000
+    bits = make_partials(1062, 0, 8, "bf16", n, "normal", 1.0)
+    with comm_for(8, dt, n * 2, chunk_bytes=65536, pipeline_buffers=4, threads=512) as c:
+        for g in (3, 8):  # 3 divides neither 4 consumer waves nor 4 buffers; 8 exceeds the waves
+            c.set_option("consumer_groups", g)
+            with pytest.raises(llar.LlarError):
+                run(c, bits, "sentinel_pipelined", dt)
+        c.set_option("pipeline_buffers", 6)
+        c.set_option("consumer_groups", 4)  # divides the waves, not the 6 buffers
+        with pytest.raises(llar.LlarError):
+            run(c, bits, "sentinel_pipelined", dt)
+        c.set_option("consumer_groups", 0)
+        assert_exact(run(c, bits, "sentinel_pipelined", dt), oracle.allreduce(bits, dt), dt, "after the refusals")
 
 
 @pytest.mark.parametrize("threads", [256, 512])

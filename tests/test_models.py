@@ -454,3 +454,28 @@ def test_owner_credit_from_the_own_consumer_alone_overwrites():
     for n_ranks in (2, 3):
         r = models.check_owner_credit(n_ranks=n_ranks, slices=1, chunks=4, buffers=2, credit="own")
         assert any(v[0] == "overwrite" for v in r.violations), n_ranks
+
+
+def test_workgroup_credit_with_consumer_groups_is_safe():
+    # the workgroup pipeline with its chunks dealt to G consumer groups
+    # (group g takes chunks g, g + G, ...): with B >= 2 lag + 2 buffers and G
+    # dividing B, no overwrite, no stale read and no deadlock, with no
+    # explicit wave-order wait (the group that polls chunk c consumed c - B)
+    for shape in [dict(n_ranks=2, slices=1, chunks=6, buffers=4, cons_waves=2, lag=1),
+                  dict(n_ranks=3, slices=1, chunks=5, buffers=4, cons_waves=2, lag=1),
+                  dict(n_ranks=2, slices=1, chunks=7, buffers=6, cons_waves=3, lag=2),
+                  dict(n_ranks=2, slices=1, chunks=6, buffers=4, cons_waves=4, lag=1),
+                  dict(n_ranks=2, slices=1, chunks=5, buffers=4, cons_waves=1, lag=1)]:
+        r = models.check_owner_credit(**shape, credit="workgroup", wave_order=False)
+        assert not r.violations and r.deadlocks == 0 and r.terminal_ok == 1, (shape, r)
+
+
+def test_workgroup_credit_with_consumer_groups_failure_modes():
+    # one buffer too few overwrites; groups that do not divide B read a
+    # previous chunk's full line as their own; a lag too large for B overwrites
+    cases = [(dict(n_ranks=2, slices=1, chunks=6, buffers=3, cons_waves=1, lag=1), "overwrite"),
+             (dict(n_ranks=2, slices=1, chunks=6, buffers=4, cons_waves=3, lag=1), "stale read"),
+             (dict(n_ranks=3, slices=1, chunks=6, buffers=4, cons_waves=2, lag=2), "overwrite")]
+    for shape, kind in cases:
+        r = models.check_owner_credit(**shape, credit="workgroup", wave_order=False)
+        assert any(v[0] == kind for v in r.violations), (shape, r.violations[:2])
