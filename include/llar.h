@@ -307,6 +307,8 @@ int llar_clear_device_status(llar_comm* h);
  *                      are consumed at once; G must divide the consumer waves (half of the
  *                      workgroup's) and "pipeline_buffers", else LLAR_ERR_ARG.  0 = two groups
  *                      where the consumer waves split evenly, else one
+ *   "producer_groups"  the same for the producer waves (group p stores chunks p, p + PG, ...); PG
+ *                      must divide the producer waves (half of the workgroup's).  0 = 1
  *   "local_xcds"       one-shot LL / Sentinel (and send/recv) under the local placement: keep the
  *                      slices on XCDs 0 .. k-1 (slice w on XCD w mod k, the workgroups that land on
  *                      the other XCDs idle); 0 = all eight.  XCDs start a launch at different times

@@ -96,7 +96,8 @@ struct llar_comm {
   long long pipe_buffers = 4;  // staging buffers of the pipelined Sentinel (2..64, even for the workgroup credit; they must fit the region)
   long long sentinel_credit = 0;  // pipelined Sentinel: 0 = workgroup credit, 1 = slot handshake, 2 = owner credit
   long long cons_waves = 0;       // slot handshake: consumer waves per workgroup (0 = a quarter)
-  long long cons_groups = 0;      // pipelined Sentinel, workgroup credit: consumer groups (0 = 1)
+  long long cons_groups = 0;      // pipelined Sentinel, workgroup credit: consumer groups (0 = 2 where they divide)
+  long long prod_groups = 0;      // pipelined Sentinel, workgroup credit: producer groups (0 = 1)
   long long barrier_ablation = 0;  // 1: LL/Sentinel AllReduce behind a grid-wide barrier (measurement)
   long long ll128_kernel = 0;      // pipelined LL128: 0 = producer/consumer waves, B buffers; 1 = alternating, 2 parities
   long long auto_proto = 0;        // 0: AUTO follows the threshold table; 1..5: AUTO AllReduce calls run this protocol
@@ -425,6 +426,7 @@ const OptionEntry kOptions[] = {
     {"log", &llar_comm::log},
     {"local_xcds", &llar_comm::local_xcds},
     {"consumer_groups", &llar_comm::cons_groups},
+    {"producer_groups", &llar_comm::prod_groups},
     {"auto_threshold_sentinel", &llar_comm::thr_sentinel},
     {"auto_threshold_ll128", &llar_comm::thr_ll128},
     {"auto_threshold_pipelined", &llar_comm::thr_pipelined},
@@ -452,7 +454,7 @@ bool option_value_ok(const char* key, long long value, int n_ranks) {
   if (is("ll128_buffers")) return value == 0 || (value >= 2 && value <= 64 && value % 2 == 0);
   if (is("auto_protocol")) return value >= 0 && value <= LLAR_SENTINEL_PIPELINED;
   if (is("local_xcds")) return value >= 0 && value <= 8;
-  if (is("consumer_groups")) return value >= 0 && value <= 8;
+  if (is("consumer_groups") || is("producer_groups")) return value >= 0 && value <= 8;
   if (is("timing") || is("keep_staging") || is("trace") || is("device_epoch") || is("barrier_ablation") || is("log"))
     return value == 0 || value == 1;
   if (is("debug_drop_rank")) return value >= -1 && (n_ranks == 0 || value < n_ranks);
@@ -856,6 +858,7 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
                       : 0u;
     a.credit = nullptr;
     a.cons_groups = 1u;
+    a.prod_groups = 1u;
     if (g.kernel == kKernSentinelPipe || g.kernel == kKernSentinelPipeLocal) {
       // the workgroup credit needs an even buffer count (B >= 2 lag + 2);
       // consumer groups must divide both the consumer waves (half of the
@@ -866,9 +869,13 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
       // 284-292 against 296-311 us per call; four one-wave groups, which need
       // two batches per chunk, 455-465 us
       const uint32_t n_cons = (uint32_t)g.threads / 64u - (uint32_t)g.threads / 128u;
+      const uint32_t n_prod = (uint32_t)g.threads / 128u;
       const uint32_t G = h->cons_groups > 0 ? (uint32_t)h->cons_groups : (n_cons % 2u == 0u ? 2u : 1u);
+      const uint32_t PG = h->prod_groups > 0 ? (uint32_t)h->prod_groups : 1u;
       if (n_cons % G != 0u || a.n_buffers % G != 0u) return fail(LLAR_ERR_ARG);
+      if (n_prod % PG != 0u) return fail(LLAR_ERR_ARG);
       a.cons_groups = G;
+      a.prod_groups = PG;
       // buffers spaced by this chunk's own stride, so that small chunks can
       // use more of them in the same region
       a.shard_cap = sentinel_shard_cap((size_t)g.chunk_elems * h->elem, h->n_ranks);

@@ -103,6 +103,7 @@ struct TwoShotArgs {
   uint32_t n_buffers;    // Sentinel pipeline: staging buffers
   uint32_t cons_waves;   // Sentinel slot handshake: consumer waves per workgroup
   uint32_t cons_groups;  // Sentinel pipeline, workgroup credit: consumer groups (chunks dealt round-robin)
+  uint32_t prod_groups;  // Sentinel pipeline, workgroup credit: producer groups (chunks dealt round-robin)
   uint32_t grid;
   uint32_t slices;
   uint32_t placement;

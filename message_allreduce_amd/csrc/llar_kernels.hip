@@ -735,11 +735,12 @@ __global__ void __launch_bounds__(1024) k_twoshot_ll128_ws(TwoShotArgs a) {
 // shard into W slices; a vector keeps its (owner, slice) in every chunk
 // (the partition uses the nominal chunk, the tail of the message is masked).
 // Workgroup (r, w) is split in two halves:
-//   producer waves: for every chunk c, request rank r's vectors of slice
-//            (s, w) for every owner s != r, then -- once this workgroup's
-//            consumer waves have finished chunks 0..c-1-lag -- store them,
-//            sentinel-canonicalised, into [c % B][s][r].  The loads are
-//            issued before the credit wait, so HBM reads overlap it;
+//   producer waves, in PG groups (group p takes chunks p, p + PG, ...): for
+//            its chunk c, request rank r's vectors of slice (s, w) for every
+//            owner s != r, then -- once this workgroup's consumer waves have
+//            finished chunks 0..c-1-lag -- store them, sentinel-canonicalised,
+//            into [c % B][s][r].  The loads are issued before the credit
+//            wait, so HBM reads overlap it;
 //   consumer waves, in G groups (group g takes chunks g, g + G, ...): for
 //            each vector of slice (r, w) of its chunk c, poll the N-1 slots
 //            [c % B][r][*], add the own partial (requested one chunk early)
@@ -754,7 +755,8 @@ __global__ void __launch_bounds__(1024) k_twoshot_ll128_ws(TwoShotArgs a) {
 // user of chunk c's buffer.  G divides B, so the group that polls chunk c
 // reset chunk c-B's slots itself before (a poll never finds an old chunk's
 // full slot).  With G > 1 up to G chunks are consumed at once, each group's
-// poll, reduce, reset and drain overlapping the others'.
+// poll, reduce, reset and drain overlapping the others'; with PG > 1 chunks
+// may be stored out of order, which the argument above does not use.
 template <int kKind, int N, bool kLocal>
 __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   constexpr int kU = 2;   // vectors per producer lane per owner per batch
@@ -767,7 +769,7 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   LLAR_UNIFORM_AT_ENTRY("s"(src), "s"(a.out), "s"(a.stage), "s"(a.ctrl), "s"(a.n), "s"(a.spin_limit),
                         "s"(a.chunk_elems), "s"(a.n_chunks), "s"(a.stage_bytes), "s"(a.parity_stride),
                         "s"(a.shard_cap), "s"(a.n_buffers), "s"(a.grid), "s"(a.slices), "s"(a.timing), "s"(a.keep),
-                        "s"(a.drop_rank), "s"(a.host_epoch), "s"(a.trace), "s"(a.cons_groups));
+                        "s"(a.drop_rank), "s"(a.host_epoch), "s"(a.trace), "s"(a.cons_groups), "s"(a.prod_groups));
   const bool idle = (w >= a.slices);
   WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
   using E = Elem<kKind>;
@@ -788,8 +790,10 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   const uint32_t n_prod = n_waves / 2, n_cons = n_waves - n_prod;
   const uint32_t n_buf = a.n_buffers;
   const uint32_t lag = n_buf / 2u - 1u;
-  // consumer groups: G divides both the consumer waves and B (host-checked)
+  // consumer groups: G divides both the consumer waves and B; producer
+  // groups: PG divides the producer waves (host-checked)
   const uint32_t n_grp = a.cons_groups, gw = n_cons / n_grp;
+  const uint32_t n_pgrp = a.prod_groups, pgw = n_prod / n_pgrp;
   // the partition uses the nominal chunk so that a slot keeps its (owner,
   // slice) in every chunk; vectors past the end of the message are masked
   const uint32_t nv = chunk_vecs;
@@ -800,8 +804,10 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   };
 
   if (wave < n_prod) {
-    // ---------------- producer waves
-    const uint32_t pl = wave * 64u + lane, PL = n_prod * 64u;
+    // ---------------- producer waves, in PG groups (group p stores chunks
+    // p, p + PG, ...: PG chunks' loads in flight at once)
+    const uint32_t pg = wave / pgw, pgi = wave % pgw;  // group, and wave within it
+    const uint32_t pl = pgi * 64u + lane, PL = pgw * 64u;
     const bool silent = ((uint32_t)r == a.drop_rank);
     // slice w of every other owner's shard, the same in every chunk: owner s
     // holds vectors [s nv / N, (s+1) nv / N) of a chunk, split evenly into
@@ -815,7 +821,7 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
       sl0[k] = o0 + w * (o1 - o0) / a.slices;
       sl1[k] = o0 + (w + 1u) * (o1 - o0) / a.slices;
     }
-    for (uint32_t c = 0; c < a.n_chunks && !dead; ++c) {
+    for (uint32_t c = pg; c < a.n_chunks && !dead; c += n_pgrp) {
       const uint64_t vbase = (uint64_t)c * chunk_vecs;
       // vectors of this chunk that exist; the partition below uses the
       // nominal chunk so that a slot keeps its (owner, slice) in every chunk
@@ -861,7 +867,7 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
           }
           if (dead) break;
         }
-        if (b0 == 0 && wave == 0) stamp(0, c);
+        if (b0 == 0 && pgi == 0) stamp(0, c);
         if (silent) continue;
 #pragma unroll
         for (int k = 0; k < N - 1; ++k) {
@@ -872,13 +878,14 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
             if (vo[k][u] != ~0u) st16_stage<kLocal>(rs, slot + vo[k][u] * 16u, sentinel_canon<kKind>(x[k][u]));
         }
       }
-      if (wave == 0) stamp(1, c);
+      if (pgi == 0) stamp(1, c);
     }
-    // the partial last vector of the message (its chunk's credit was taken
-    // when that chunk was staged), by one lane, for the owner whose slice w
-    // holds it; the owner's own vector is read by its consumer directly
-    if (has_tail && !dead && !silent && wave == 0 && lane == 0) {
-      const uint32_t tc = (uint32_t)(full_vecs / chunk_vecs), tv = (uint32_t)(full_vecs % chunk_vecs);
+    // the partial last vector of the message, by one lane of the group that
+    // staged its chunk (that group took the chunk's credit), for the owner
+    // whose slice w holds it; the owner's own vector is read by its consumer
+    // directly
+    const uint32_t tc = (uint32_t)(full_vecs / chunk_vecs), tv = (uint32_t)(full_vecs % chunk_vecs);
+    if (has_tail && !dead && !silent && pg == tc % n_pgrp && pgi == 0 && lane == 0) {
 #pragma unroll
       for (int k = 0; k < N - 1; ++k) {
         if (tv < sl0[k] || tv >= sl1[k]) continue;

@@ -483,7 +483,7 @@ def _check_split(n_ranks, slices, chunks, parities, max_states, credit_lag=0):
 
 
 def check_owner_credit(n_ranks: int, slices: int, chunks: int, buffers: int, cons_waves: int = 1,
-                       wave_order: bool = True, credit: str = "owner", lag: int = 0,
+                       wave_order: bool = True, credit: str = "owner", lag: int = 0, prod_groups: int = 1,
                        max_states: int = 2_000_000) -> PipelineResult:
     """Model of the owner-credit schedule over B rotating Sentinel buffers.
 
@@ -496,7 +496,9 @@ def check_owner_credit(n_ranks: int, slices: int, chunks: int, buffers: int, con
         chunk <= c - B; credit "own" -- only P's own consumer has (a weaker
         credit, which the checker must catch); credit "workgroup" -- P's own
         consumers have consumed every chunk < c - lag (the implicit credit of
-        the workgroup pipeline: safe with B >= 2 lag + 2 buffers);
+        the workgroup pipeline: safe with B >= 2 lag + 2 buffers); with
+        prod_groups = PG the pair has PG producers, producer p emitting
+        chunks p, p + PG, ... (so chunks may be stored out of order);
       consumer wave q consumes chunks q, q + Q, ... in order; with
         ``wave_order`` chunk c also waits until chunk c - B (another wave's,
         the previous user of the line) is consumed.  Like the Sentinel, a
@@ -518,7 +520,9 @@ def check_owner_credit(n_ranks: int, slices: int, chunks: int, buffers: int, con
     def all_below(cnts, x):  # every chunk < x consumed
         return all(consumed(cnts, c) for c in range(min(x, chunks)))
 
-    init = (tuple([(0, 0)] * len(pairs)), tuple([tuple([0] * Q)] * len(pairs)), tuple([(-1, 0)] * n_lines))
+    PG = prod_groups
+    init = (tuple((p, 0) for _ in pairs for p in range(PG)), tuple([tuple([0] * Q)] * len(pairs)),
+            tuple([(-1, 0)] * n_lines))
     res = PipelineResult(states=0, terminal_ok=0)
     seen, stack = set(), [init]
     while stack:
@@ -530,14 +534,17 @@ def check_owner_credit(n_ranks: int, slices: int, chunks: int, buffers: int, con
         if res.states > max_states:
             raise RuntimeError("state space too large")
         prod, cons, lines = st
-        if all(p[0] == chunks for p in prod) and all(q + cnt * Q >= chunks for cc in cons
+        if all(p[0] >= chunks for p in prod) and all(q + cnt * Q >= chunks for cc in cons
                                                      for q, cnt in enumerate(cc)):
             res.terminal_ok += 1
             continue
         moved = False
         for ai, (r, w) in enumerate(pairs):
-            c, s = prod[ai]
-            if c < chunks:
+            for pg in range(PG):
+                pi = ai * PG + pg
+                c, s = prod[pi]
+                if c >= chunks:
+                    continue
                 need = c - buffers + 1  # chunks below this must be consumed
                 if credit == "owner":
                     ok = all(all_below(cons[idx[(o, w)]], need) for o in range(n_ranks))
@@ -545,18 +552,21 @@ def check_owner_credit(n_ranks: int, slices: int, chunks: int, buffers: int, con
                     ok = all_below(cons[ai], c - lag)
                 else:
                     ok = all_below(cons[ai], need)
-                if ok:
-                    lid = line_id(c % buffers, s, w)
-                    held, cnt = lines[lid]
-                    if held not in (-1, c):
-                        res.violations.append(("overwrite", (r, w), c, s, held))
-                        break
-                    nl = list(lines)
-                    nl[lid] = (c, cnt + 1)
-                    npr = list(prod)
-                    npr[ai] = (c, s + 1) if s + 1 < n_ranks else (c + 1, 0)
-                    stack.append((tuple(npr), cons, tuple(nl)))
-                    moved = True
+                if not ok:
+                    continue
+                lid = line_id(c % buffers, s, w)
+                held, cnt = lines[lid]
+                if held not in (-1, c):
+                    res.violations.append(("overwrite", (r, w), c, s, held))
+                    break
+                nl = list(lines)
+                nl[lid] = (c, cnt + 1)
+                npr = list(prod)
+                npr[pi] = (c, s + 1) if s + 1 < n_ranks else (c + PG, 0)
+                stack.append((tuple(npr), cons, tuple(nl)))
+                moved = True
+            if res.violations:
+                break
             for q in range(Q):
                 cc = q + cons[ai][q] * Q
                 if cc >= chunks:

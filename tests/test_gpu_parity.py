@@ -352,18 +352,20 @@ def test_sentinel_pipelined_buffers_and_credit_order(buffers):
         assert (credit[:, lag + 1:] >= done[:, :chunks - lag - 1]).all()
 
 
-@pytest.mark.parametrize("groups,buffers", [(2, 4), (2, 8), (4, 4), (4, 8), (2, 16)])
-def test_sentinel_pipelined_consumer_groups(groups, buffers):
+@pytest.mark.parametrize("groups,pgroups,buffers", [(2, 1, 4), (2, 1, 8), (4, 1, 4), (4, 1, 8), (2, 1, 16),
+                                                     (1, 2, 4), (2, 2, 4), (2, 4, 8), (4, 2, 8)])
+def test_sentinel_pipelined_consumer_groups(groups, pgroups, buffers):
     """Chunks dealt to G consumer groups (group g takes chunks g, g + G, ...)
-    under the workgroup credit: exact, the staging left all-ones, and the
-    per-chunk stamps follow the rules -- a group takes its chunks in order,
-    and the producers enter chunk c only after every chunk up to c - 1 - lag
-    is done, whichever group had it."""
+    and to PG producer groups under the workgroup credit: exact, the staging
+    left all-ones, and the per-chunk stamps follow the rules -- a consumer
+    group takes its chunks in order, and chunk c is stored only after every
+    chunk up to c - 1 - lag is done, whichever groups had them."""
     dt = BF16
     n = (3 << 20) // 2 + 11  # 3 MiB + a ragged tail: 49 chunks of 64 KiB
     chunk = 65536
-    bits = make_partials(1060, 10 * groups + buffers, 8, "bf16", n, "normal", 1.0)
-    with comm_for(8, dt, n * 2, chunk_bytes=chunk, pipeline_buffers=buffers, consumer_groups=groups, trace=1) as c:
+    bits = make_partials(1060, 100 * pgroups + 10 * groups + buffers, 8, "bf16", n, "normal", 1.0)
+    with comm_for(8, dt, n * 2, chunk_bytes=chunk, pipeline_buffers=buffers, consumer_groups=groups,
+                  producer_groups=pgroups, trace=1) as c:
         got = run(c, bits, "sentinel_pipelined", dt)
         assert_exact(got, oracle.allreduce(bits, dt), dt, "groups %d buffers %d" % (groups, buffers))
         assert (c.staging(llar.SENTINEL_PIPELINED) == 0xFF).all()
@@ -381,12 +383,13 @@ def test_sentinel_pipelined_consumer_groups(groups, buffers):
         for ch in range(lag + 1, chunks):
             assert (credit[:, ch] >= done[:, :ch - lag].max(axis=1)).all(), ch
         # a second call through the same buffers stays exact
-        bits = make_partials(1061, 10 * groups + buffers, 8, "bf16", n, "normal", 1.0)
+        bits = make_partials(1061, 100 * pgroups + 10 * groups + buffers, 8, "bf16", n, "normal", 1.0)
         assert_exact(run(c, bits, "sentinel_pipelined", dt), oracle.allreduce(bits, dt), dt, "second call")
 
 
 def test_sentinel_pipelined_consumer_groups_refusals():
-    """Groups that do not divide the consumer waves or the buffer count are
+    """Consumer groups that do not divide the consumer waves or the buffer
+    count, and producer groups that do not divide the producer waves, are
     refused with nothing launched; the default afterwards is exact."""
     dt = BF16
     n = 200000
@@ -401,6 +404,10 @@ def test_sentinel_pipelined_consumer_groups_refusals():
         with pytest.raises(llar.LlarError):
             run(c, bits, "sentinel_pipelined", dt)
         c.set_option("consumer_groups", 0)
+        c.set_option("producer_groups", 3)  # does not divide the 4 producer waves
+        with pytest.raises(llar.LlarError):
+            run(c, bits, "sentinel_pipelined", dt)
+        c.set_option("producer_groups", 0)
         assert_exact(run(c, bits, "sentinel_pipelined", dt), oracle.allreduce(bits, dt), dt, "after the refusals")
 
 

@@ -470,6 +470,22 @@ def test_workgroup_credit_with_consumer_groups_is_safe():
         assert not r.violations and r.deadlocks == 0 and r.terminal_ok == 1, (shape, r)
 
 
+def test_workgroup_credit_with_producer_groups_is_safe():
+    # producers in PG groups (group p stores chunks p, p + PG, ..., so chunks
+    # land out of order) under the same credit: still no overwrite, no stale
+    # read, no deadlock; one buffer too few or a lag too large still overwrites
+    for shape in [dict(n_ranks=2, slices=1, chunks=6, buffers=4, cons_waves=2, lag=1, prod_groups=2),
+                  dict(n_ranks=3, slices=1, chunks=5, buffers=4, cons_waves=2, lag=1, prod_groups=2),
+                  dict(n_ranks=2, slices=1, chunks=7, buffers=6, cons_waves=2, lag=2, prod_groups=3),
+                  dict(n_ranks=2, slices=1, chunks=6, buffers=4, cons_waves=1, lag=1, prod_groups=2)]:
+        r = models.check_owner_credit(**shape, credit="workgroup", wave_order=False)
+        assert not r.violations and r.deadlocks == 0 and r.terminal_ok == 1, (shape, r)
+    for shape in [dict(n_ranks=2, slices=1, chunks=6, buffers=3, cons_waves=1, lag=1, prod_groups=2),
+                  dict(n_ranks=3, slices=1, chunks=6, buffers=4, cons_waves=2, lag=2, prod_groups=2)]:
+        r = models.check_owner_credit(**shape, credit="workgroup", wave_order=False)
+        assert any(v[0] == "overwrite" for v in r.violations), shape
+
+
 def test_workgroup_credit_with_consumer_groups_failure_modes():
     # one buffer too few overwrites; groups that do not divide B read a
     # previous chunk's full line as their own; a lag too large for B overwrites
