@@ -309,6 +309,9 @@ int llar_clear_device_status(llar_comm* h);
  *                      where the consumer waves split evenly, else one
  *   "producer_groups"  the same for the producer waves (group p stores chunks p, p + PG, ...); PG
  *                      must divide the producer waves (half of the workgroup's).  0 = 1
+ *   "consumer_split"   one-shot LL / Sentinel under the local placement: rank 0's part of each slice
+ *                      on 1 or 2 consumer workgroups (contiguous halves of the slice's units, each
+ *                      issuing half the polls); 0 = two from four ranks on, one below
  *   "local_xcds"       one-shot LL / Sentinel (and send/recv) under the local placement: keep the
  *                      slices on XCDs 0 .. k-1 (slice w on XCD w mod k, the workgroups that land on
  *                      the other XCDs idle); 0 = all eight.  XCDs start a launch at different times

@@ -98,6 +98,7 @@ struct llar_comm {
   long long cons_waves = 0;       // slot handshake: consumer waves per workgroup (0 = a quarter)
   long long cons_groups = 0;      // pipelined Sentinel, workgroup credit: consumer groups (0 = 2 where they divide)
   long long prod_groups = 0;      // pipelined Sentinel, workgroup credit: producer groups (0 = 1)
+  long long cons_split = 0;       // one-shot, local placement: consumer workgroups per slice (0 = 2 from N = 4)
   long long barrier_ablation = 0;  // 1: LL/Sentinel AllReduce behind a grid-wide barrier (measurement)
   long long ll128_kernel = 0;      // pipelined LL128: 0 = producer/consumer waves, B buffers; 1 = alternating, 2 parities
   long long auto_proto = 0;        // 0: AUTO follows the threshold table; 1..5: AUTO AllReduce calls run this protocol
@@ -116,6 +117,19 @@ struct llar_comm {
 namespace {
 
 int elem_bytes_of(int dtype) { return dtype == LLAR_FP32 ? 4 : 2; }
+
+// Consumer workgroups per slice of a one-shot call under the local placement
+// (rank 0's work on a slice split into two parts, so that each consumer
+// workgroup issues half the polls; measured on MI355X, N = 8 bf16 LL, device
+// span: 8 KiB 1.44-1.49 against 1.51-1.59 us, 16 KiB 1.44-1.50 against
+// 1.51-1.61, 64 KiB 1.67-1.70 against 1.75-1.78; fp16 Sentinel 128 KiB
+// 2.00-2.03 against 2.14-2.16; N = 4 and N = 2 unchanged).  Option
+// "consumer_split": 0 = two from four ranks on, 1 = one, 2 = two.
+int oneshot_split(const llar_comm* h, int kernel) {
+  if (kernel != kKernOneShotLLLocal && kernel != kKernOneShotSentinelLocal) return 1;
+  if (h->cons_split == 0) return h->n_ranks >= 4 ? 2 : 1;
+  return (int)h->cons_split;
+}
 
 // Workgroups of `kernel` at `threads` that one CU holds at once, for this
 // communicator's device and dtype (0 on a failed query, which is asked again
@@ -366,11 +380,13 @@ int plan(const llar_comm* h, size_t n_elems, int proto, Geometry& g) {
     return LLAR_ERR_ARG;
   // a one-shot call kept on the first k XCDs needs all of its workgroups
   // resident there at once: by default its slices shrink to what those
-  // XCDs' CUs hold (slice w runs on XCD w mod k with its N ranks)
+  // XCDs' CUs hold (slice w runs on XCD w mod k with its N ranks, and the
+  // second consumer workgroup of a split consumer)
   if (g.placement == kPlaceLocal && g.xcd_span < 8 && !h->slices) {
     const int occ = occupancy_of(h, N, g.kernel, g.threads);
     if (occ <= 0) return LLAR_ERR_HIP;
-    const long long fit = (long long)g.xcd_span * ((long long)occ * (h->cu_count / 8) / N);
+    const int per_slice = N + oneshot_split(h, g.kernel) - 1;
+    const long long fit = (long long)g.xcd_span * ((long long)occ * (h->cu_count / 8) / per_slice);
     g.slices = clampi(std::min<long long>(g.slices, fit), 1, g.slices);
     g.grid_slices = (int)ceil_div((size_t)g.slices, (size_t)g.xcd_span) * 8;
   }
@@ -427,6 +443,7 @@ const OptionEntry kOptions[] = {
     {"local_xcds", &llar_comm::local_xcds},
     {"consumer_groups", &llar_comm::cons_groups},
     {"producer_groups", &llar_comm::prod_groups},
+    {"consumer_split", &llar_comm::cons_split},
     {"auto_threshold_sentinel", &llar_comm::thr_sentinel},
     {"auto_threshold_ll128", &llar_comm::thr_ll128},
     {"auto_threshold_pipelined", &llar_comm::thr_pipelined},
@@ -455,6 +472,7 @@ bool option_value_ok(const char* key, long long value, int n_ranks) {
   if (is("auto_protocol")) return value >= 0 && value <= LLAR_SENTINEL_PIPELINED;
   if (is("local_xcds")) return value >= 0 && value <= 8;
   if (is("consumer_groups") || is("producer_groups")) return value >= 0 && value <= 8;
+  if (is("consumer_split")) return value >= 0 && value <= 2;
   if (is("timing") || is("keep_staging") || is("trace") || is("device_epoch") || is("barrier_ablation") || is("log"))
     return value == 0 || value == 1;
   if (is("debug_drop_rank")) return value >= -1 && (n_ranks == 0 || value < n_ranks);
@@ -736,7 +754,7 @@ int llar_launch_geometry(llar_comm* h, size_t n_elems, llar_protocol protocol, i
   Geometry g;
   int st = plan(h, n_elems, proto, g);
   if (st != LLAR_OK) return fail(st);
-  if (grid) *grid = h->n_ranks * g.grid_slices;
+  if (grid) *grid = (h->n_ranks + oneshot_split(h, g.kernel) - 1) * g.grid_slices;
   if (threads) *threads = g.threads;
   if (slices) *slices = g.slices;
   if (chunks) *chunks = g.chunks;
@@ -797,7 +815,8 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
   ls.n_ranks = n_launch;
   ls.kernel = g.kernel;
   ls.threads = g.threads;
-  ls.grid = n_launch * g.grid_slices;
+  ls.oneshot_split = oneshot_split(h, g.kernel);
+  ls.grid = (n_launch + ls.oneshot_split - 1) * g.grid_slices;
 
   // every workgroup must be resident at once: consumers spin on producers
   int occ = occupancy_of(h, n_launch, g.kernel, g.threads);

@@ -162,6 +162,7 @@ struct LaunchSpec {
   int kernel;
   int grid;
   int threads;
+  int oneshot_split;  // local one-shot: consumer workgroups per slice (1 or 2)
   OneShotArgs oneshot;
   TwoShotArgs twoshot;
   MultiArgs multi;

@@ -164,24 +164,31 @@ __device__ __forceinline__ void trace_at(uint64_t* tr, int slot, bool drain) {
 
 // kCopy (point-to-point, N = 2): rank 1 sends, rank 0 writes what arrived
 // instead of a sum and reads no partial of its own.
-template <int kWire, int kKind, int N, bool kLocal, bool kCopy = false>
+// kSplit: rank 0's work on a slice is split over kSplit consumer workgroups
+// (contiguous parts of the slice's units), so that fewer polls issue per CU;
+// a slice then has N - 1 + kSplit workgroups.
+template <int kWire, int kKind, int N, bool kLocal, bool kCopy = false, int kSplit = 1>
 __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
   const uint64_t t_entry = wall_ticks();
-  int r;
-  uint32_t w;
+  static_assert(kSplit >= 1 && (!kCopy || kSplit == 1), "consumer split");
+  constexpr uint32_t NR = (uint32_t)N + kSplit - 1u;  // workgroups per slice
+  uint32_t rr, w;  // role in the slice: 0 .. kSplit-1 rank 0's parts, then ranks 1 .. N-1
   // local placement over the first xcd_span XCDs: workgroup b runs on XCD
-  // b mod 8; slice w lives on XCD w mod span with its N ranks, and the
+  // b mod 8; slice w lives on XCD w mod span with its workgroups, and the
   // workgroups on the other XCDs idle (span 8: decode_role_t's placement)
   const uint32_t span = a.xcd_span;
   bool off_span = false;
   if constexpr (kLocal) {
     const uint32_t x = blockIdx.x & 7u, q = blockIdx.x >> 3;
-    r = (int)(q % (uint32_t)N);
-    w = (q / (uint32_t)N) * span + x;
+    rr = q % NR;
+    w = (q / NR) * span + x;
     off_span = x >= span;
   } else {
-    decode_role_t<false, N>(blockIdx.x, r, w);
+    rr = blockIdx.x % NR;
+    w = blockIdx.x / NR;
   }
+  const int r = rr < (uint32_t)kSplit ? 0 : (int)(rr - kSplit + 1u);
+  const uint32_t part = rr < (uint32_t)kSplit ? rr : 0u;
   // every kernel argument used below, requested at entry as one batch
   const uint8_t* const src = a.part[r];
   uint8_t* const out = a.out;
@@ -202,11 +209,14 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
   const uint32_t v1 = idle ? 0u : v0 + vq + (w < vr ? 1u : 0u);
   const bool producer = (r != 0) && !idle && (uint32_t)r != drop_rank;
   const bool consumer = (r == 0) && !idle;
+  // this consumer workgroup's units: part `part` of the slice's [2 v0, 2 v1)
+  const uint32_t ups = (2u * (v1 - v0) + kSplit - 1u) / kSplit;
+  const uint32_t u_lo = min(2u * v0 + part * ups, 2u * v1), u_hi = min(u_lo + ups, 2u * v1);
   // the first input of this thread is requested before anything else
   u32x4 first_vec = {0u, 0u, 0u, 0u};
   u32x2 first_unit = {0u, 0u};
   if (producer && v0 + threadIdx.x < v1) first_vec = load_vec<false>(src, v0 + threadIdx.x, nbytes);
-  if (!kCopy && consumer && 2 * v0 + threadIdx.x < 2 * v1) first_unit = load_unit(src, 2 * v0 + threadIdx.x, nbytes);
+  if (!kCopy && consumer && u_lo + threadIdx.x < u_hi) first_unit = load_unit(src, u_lo + threadIdx.x, nbytes);
   WgState st = wg_begin(ctrl, host_epoch, timing, idle);
   if (trace && threadIdx.x == 0) trace[blockIdx.x * kTraceWords + 0] = t_entry;
   trace_at(trace, 1, false);
@@ -227,10 +237,10 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
   } else if (consumer) {
     constexpr uint32_t kUnitStage = (kWire == kWireLL) ? 16u : 8u;
     bool dead = false;  // set after a timeout: stop waiting for anything else
-    for (uint32_t u = 2 * v0 + threadIdx.x; u < 2 * v1 && !dead; u += blockDim.x) {
+    for (uint32_t u = u_lo + threadIdx.x; u < u_hi && !dead; u += blockDim.x) {
       u32x2 own = {0u, 0u};
-      if constexpr (!kCopy) own = (u == 2 * v0 + threadIdx.x) ? first_unit : load_unit(src, u, nbytes);
-      if (u == 2 * v0) trace_at(trace, 2, true);
+      if constexpr (!kCopy) own = (u == u_lo + threadIdx.x) ? first_unit : load_unit(src, u, nbytes);
+      if (u == u_lo) trace_at(trace, 2, true);
       // A slot that is ready stays ready for the rest of the call (LL lines
       // carry this call's epoch; a filled Sentinel slot is only reset by this
       // thread), so reload every slot until one pass sees all of them ready
@@ -257,10 +267,10 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
         dead = true;
         continue;
       }
-      if (u == 2 * v0) trace_at(trace, 3, false);
+      if (u == u_lo) trace_at(trace, 3, false);
       if constexpr (kCopy) store_unit(out, u, nbytes, d[0]);
       else store_unit(out, u, nbytes, reduce_unit<kKind, N>(own, d));
-      if (u == 2 * v0) trace_at(trace, 4, true);
+      if (u == u_lo) trace_at(trace, 4, true);
       if constexpr (kWire == kWireSentinel) {
         if (!keep) {
 #pragma unroll
@@ -1556,10 +1566,16 @@ static hipError_t launch_n(const LaunchSpec& ls, hipStream_t stream) {
       hipLaunchKernelGGL((k_oneshot<kWireSentinel, kKind, N, false>), grid, block, 0, stream, ls.oneshot);
       break;
     case kKernOneShotLLLocal:
-      hipLaunchKernelGGL((k_oneshot<kWireLL, kKind, N, true>), grid, block, 0, stream, ls.oneshot);
+      if (ls.oneshot_split == 2)
+        hipLaunchKernelGGL((k_oneshot<kWireLL, kKind, N, true, false, 2>), grid, block, 0, stream, ls.oneshot);
+      else
+        hipLaunchKernelGGL((k_oneshot<kWireLL, kKind, N, true>), grid, block, 0, stream, ls.oneshot);
       break;
     case kKernOneShotSentinelLocal:
-      hipLaunchKernelGGL((k_oneshot<kWireSentinel, kKind, N, true>), grid, block, 0, stream, ls.oneshot);
+      if (ls.oneshot_split == 2)
+        hipLaunchKernelGGL((k_oneshot<kWireSentinel, kKind, N, true, false, 2>), grid, block, 0, stream, ls.oneshot);
+      else
+        hipLaunchKernelGGL((k_oneshot<kWireSentinel, kKind, N, true>), grid, block, 0, stream, ls.oneshot);
       break;
     case kKernLL128Acc32:
       hipLaunchKernelGGL((k_twoshot_ll128<kKind, 0, N>), grid, block, 0, stream, ls.twoshot);

@@ -752,9 +752,10 @@ def test_default_geometry_rules():
     """The host's default geometry: one-shot workgroups of 256 threads below
     64 slices' worth of 8-byte units, 512 from there; under the local
     placement a call of 5 to 8 slices keeps to XCDs 0-2 (the grid covers
-    three slices per round of eight XCDs), others use all eight; pipelined
-    messages cut into the fewest chunks of at most the configured size, and
-    a message shorter than the chunk as one chunk."""
+    three slices per round of eight XCDs), others use all eight, and from
+    four ranks on rank 0's part of a slice runs on two workgroups (N + 1 per
+    slice); pipelined messages cut into the fewest chunks of at most the
+    configured size, and a message shorter than the chunk as one chunk."""
     with comm_for(8, BF16, 8 << 20) as c:
         local = c.get_option("local_placement_ok") == 1
         for nbytes, threads, span in ((8192, 256, 8), (8192 + 16, 256, 3), (16384, 256, 3), (16384 + 16, 256, 8),
@@ -766,10 +767,13 @@ def test_default_geometry_rules():
                 slices = min(64, -(-units // threads))
                 assert geo["slices"] == slices, (nbytes, geo)
                 if local:
-                    assert geo["grid"] == 8 * 8 * (-(-slices // span)), (nbytes, geo)
+                    assert geo["grid"] == 9 * 8 * (-(-slices // span)), (nbytes, geo)
         # a given thread count or slice count keeps all eight XCDs
         c.set_option("threads", 256)
+        assert c.geometry(8192, llar.LL)["grid"] == (72 if local else 64)
+        c.set_option("consumer_split", 1)
         assert c.geometry(8192, llar.LL)["grid"] == 64
+        c.set_option("consumer_split", 0)
         c.set_option("threads", 0)
         for nbytes in (128, 65536, (1 << 20) - 16, 1 << 20, (1 << 20) + 16, (3 << 19), 8 << 20):
             geo = c.geometry(nbytes // 2, llar.SENTINEL_PIPELINED)
@@ -941,6 +945,30 @@ def test_process_defaults_reach_new_communicators_and_log_prints_geometry(capfd)
         assert llar.llar_set_option(None, "log", 0) == 0
     with comm_for(8, dt, n * 2) as c:
         assert c.get_option("auto_protocol") == 0 and c.select_protocol(n * 2) == llar.LL
+
+
+@pytest.mark.parametrize("split", [1, 2])
+@pytest.mark.parametrize("n_ranks", [2, 5, 8])
+@pytest.mark.parametrize("proto", ["ll", "sentinel"])
+def test_one_shot_consumer_split(proto, n_ranks, split):
+    """Rank 0's part of each slice on one or two consumer workgroups (option
+    consumer_split): bit-exact over ragged sizes, slice counts and thread
+    counts (a part may be empty), under the local placement and, where the
+    split does not apply, the spread one."""
+    dt = BF16
+    with comm_for(n_ranks, dt, 256 << 10, consumer_split=split) as c:
+        for i, n in enumerate((1, 3, 999, 8192, 8192 + 5, 65536 + 77, 131072)):
+            bits = make_partials(3400 + 10 * n_ranks + split, i, n_ranks, "bf16", n, "normal", 1.0)
+            assert_exact(run(c, bits, proto, dt), oracle.allreduce(bits, dt), dt, "%s N=%d n=%d split %d" % (proto, n_ranks, n, split))
+        bits = make_partials(3450 + split, n_ranks, n_ranks, "bf16", 20000, "normal", 1.0)
+        for threads, slices in ((64, 3), (128, 7), (512, 1)):
+            c.set_option("threads", threads)
+            c.set_option("slices", slices)
+            assert_exact(run(c, bits, proto, dt), oracle.allreduce(bits, dt), dt, "threads %d slices %d" % (threads, slices))
+        c.set_option("threads", 0)
+        c.set_option("slices", 0)
+        c.set_option("placement", 1)
+        assert_exact(run(c, bits, proto, dt), oracle.allreduce(bits, dt), dt, "spread placement")
 
 
 @pytest.mark.parametrize("xcds", [1, 2, 3, 4, 8])
