@@ -352,7 +352,7 @@ def test_sentinel_pipelined_buffers_and_credit_order(buffers):
         assert (credit[:, lag + 1:] >= done[:, :chunks - lag - 1]).all()
 
 
-@pytest.mark.parametrize("groups,pgroups,buffers", [(2, 1, 4), (2, 1, 8), (4, 1, 4), (4, 1, 8), (2, 1, 16),
+@pytest.mark.parametrize("groups,pgroups,buffers", [(2, 1, 2), (2, 1, 4), (2, 1, 8), (4, 1, 4), (4, 1, 8), (2, 1, 16),
                                                      (1, 2, 4), (2, 2, 4), (2, 4, 8), (4, 2, 8)])
 def test_sentinel_pipelined_consumer_groups(groups, pgroups, buffers):
     """Chunks dealt to G consumer groups (group g takes chunks g, g + G, ...)

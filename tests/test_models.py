@@ -465,7 +465,8 @@ def test_workgroup_credit_with_consumer_groups_is_safe():
                   dict(n_ranks=3, slices=1, chunks=5, buffers=4, cons_waves=2, lag=1),
                   dict(n_ranks=2, slices=1, chunks=7, buffers=6, cons_waves=3, lag=2),
                   dict(n_ranks=2, slices=1, chunks=6, buffers=4, cons_waves=4, lag=1),
-                  dict(n_ranks=2, slices=1, chunks=5, buffers=4, cons_waves=1, lag=1)]:
+                  dict(n_ranks=2, slices=1, chunks=5, buffers=4, cons_waves=1, lag=1),
+                  dict(n_ranks=3, slices=1, chunks=4, buffers=2, cons_waves=2, lag=0)]:
         r = models.check_owner_credit(**shape, credit="workgroup", wave_order=False)
         assert not r.violations and r.deadlocks == 0 and r.terminal_ok == 1, (shape, r)
 
