@@ -783,12 +783,6 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   const bool idle = (w >= a.slices);
   WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
   using E = Elem<kKind>;
-  // per consumer wave: the next chunk of its group it has not finished (its
-  // group's chunks below are done); a group starts at its first chunk
-  __shared__ uint32_t s_done[8];
-  const uint32_t n_waves_ = blockDim.x >> 6, n_cons_ = n_waves_ - n_waves_ / 2;
-  if (threadIdx.x < 8) s_done[threadIdx.x] = threadIdx.x / max(n_cons_ / max(a.cons_groups, 1u), 1u);
-  __syncthreads();
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.stage, a.stage_bytes);
   const uint64_t nbytes = a.n * (uint64_t)E::kBytes;
   const uint32_t chunk_vecs = (uint32_t)(((uint64_t)a.chunk_elems * E::kBytes + 15u) / 16u);
@@ -804,6 +798,11 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   // groups: PG divides the producer waves (host-checked)
   const uint32_t n_grp = a.cons_groups, gw = n_cons / n_grp;
   const uint32_t n_pgrp = a.prod_groups, pgw = n_prod / n_pgrp;
+  // per consumer wave: the next chunk of its group it has not finished (its
+  // group's chunks below are done); a group starts at its first chunk
+  __shared__ uint32_t s_done[8];
+  if (threadIdx.x < n_cons) s_done[threadIdx.x] = threadIdx.x / gw;
+  __syncthreads();
   // the partition uses the nominal chunk so that a slot keeps its (owner,
   // slice) in every chunk; vectors past the end of the message are masked
   const uint32_t nv = chunk_vecs;
