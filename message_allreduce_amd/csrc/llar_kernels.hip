@@ -74,6 +74,21 @@ __device__ __forceinline__ void store_unit(uint8_t* p, uint64_t u, uint64_t nbyt
     if (off + k < nbytes) *reinterpret_cast<uint16_t*>(p + off + k) = (uint16_t)(x[k >> 2] >> ((k & 2u) * 8u));
   }
 }
+// 4-byte half units (the one-shot consumer's granularity when each lane
+// needs only one): the last one of a 16-bit message may hold one element
+__device__ __forceinline__ uint32_t load_half(const uint8_t* p, uint64_t h, uint64_t nbytes) {
+  const uint64_t off = h * 4u;
+  if (off + 4u <= nbytes) return *reinterpret_cast<const uint32_t*>(p + off);
+  return off < nbytes ? (uint32_t)*reinterpret_cast<const uint16_t*>(p + off) : 0u;
+}
+__device__ __forceinline__ void store_half(uint8_t* p, uint64_t h, uint64_t nbytes, uint32_t x) {
+  const uint64_t off = h * 4u;
+  if (off + 4u <= nbytes) {
+    *reinterpret_cast<uint32_t*>(p + off) = x;
+    return;
+  }
+  if (off < nbytes) *reinterpret_cast<uint16_t*>(p + off) = (uint16_t)x;
+}
 template <bool kStream = false>
 __device__ __forceinline__ void store_vec(uint8_t* p, uint64_t v, uint64_t nbytes, u32x4 x) {
   const uint64_t off = v * 16u;
@@ -147,6 +162,27 @@ __device__ __forceinline__ u32x2 reduce_unit(const u32x2& own, const u32x2 (&d)[
   return out;
 }
 
+// The same for a 4-byte half unit (one binary32 or two 16-bit elements).
+template <int kKind, int N>
+__device__ __forceinline__ uint32_t reduce_half(uint32_t own, const uint32_t (&d)[N > 1 ? N - 1 : 1]) {
+  constexpr int kPer = 4 / Elem<kKind>::kBytes;
+  uint32_t out = 0u;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    auto elem = [&](uint32_t v) -> uint32_t {
+      if constexpr (Elem<kKind>::kBytes == 4) return v;
+      else return (v >> (j * 16)) & 0xFFFFu;
+    };
+    double s = Elem<kKind>::dec(elem(own));
+#pragma unroll
+    for (int r = 1; r < N; ++r) s += Elem<kKind>::dec(elem(d[r - 1]));
+    const uint32_t bits = Elem<kKind>::enc(s);
+    if constexpr (Elem<kKind>::kBytes == 4) out = bits;
+    else out |= (bits & 0xFFFFu) << (j * 16);
+  }
+  return out;
+}
+
 // ---------------------------------------------------------------------------
 // one-shot LL / Sentinel: ranks 1..N-1 push, rank 0 reduces the whole message
 // ---------------------------------------------------------------------------
@@ -212,11 +248,25 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
   // this consumer workgroup's units: part `part` of the slice's [2 v0, 2 v1)
   const uint32_t ups = (2u * (v1 - v0) + kSplit - 1u) / kSplit;
   const uint32_t u_lo = min(2u * v0 + part * ups, 2u * v1), u_hi = min(u_lo + ups, 2u * v1);
+  // LL: when every 4-byte half of this consumer's units has a lane of its
+  // own, each lane takes a half (the LL half line {data, epoch}): the same
+  // polls spread over twice the lanes, and half the binary64 reduce per lane
+  // on the path's critical end (16 KiB x 8 bf16, device span 1.47-1.51 ->
+  // 1.39-1.46 us on MI355X).  Sentinel keeps 8-byte units: 4-byte quarter
+  // slots measured slower there (128 KiB x 8 fp16, 2.29 -> 2.37 us).
+  // Uniform per workgroup.
+  const bool halves = kWire == kWireLL && 2u * (u_hi - u_lo) <= blockDim.x;
   // the first input of this thread is requested before anything else
   u32x4 first_vec = {0u, 0u, 0u, 0u};
   u32x2 first_unit = {0u, 0u};
   if (producer && v0 + threadIdx.x < v1) first_vec = load_vec<false>(src, v0 + threadIdx.x, nbytes);
-  if (!kCopy && consumer && u_lo + threadIdx.x < u_hi) first_unit = load_unit(src, u_lo + threadIdx.x, nbytes);
+  if (!kCopy && consumer) {
+    if (halves) {
+      if (2u * u_lo + threadIdx.x < 2u * u_hi) first_unit[0] = load_half(src, 2u * u_lo + threadIdx.x, nbytes);
+    } else if (u_lo + threadIdx.x < u_hi) {
+      first_unit = load_unit(src, u_lo + threadIdx.x, nbytes);
+    }
+  }
   WgState st = wg_begin(ctrl, host_epoch, timing, idle);
   if (trace && threadIdx.x == 0) trace[blockIdx.x * kTraceWords + 0] = t_entry;
   trace_at(trace, 1, false);
@@ -233,6 +283,87 @@ __global__ void __launch_bounds__(512) k_oneshot(OneShotArgs a) {
       if constexpr (kWire == kWireLL) llar_wire::ll_put16<scope_of(kLocal)>(rs, off, x, e);
       else llar_wire::sentinel_put<Elem<kKind>::kBytes, scope_of(kLocal)>(rs, off, x);
       if (v == v0) trace_at(trace, 3, true);
+    }
+  } else if (consumer && halves) {
+    // (LL only) one 4-byte half unit per lane: half h of unit u = h / 2 is
+    // the half line {data, epoch} at u * 16 + (h % 2) * 8
+    const uint32_t h = 2u * u_lo + threadIdx.x;
+    if (h < 2u * u_hi) {
+      const uint32_t own = kCopy ? 0u : first_unit[0];
+      if (h == 2u * u_lo) trace_at(trace, 2, true);
+      const uint32_t off_h = (h >> 1) * 16u + (h & 1u) * 8u;
+      // With two ranks, two poll passes in flight, issued half a round trip
+      // apart: a pass is re-issued as soon as its answer is checked, so the
+      // slot is sampled about every half round trip and an arrival is seen
+      // sooner than with one pass at a time (128 B x 2 fp32, device span
+      // 0.76 -> 0.64-0.68 us).  With more ranks the doubled poll traffic
+      // slows the senders' stores more than it saves (64 KiB x 8 bf16,
+      // 2.1 -> 2.4 us), so one pass at a time.  A slot that is ready stays
+      // ready for the rest of the call (its line carries this call's epoch),
+      // so the pass that first finds every slot ready supplies the data.
+      constexpr bool kTwoPass = N <= 2;
+      using PT = u32x2;
+      PT pa[N > 1 ? N - 1 : 1], pb[N > 1 ? N - 1 : 1];
+      auto issue = [&](PT (&q)[N > 1 ? N - 1 : 1]) {
+#pragma unroll
+        for (int k = 0; k < N - 1; ++k) {
+          q[k] = llar_wire::ld8_coh(rs, par_off + (uint32_t)k * rank_stride + off_h);
+        }
+      };
+      auto ready = [&](const PT (&q)[N > 1 ? N - 1 : 1]) {
+        bool all = true;
+#pragma unroll
+        for (int k = 0; k < N - 1; ++k) all &= q[k][1] == e;
+        return all;
+      };
+      uint32_t d[N > 1 ? N - 1 : 1];
+      auto take = [&](const PT (&q)[N > 1 ? N - 1 : 1]) {
+#pragma unroll
+        for (int k = 0; k < N - 1; ++k) d[k] = q[k][0];
+      };
+      bool ok = true;
+      if constexpr (kTwoPass) {
+        llar_wire::PollT<0> spin(spin_limit);
+        issue(pa);
+        __builtin_amdgcn_s_sleep(2);  // about half an L2 round trip
+        while (true) {
+          issue(pb);
+          if (ready(pa)) {
+            take(pa);
+            break;
+          }
+          issue(pa);
+          if (ready(pb)) {
+            take(pb);
+            break;
+          }
+          if (spin.expired()) {
+            raise_status(ctrl, kStatusTimeout);
+            ok = false;
+            break;
+          }
+        }
+      } else {
+        Spin spin(spin_limit);
+        while (true) {
+          issue(pa);
+          if (ready(pa)) {
+            take(pa);
+            break;
+          }
+          if (spin.expired()) {
+            raise_status(ctrl, kStatusTimeout);
+            ok = false;
+            break;
+          }
+        }
+      }
+      if (ok) {
+        if (h == 2u * u_lo) trace_at(trace, 3, false);
+        if constexpr (kCopy) store_half(out, h, nbytes, d[0]);
+        else store_half(out, h, nbytes, reduce_half<kKind, N>(own, d));
+        if (h == 2u * u_lo) trace_at(trace, 4, true);
+      }
     }
   } else if (consumer) {
     constexpr uint32_t kUnitStage = (kWire == kWireLL) ? 16u : 8u;
