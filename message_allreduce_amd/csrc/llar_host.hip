@@ -981,6 +981,7 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
     a.drop_rank = h->debug_drop_rank < 0 ? 0xFFFFFFFFu : (uint32_t)h->debug_drop_rank;
     a.host_epoch = host_epoch;
     a.trace = nullptr;
+    a.threads = (uint32_t)ls.threads;
     const bool pipe_kernel = g.kernel == kKernSentinelPipe || g.kernel == kKernSentinelPipeLocal ||
                              g.kernel == kKernSentinelHs || g.kernel == kKernSentinelHsLocal ||
                              g.kernel == kKernSentinelOc || g.kernel == kKernSentinelOcLocal;

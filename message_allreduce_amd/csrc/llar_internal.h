@@ -113,6 +113,8 @@ struct TwoShotArgs {
   uint32_t host_epoch;
   uint64_t* trace;       // per-workgroup, per-chunk stamps (kPipeTraceWords each), or null
   uint32_t* credit;      // Sentinel pipeline, owner credit: [rank][slice][consumer wave] {count, epoch}, or null
+  uint32_t threads;      // workgroup size, read with the other arguments (blockDim.x would be
+                         // one more dependent scalar load, from the kernarg line after them)
 };
 
 // ReduceScatter / AllGather over the LL or Sentinel wire.  A block is what

@@ -455,7 +455,7 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
   LLAR_UNIFORM_AT_ENTRY("s"(src_l), "s"(src_s), "s"(a.out), "s"(a.stage), "s"(a.ctrl), "s"(a.n), "s"(a.spin_limit),
                         "s"(a.chunk_elems), "s"(a.n_chunks), "s"(a.stage_bytes), "s"(a.parity_stride), "s"(a.grid),
                         "s"(a.slices), "s"(a.placement), "s"(a.timing), "s"(a.keep), "s"(a.drop_rank),
-                        "s"(a.host_epoch));
+                        "s"(a.host_epoch), "s"(a.threads));
   const bool local = (a.placement == kPlaceLocal);
   const int r = local ? r_l : r_s;
   const uint32_t w = local ? w_l : w_s;
@@ -465,7 +465,7 @@ __global__ void __launch_bounds__(512) k_twoshot_ll128(TwoShotArgs a) {
   constexpr int kSlots = kAcc16 ? 64 : 32;
   constexpr int K = kSlots - 1;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.stage, a.stage_bytes);
-  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
+  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = a.threads >> 6;
   const uint8_t* src = local ? src_l : src_s;
   // flag value N in the staging type
   uint32_t flag_full;
@@ -644,7 +644,7 @@ __global__ void __launch_bounds__(1024) k_twoshot_ll128_ws(TwoShotArgs a) {
   LLAR_UNIFORM_AT_ENTRY("s"(src_l), "s"(src_s), "s"(a.out), "s"(a.stage), "s"(a.ctrl), "s"(a.n), "s"(a.spin_limit),
                         "s"(a.chunk_elems), "s"(a.n_chunks), "s"(a.stage_bytes), "s"(a.parity_stride), "s"(a.grid),
                         "s"(a.slices), "s"(a.placement), "s"(a.timing), "s"(a.keep), "s"(a.drop_rank),
-                        "s"(a.host_epoch), "s"(a.n_buffers), "s"(a.cons_waves));
+                        "s"(a.host_epoch), "s"(a.n_buffers), "s"(a.cons_waves), "s"(a.threads));
   const bool local = (a.placement == kPlaceLocal);
   const int r = local ? r_l : r_s;
   const uint32_t w = local ? w_l : w_s;
@@ -659,7 +659,7 @@ __global__ void __launch_bounds__(1024) k_twoshot_ll128_ws(TwoShotArgs a) {
   if (threadIdx.x == 0) s_dead = 0u;
   __syncthreads();
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.stage, a.stage_bytes);
-  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
+  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = a.threads >> 6;
   const uint32_t n_cons = a.cons_waves, n_prod = n_waves - n_cons;
   const uint32_t n_buf = a.n_buffers, lag = n_buf / 2u - 1u;
   const uint8_t* src = local ? src_l : src_s;
@@ -910,7 +910,7 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   LLAR_UNIFORM_AT_ENTRY("s"(src), "s"(a.out), "s"(a.stage), "s"(a.ctrl), "s"(a.n), "s"(a.spin_limit),
                         "s"(a.chunk_elems), "s"(a.n_chunks), "s"(a.stage_bytes), "s"(a.parity_stride),
                         "s"(a.shard_cap), "s"(a.n_buffers), "s"(a.grid), "s"(a.slices), "s"(a.timing), "s"(a.keep),
-                        "s"(a.drop_rank), "s"(a.host_epoch), "s"(a.trace), "s"(a.cons_groups), "s"(a.prod_groups));
+                        "s"(a.drop_rank), "s"(a.host_epoch), "s"(a.trace), "s"(a.cons_groups), "s"(a.prod_groups), "s"(a.threads));
   const bool idle = (w >= a.slices);
   WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
   using E = Elem<kKind>;
@@ -921,7 +921,7 @@ __global__ void __launch_bounds__(512) k_twoshot_sentinel(TwoShotArgs a) {
   const uint64_t full_vecs = nbytes / 16u;          // whole vectors of the message
   const bool has_tail = (nbytes % 16u) != 0u;       // vector full_vecs is partial
   const uint32_t slot_bytes = a.shard_cap * 16u;
-  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
+  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = a.threads >> 6;
   const uint32_t n_prod = n_waves / 2, n_cons = n_waves - n_prod;
   const uint32_t n_buf = a.n_buffers;
   const uint32_t lag = n_buf / 2u - 1u;
@@ -1169,7 +1169,7 @@ __global__ void __launch_bounds__(1024) k_twoshot_sentinel_hs(TwoShotArgs a) {
   LLAR_UNIFORM_AT_ENTRY("s"(src), "s"(a.out), "s"(a.stage), "s"(a.ctrl), "s"(a.n), "s"(a.spin_limit),
                         "s"(a.chunk_elems), "s"(a.n_chunks), "s"(a.stage_bytes), "s"(a.parity_stride),
                         "s"(a.shard_cap), "s"(a.n_buffers), "s"(a.grid), "s"(a.slices), "s"(a.timing), "s"(a.keep),
-                        "s"(a.drop_rank), "s"(a.host_epoch), "s"(a.cons_waves));
+                        "s"(a.drop_rank), "s"(a.host_epoch), "s"(a.cons_waves), "s"(a.threads));
   const bool idle = (w >= a.slices);
   WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
   using E = Elem<kKind>;
@@ -1180,7 +1180,7 @@ __global__ void __launch_bounds__(1024) k_twoshot_sentinel_hs(TwoShotArgs a) {
   const bool has_tail = (nbytes % 16u) != 0u;       // vector full_vecs is partial
   const uint64_t total_vecs = full_vecs + (has_tail ? 1u : 0u);
   const uint32_t slot_bytes = a.shard_cap * 16u;
-  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
+  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = a.threads >> 6;
   // the host splits the waves: n_cons consume (staging reads only), the
   // rest produce
   const uint32_t n_cons = a.cons_waves, n_prod = n_waves - n_cons;
@@ -1419,7 +1419,7 @@ __global__ void __launch_bounds__(1024) k_twoshot_sentinel_oc(TwoShotArgs a) {
   LLAR_UNIFORM_AT_ENTRY("s"(src), "s"(a.out), "s"(a.stage), "s"(a.ctrl), "s"(a.n), "s"(a.spin_limit),
                         "s"(a.chunk_elems), "s"(a.n_chunks), "s"(a.stage_bytes), "s"(a.parity_stride),
                         "s"(a.shard_cap), "s"(a.n_buffers), "s"(a.grid), "s"(a.slices), "s"(a.timing), "s"(a.keep),
-                        "s"(a.drop_rank), "s"(a.host_epoch), "s"(a.cons_waves), "s"(a.credit));
+                        "s"(a.drop_rank), "s"(a.host_epoch), "s"(a.cons_waves), "s"(a.credit), "s"(a.threads));
   const bool idle = (w >= a.slices);
   WgState st = wg_begin(a.ctrl, a.host_epoch, a.timing, idle);
   using E = Elem<kKind>;
@@ -1434,7 +1434,7 @@ __global__ void __launch_bounds__(1024) k_twoshot_sentinel_oc(TwoShotArgs a) {
   const uint64_t full_vecs = nbytes / 16u;
   const bool has_tail = (nbytes % 16u) != 0u;  // vector full_vecs is partial
   const uint32_t slot_bytes = a.shard_cap * 16u;
-  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
+  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6, n_waves = a.threads >> 6;
   const uint32_t n_cons = a.cons_waves, n_prod = n_waves - n_cons - 1u;
   const uint32_t n_buf = a.n_buffers, n_chunks = a.n_chunks;
   const uint32_t reset_off = a.keep ? kOff : 0u;  // tests: keep the staged data
