@@ -83,3 +83,38 @@ def test_ll_send_recv_switch_bit_exact(dtype):
                 assert st == 0, "device status %d bits %#x" % (st, sbits)
                 assert_exact(to_host(recv, dt), models.p2p_transfer(bits, dt, "ll"), dt,
                              "send/recv %s %d B rep %d" % (dtype, nbytes, rep))
+
+
+@pytest.mark.parametrize("copy", [False, True], ids=["allreduce", "send_recv"])
+def test_two_rank_two_pass_poll_times_out_and_recovers(copy):
+    """Two ranks: the half-line consumer keeps two poll passes in flight.  With
+    the sending rank silenced from the host its bounded wait still expires
+    (status TIMEOUT, the kernel ends), and after a reset the same call is
+    exact again."""
+    dt = CODE["fp32"]
+    n = 32
+    bits = make_partials(910, 0, 2, "fp32", n, "uniform", 1.0)
+    with comm_for(2, dt, 64 << 10) as c:
+        c.set_option("spin_timeout_us", 2000)
+        c.set_option("debug_drop_rank", 1)
+        out = torch.empty(n, dtype=TORCH_DT[dt], device="cuda")
+        parts = [to_device(bits[r], dt) for r in range(2)]
+        if copy:
+            c.send_recv(parts[1], out, "ll")
+        else:
+            c.allreduce(parts, out, "ll")
+        torch.cuda.synchronize()
+        st, status_bits = c.device_status()
+        assert st == -5 and (status_bits & 1), (st, status_bits)
+        c.clear_device_status()
+        c.set_option("debug_drop_rank", -1)
+        c.set_option("spin_timeout_us", 100_000)
+        if copy:
+            c.send_recv(parts[1], out, "ll")
+            torch.cuda.synchronize()
+            st, status_bits = c.device_status()
+            assert st == 0, (st, status_bits)
+            assert_exact(to_host(out, dt), models.p2p_transfer(bits[1], dt, "ll"), dt, "send/recv after recovery")
+        else:
+            got = run(c, bits, "ll", dt)
+            assert_exact(got, oracle.allreduce(bits, dt), dt, "allreduce after recovery")
