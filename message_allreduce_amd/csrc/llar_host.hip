@@ -982,6 +982,7 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
     a.host_epoch = host_epoch;
     a.trace = nullptr;
     a.threads = (uint32_t)ls.threads;
+    a.slices_rcp = 0u;
     const bool pipe_kernel = g.kernel == kKernSentinelPipe || g.kernel == kKernSentinelPipeLocal ||
                              g.kernel == kKernSentinelHs || g.kernel == kKernSentinelHsLocal ||
                              g.kernel == kKernSentinelOc || g.kernel == kKernSentinelOcLocal;
@@ -997,6 +998,19 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
       size_t K = (g.kernel == kKernLL128Acc16) ? 63 : 31;
       size_t lines = ceil_div((size_t)g.chunk_elems, K);  // the nominal chunk's lines
       if (lines * 128 > reg->parity_stride) return fail(LLAR_ERR_UNSUPPORTED);
+      // The line partition divides w x (lines of an owner) by the slice
+      // count, w <= slices.  With m = ceil(2^32 / d) and e = m d - 2^32 < d,
+      // umulhi(x, m) = floor(x / d) whenever x e < 2^32 (the error term
+      // x e / (d 2^32) then stays below 1 / d), so the kernel multiplies
+      // instead of dividing when that holds for the largest numerator.
+      a.slices_rcp = 0u;
+      const uint64_t d = (uint64_t)g.slices;
+      if (d >= 2u) {
+        const uint64_t m = ((1ull << 32) + d - 1u) / d;
+        const uint64_t e = m * d - (1ull << 32);
+        const uint64_t x_max = d * ceil_div((uint64_t)lines, (uint64_t)h->n_ranks);
+        if (m <= 0xFFFFFFFFull && x_max * e < (1ull << 32)) a.slices_rcp = (uint32_t)m;
+      }
     }
   }
   if (!reg->ptr) return fail(LLAR_ERR_UNSUPPORTED);

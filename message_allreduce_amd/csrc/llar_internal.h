@@ -115,6 +115,8 @@ struct TwoShotArgs {
   uint32_t* credit;      // Sentinel pipeline, owner credit: [rank][slice][consumer wave] {count, epoch}, or null
   uint32_t threads;      // workgroup size, read with the other arguments (blockDim.x would be
                          // one more dependent scalar load, from the kernarg line after them)
+  uint32_t slices_rcp;   // one-round LL128: ceil(2^32 / slices) when x / slices == umulhi(x, it)
+                         // for every numerator of the line partition, else 0 (divide)
 };
 
 // ReduceScatter / AllGather over the LL or Sentinel wire.  A block is what
