@@ -1009,7 +1009,7 @@ int issue(llar_comm* h, const void* const* parts, int n_launch, void* out, size_
         const uint64_t m = ((1ull << 32) + d - 1u) / d;
         const uint64_t e = m * d - (1ull << 32);
         const uint64_t x_max = d * ceil_div((uint64_t)lines, (uint64_t)h->n_ranks);
-        if (m <= 0xFFFFFFFFull && x_max * e < (1ull << 32)) a.slices_rcp = (uint32_t)m;
+        if (m <= 0xFFFFFFFFull && x_max < (1ull << 32) && x_max * e < (1ull << 32)) a.slices_rcp = (uint32_t)m;
       }
     }
   }
