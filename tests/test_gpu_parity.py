@@ -1014,3 +1014,21 @@ def test_first_xcds_default_slices_fit_the_span(proto, xcds):
         c.set_option("slices", 64 * xcds)  # 8 x 64 workgroups on each XCD: more than its CUs hold
         with pytest.raises(llar.LlarError):
             run(c, bits, proto, dt)
+
+
+@pytest.mark.parametrize("slices", [1, 2, 3, 5, 7, 31, 33, 63, 64])
+@pytest.mark.parametrize("n_ranks,n,acc", [(4, 8192, 0), (8, 8192, 0), (4, 8191, 1), (8, 3001, 0)])
+def test_ll128_line_partition_every_slice_count(slices, n_ranks, n, acc):
+    """The one-round LL128 kernel splits every owner's lines into slices (the
+    host's reciprocal multiply where it is exact, a division otherwise).  A
+    line left to no slice would never be consumed (time-out); a line in two
+    slices would be counted twice.  Integer data sums exactly in any order,
+    so the result must equal the oracle bit for bit, and the staging must be
+    zero again afterwards."""
+    dt = BF16
+    with comm_for(n_ranks, dt, n * 2, slices=slices, ll128_acc=acc) as c:
+        for rep in range(2):
+            bits = make_partials(950 + n_ranks, rep * 100 + slices, n_ranks, "bf16", n, "integer", 1.0)
+            got = run(c, bits, "ll128", dt)
+            assert_exact(got, oracle.allreduce(bits, dt), dt, "slices %d rep %d" % (slices, rep))
+        assert not c.staging(llar.LL128).any(), "LL128 staging must be zero after every call"
