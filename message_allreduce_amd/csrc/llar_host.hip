@@ -1107,12 +1107,20 @@ int run_multi(llar_comm* h, const void* const* ins, void* const* outs, int n_rec
     return LLAR_OK;
   }
   const size_t nv = ceil_div(blk, 16);
-  // measured on MI355X (N = 8, bf16, 16 KiB and 1 MiB in total): the best
-  // slice count grows as the square root of a block's 8-byte units (4 at
-  // 256 units, 32 at 16384); below 8 slices the spread placement wins, the
-  // local one pads the grid to 8 slices with idle workgroups
-  const int slices = h->slices ? (int)h->slices
-                               : clampi(std::llround(std::sqrt((double)(2 * nv)) / 4.0), 1, 64);
+  // measured on MI355X (bf16; N = 8 at 1 KiB to 1 MiB in total over every
+  // power of two from 1 to 64 slices, N = 2 and 4 at 1 KiB to 1 MiB): from 8
+  // slices on the local placement keeps each slice's exchange on one XCD, and
+  // 2 to 7 slices, spread over the XCDs, lose to both 1 and 8.  The best
+  // count grows as about the square root of a block's 8-byte units (8-16 at
+  // 16 to 256 units, 32 at 2048, 64 and more at 16384): N = 8 device time
+  // 16 KiB RS 2.74 -> 2.27 us, AG 2.61 -> 2.11; 128 KiB RS 3.42 -> 2.79;
+  // 1 MiB RS 6.16 -> 4.65 against the earlier square root / 4.  One slice
+  // stays best for blocks of fewer than 8 vectors and for an exchange under
+  // 2 KiB among fewer than 8 ranks (N = 2 and 4 at 1 KiB: 3.1-3.3 against
+  // 3.4-3.8 us per call at 8 slices).
+  int slices = (int)h->slices;
+  if (!slices)
+    slices = (nv < 8 || (N < 8 && total < 2048)) ? 1 : clampi(std::llround(std::sqrt((double)(2 * nv)) / 1.5), 8, 64);
   uint32_t place = kPlaceSpread;
   if (h->local_ok && (h->placement == 2 || (h->placement == 0 && slices >= 8))) place = kPlaceLocal;
   const int grid_slices = place == kPlaceLocal ? (int)ceil_div((size_t)slices, 8) * 8 : slices;
