@@ -411,3 +411,27 @@ def test_collectives_argument_errors():
         assert llar.llar_reduce_scatter(c.h, p, o, 0, BF16, llar.LL, 0) == 0            # no-op
         assert llar.llar_all_gather(c.h, o, p, 0, BF16, llar.LL, 0) == 0
         ok_status(c)
+
+
+# --------------------------------------------------------------------------- LL receiver lanes
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("n_ranks", [8, 3, 2])
+def test_reduce_scatter_ll_half_line_switch_bit_exact(n_ranks, dtype):
+    """The LL ReduceScatter's receiver gives each lane one 4-byte half line
+    while every half of its slice has a lane (one 256-thread slice: blocks up
+    to 64 vectors, 1 KiB), and whole 8-byte units per lane beyond.  Blocks on
+    both sides of that switch, ragged ones included (partial last vector, a
+    last half holding one 16-bit element), bit-exact against the oracle with
+    fresh inputs each repetition."""
+    dt = CODE[dtype]
+    esize = 4 if dtype == "fp32" else 2
+    blocks = sorted({1024 - 16, 1024 - esize, 1024, 1024 + esize, 1024 + 16, 2 * 1024 + esize, 8, esize})
+    with comm_for(n_ranks, dt, n_ranks * 16384, threads=256, slices=1) as c:
+        for blk in blocks:
+            cnt = blk // esize
+            for rep in range(2):
+                bits = rs_inputs(5100 + n_ranks, rep * 10000 + blk, n_ranks, cnt, dtype)
+                got = rs_run(c, bits, dt, "ll")
+                want = oracle.reduce_scatter(bits, dt)
+                for j in range(n_ranks):
+                    assert_exact(got[j], want[j], dt, "N=%d %s block %d B rep %d rank %d" % (n_ranks, dtype, blk, rep, j))
