@@ -297,7 +297,7 @@ int llar_clear_device_status(llar_comm* h);
  *                      zeroed, staging is left as it is); llar_get_option reads them back
  *   "auto_threshold_sentinel", "auto_threshold_ll128", "auto_threshold_pipelined"
  *                      AUTO size boundaries in bytes per rank: LL up to 64 KiB, one-shot Sentinel
- *                      up to 1 MiB, pipelined Sentinel above; LL128 only above its own threshold
+ *                      up to 1.5 MiB, pipelined Sentinel above; LL128 only above its own threshold
  *                      (default: never, its atomics are slower than the Sentinel exchange here)
  *   "auto_protocol"    0 = AUTO follows the thresholds above; 1..5 = AllReduce calls that pass
  *                      LLAR_AUTO run this protocol (send/recv, ReduceScatter and AllGather keep

@@ -107,7 +107,10 @@ struct llar_comm {
   long long ll128_buffers = 0;     // pipelined LL128, wave-split kernel: staging buffers (0 = 8, fewer if they do not fit)
   long long thr_sentinel = 64ll << 10;    // AUTO: LL up to (<=) this many bytes
   long long thr_ll128 = 1ll << 62;        // AUTO: one-shot Sentinel up to here (LL128 one round above)
-  long long thr_pipelined = 1ll << 20;    // AUTO: pipelined Sentinel above this
+  // AUTO: pipelined Sentinel above this (measured on MI355X, 8 x bf16 per
+  // call: one-shot Sentinel 8.1 / 11.4 / 14.3 us at 1 / 1.5 / 2 MiB, the
+  // pipeline 9.9 / 12.7 / 13.5)
+  long long thr_pipelined = 3ll << 19;
   // resident workgroups per CU by [ranks - 1][kernel][threads 64 .. 1024],
   // 0 = not asked yet: the occupancy query costs more host time than the
   // rest of a call's set-up

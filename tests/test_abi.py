@@ -207,7 +207,7 @@ def test_null_handle_options_are_the_process_defaults(L):
     assert L.llar_set_option(None, b"threads", 300) == -1
     assert L.llar_set_option(None, b"no_such_key", 1) == -1
     assert L.llar_get_option(None, b"local_placement_ok", ctypes.byref(v)) == -1
-    assert L.llar_get_option(None, b"auto_threshold_pipelined", ctypes.byref(v)) == 0 and v.value == 1 << 20
+    assert L.llar_get_option(None, b"auto_threshold_pipelined", ctypes.byref(v)) == 0 and v.value == 3 << 19
     assert L.llar_set_option(None, b"auto_threshold_pipelined", 2 << 20) == 0
     assert L.llar_get_option(None, b"auto_threshold_pipelined", ctypes.byref(v)) == 0 and v.value == 2 << 20
-    assert L.llar_set_option(None, b"auto_threshold_pipelined", 1 << 20) == 0  # the default again
+    assert L.llar_set_option(None, b"auto_threshold_pipelined", 3 << 19) == 0  # the default again
