@@ -1118,9 +1118,10 @@ int run_multi(llar_comm* h, const void* const* ins, void* const* outs, int n_rec
   // 16 to 256 units, 32 at 2048, 64 and more at 16384): N = 8 device time
   // 16 KiB RS 2.74 -> 2.27 us, AG 2.61 -> 2.11; 128 KiB RS 3.42 -> 2.79;
   // 1 MiB RS 6.16 -> 4.65 against the earlier square root / 4.  One slice
-  // stays best for blocks of fewer than 8 vectors and for an exchange under
-  // 2 KiB among fewer than 8 ranks (N = 2 and 4 at 1 KiB: 3.1-3.3 against
-  // 3.4-3.8 us per call at 8 slices).
+  // stays best for an exchange under 2 KiB among fewer than 8 ranks (N = 2
+  // and 4 at 1 KiB: 3.1-3.3 against 3.4-3.8 us per call at 8 slices), and
+  // blocks of fewer than 8 vectors keep the one slice the earlier rule gave
+  // them (not re-measured).
   int slices = (int)h->slices;
   if (!slices)
     slices = (nv < 8 || (N < 8 && total < 2048)) ? 1 : clampi(std::llround(std::sqrt((double)(2 * nv)) / 1.5), 8, 64);
