@@ -306,6 +306,16 @@ __device__ __forceinline__ bool ll128_wait(Wire w, uint32_t off, uint32_t full, 
 // 16 bytes of a line, after its count is complete; then zero them
 __device__ __forceinline__ u32x4 ll128_read16(Wire w, uint32_t off) { return ld16_coh(w, off); }
 __device__ __forceinline__ void ll128_reset16(Wire w, uint32_t off) { st16_coh(w, off, u32x4{0u, 0u, 0u, 0u}); }
+// The same 16 bytes (at `p`, 8-byte aligned) read and zeroed at once, after
+// the line's count is complete: two device-scope 8-byte exchanges with zero,
+// which resolve where the line's float atomics did, so no separate zeroing
+// store is left to be acknowledged
+__device__ __forceinline__ u32x4 ll128_take16(uint8_t* p) {
+  uint64_t* const q = reinterpret_cast<uint64_t*>(p);
+  const uint64_t lo = __hip_atomic_exchange(q, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_exchange(q + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+}
 
 }  // namespace llar_wire
 

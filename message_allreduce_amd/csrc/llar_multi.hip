@@ -373,7 +373,10 @@ __global__ void __launch_bounds__(512) k_rs_ll128(MultiArgs a) {
       raise_status(ctrl, kStatusTimeout);
       break;
     }
-    const u32x4 v = llar_wire::ll128_read16(rs, loff + j * 16u);
+    // 16-bit staging: read and zero the line's 16 bytes in one exchange, as
+    // the one-round AllReduce does; binary32 staging reads, then stores zeros
+    const bool take = kAcc16 && !keep;
+    const u32x4 v = take ? llar_wire::ll128_take16(stage + loff + j * 16u) : llar_wire::ll128_read16(rs, loff + j * 16u);
     if constexpr (!kAcc16) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -390,7 +393,7 @@ __global__ void __launch_bounds__(512) k_rs_ll128(MultiArgs a) {
         reinterpret_cast<uint16_t*>(out)[i] = (uint16_t)(v[t >> 1] >> ((t & 1) * 16));
       }
     }
-    if (!keep) llar_wire::ll128_reset16(rs, loff + j * 16u);
+    if (!take && !keep) llar_wire::ll128_reset16(rs, loff + j * 16u);
   }
   wg_end(ctrl, st, host_epoch, grid, timing, idle);
 }
