@@ -12,7 +12,9 @@
 //   demo_ll128_reduce          every rank adds its binary32 values into
 //                              LL128 lines and counts itself in slot 0; the
 //                              line's owner waits for the count N, writes out
-//                              and zeroes the line.
+//                              and zeroes the line (a read and a zeroing
+//                              store, or with `take` one exchange per 8
+//                              bytes that reads and zeroes at once).
 //
 // Grids: workgroup b is (rank b % N, slice b / N), so ranks sit on different
 // XCDs and every store uses the device scope.  Every launch is small enough
@@ -126,7 +128,8 @@ __global__ void __launch_bounds__(256) k_sentinel_chain(Parts in, float* out, ui
 // line slot: 32 threads per line, 8 lines per 256-thread workgroup.
 template <int N>
 __global__ void __launch_bounds__(256) k_ll128_reduce(Parts in, float* out, uint32_t n, uint8_t* stage,
-                                                       uint32_t stage_bytes, uint64_t spin, uint32_t* status) {
+                                                       uint32_t stage_bytes, uint64_t spin, uint32_t* status,
+                                                       uint32_t take) {
   const int r = (int)(blockIdx.x % N);
   const uint32_t w = blockIdx.x / N, slices = gridDim.x / N;
   const uint32_t lines = (n + 30u) / 31u;
@@ -150,13 +153,14 @@ __global__ void __launch_bounds__(256) k_ll128_reduce(Parts in, float* out, uint
       return;
     }
     if (q < 8u) {  // 8 lanes read 16 bytes each
-      const u32x4 x = ll128_read16(wire, l * kLL128LineBytes + q * 16u);
+      const uint32_t off = l * kLL128LineBytes + q * 16u;
+      const u32x4 x = take ? ll128_take16(stage + off) : ll128_read16(wire, off);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const uint32_t s = 4u * q + t, i = 31u * l + s - 1u;
         if (s != 0u && i < n) out[i] = __uint_as_float(x[t]);
       }
-      ll128_reset16(wire, l * kLL128LineBytes + q * 16u);
+      if (!take) ll128_reset16(wire, off);
     }
   }
 }
@@ -230,14 +234,14 @@ int demo_sentinel_chain(const float* const* parts, float* out, uint32_t n, int n
 }
 
 int demo_ll128_reduce(const float* const* parts, float* out, uint32_t n, int n_ranks, void* stage,
-                      uint32_t stage_bytes, uint64_t spin_ticks, uint32_t* status, void* stream) {
+                      uint32_t stage_bytes, uint64_t spin_ticks, uint32_t* status, void* stream, int take) {
   if (n == 0) return -1;
   const Parts p = make_parts(parts, nullptr, n_ranks);
   const int grid = grid_for(n_ranks, (n + 30u) / 31u, 8u);
   hipStream_t s = static_cast<hipStream_t>(stream);
 #define CALL(N)                                                                                        \
   hipLaunchKernelGGL(k_ll128_reduce<N>, dim3(grid), dim3(256), 0, s, p, out, n, (uint8_t*)stage, \
-                     stage_bytes, spin_ticks, status)
+                     stage_bytes, spin_ticks, status, take ? 1u : 0u)
   DEMO_SWITCH_N(n_ranks, CALL)
 #undef CALL
   return hipGetLastError() == hipSuccess ? 0 : -2;

@@ -41,7 +41,7 @@ def demo():
     L.demo_scaled_allreduce_ll.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_float), vp, u32, i32, vp,
                                            u32, u32, u64, vp, vp]
     L.demo_sentinel_chain.argtypes = [ctypes.POINTER(vp), vp, u32, i32, vp, u32, u64, vp, vp]
-    L.demo_ll128_reduce.argtypes = [ctypes.POINTER(vp), vp, u32, i32, vp, u32, u64, vp, vp]
+    L.demo_ll128_reduce.argtypes = [ctypes.POINTER(vp), vp, u32, i32, vp, u32, u64, vp, vp, i32]
     for f in (L.demo_scaled_allreduce_ll, L.demo_sentinel_chain, L.demo_ll128_reduce):
         f.restype = i32
     return L
@@ -107,8 +107,9 @@ def test_sentinel_relay(demo, n_ranks):
         assert (stage.cpu().numpy() == 0xFF).all(), "every slot is reset by its reader"
 
 
+@pytest.mark.parametrize("take", [0, 1], ids=["read_reset", "take"])
 @pytest.mark.parametrize("n_ranks", [2, 4, 8])
-def test_ll128_atomic_reduce(demo, n_ranks):
+def test_ll128_atomic_reduce(demo, n_ranks, take):
     n_max = max(SIZES)
     lines = (n_max + 30) // 31
     stage = torch.zeros(lines * 128, dtype=torch.uint8, device="cuda")
@@ -118,7 +119,7 @@ def test_ll128_atomic_reduce(demo, n_ranks):
         dev = [torch.from_numpy(p[r].copy()).cuda() for r in range(n_ranks)]
         out = torch.empty(n, dtype=torch.float32, device="cuda")
         rc = demo.demo_ll128_reduce(ptrs(dev), out.data_ptr(), n, n_ranks, stage.data_ptr(), stage.numel(), SPIN,
-                                    status.data_ptr(), stream())
+                                    status.data_ptr(), stream(), take)
         assert rc == 0
         torch.cuda.synchronize()
         assert int(status.item()) == 0, "a wait expired"
